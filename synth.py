@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for the decode-time fused quantized linear.
+
+This module only draws random numbers and rounds them to storage formats.  It
+holds none of the method's arithmetic (no quantizer, no LayerNorm, no product),
+so both the oracle and the HIP path can consume its arrays without sharing code.
+
+RNG: numpy's PCG64 Generator, one stream per tensor, seeded with
+    seed(c, p, id) = 1_000_000 * c + 1_000 * p + id
+for workload c (1..5), pass p (0 except in the 124-pass chain) and tensor id
+    1 x, 2 W / gate W, 3 up W, 4 gamma, 5 beta, 6 residual, 7 add.
+Values are drawn in float64 and rounded to the storage dtype; 16-bit tensors are
+returned as uint16 bit patterns, weights to be quantized as float32.
+
+The pages benchmark a trained depth decoder and an MLP geometry whose weights are
+not available; these draws stand in for them with the shapes below.
+
+Workloads (N(mu, sd): second parameter is the standard deviation, except
+N(0, 1/K) whose 1/K is the variance):
+  1  T=1, K=1024, N=1024 plain linear; x fp16 N(0,1); W dense fp16 N(0,1/K); fp16 out
+  2  T=4, K=2048, N=8192, LN + exact GELU; x bf16 N(3,1); gamma N(1,0.1); beta N(0,0.1);
+     W fp32 N(0,0.02) -> 8-bit affine, group 64; bf16 out
+  3  T=32, K=1024, N=4096, LN + residual; x, res bf16 N(0,1); W 8-bit from N(0,0.02); bf16 out
+  4  gate+up SwiGLU, M=4, K=4096, N=14336 each; x bf16 N(0,1); gate/up 4-bit from N(0,0.02)
+  5  124 dependent LN + linear passes, K=N=1024, T_p = 1 + (p mod 8); buffers B_0..B_124
+     (8, 1024) bf16 N(0,1); per pass gamma, beta as in 2, W_p 8-bit from N(0,0.02)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+NP_CODES = {F32: np.float32}
+
+TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7}
+CHAIN_PASSES = 124
+CHAIN_K = CHAIN_N = 1024
+CHAIN_TMAX = 8
+
+
+def seed(c: int, p: int, name: str) -> int:
+    return 1_000_000 * c + 1_000 * p + TENSOR_IDS[name]
+
+
+def normal(s: int, shape, mean: float = 0.0, sd: float = 1.0) -> np.ndarray:
+    """float64 draws from N(mean, sd^2) on a PCG64 stream seeded with s."""
+    rng = np.random.Generator(np.random.PCG64(s))
+    return mean + sd * rng.standard_normal(size=shape, dtype=np.float64)
+
+
+def to_bits(a64: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float64 values to a storage dtype.  fp16 -> uint16 bits (numpy's IEEE
+    conversion), bf16 -> uint16 bits (float64 -> float32 -> bfloat16, each step to
+    nearest even), fp32 -> float32 values."""
+    if dtype == F32:
+        return np.asarray(a64, np.float32)
+    if dtype == F16:
+        return np.asarray(a64, np.float64).astype(np.float16).view(np.uint16)
+    f = np.asarray(a64, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    nan = (f & 0x7FFFFFFF) > 0x7F800000
+    r = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = ((f[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+def draw(c: int, p: int, name: str, shape, mean: float, sd: float, dtype: int) -> np.ndarray:
+    return to_bits(normal(seed(c, p, name), shape, mean, sd), dtype)
+
+
+@dataclass
+class LinearCase:
+    """One fused-linear call's inputs.  w_f32 is set for quantized weights (to be packed),
+    w_dense (uint16 bits) for dense ones."""
+    name: str
+    T: int
+    K: int
+    N: int
+    x_dtype: int
+    bits: int
+    y_dtype: int
+    x: np.ndarray
+    w_f32: Optional[np.ndarray] = None
+    w_dense: Optional[np.ndarray] = None
+    w_dtype: int = F16
+    gamma: Optional[np.ndarray] = None
+    beta: Optional[np.ndarray] = None
+    eps: float = 1e-5
+    act: int = 0
+    res: Optional[np.ndarray] = None
+    add: Optional[np.ndarray] = None
+
+
+@dataclass
+class GateUpCase:
+    name: str
+    T: int
+    K: int
+    N: int
+    x_dtype: int
+    bits: int
+    y_dtype: int
+    x: np.ndarray
+    gate: np.ndarray          # float32 (N, K) to be quantized, or uint16 dense bits when bits == 16
+    up: np.ndarray
+    gamma: Optional[np.ndarray] = None
+    beta: Optional[np.ndarray] = None
+    eps: float = 1e-5
+
+
+def workload(c: int, scale_n: Optional[int] = None):
+    """The synthetic inputs of workload c (1..4).  scale_n, if given, replaces N (smaller
+    parity cases drawn from the same distributions)."""
+    if c == 1:
+        T, K, N = 1, 1024, scale_n or 1024
+        return LinearCase("plain-fp16-T1-K1024-N1024", T, K, N, F16, 16, F16,
+                          x=draw(1, 0, "x", (T, K), 0.0, 1.0, F16),
+                          w_dense=draw(1, 0, "w", (N, K), 0.0, 1.0 / np.sqrt(K), F16), w_dtype=F16)
+    if c == 2:
+        T, K, N = 4, 2048, scale_n or 8192
+        return LinearCase("ln-gelu-q8-T4-K2048-N8192", T, K, N, BF16, 8, BF16,
+                          x=draw(2, 0, "x", (T, K), 3.0, 1.0, BF16),
+                          w_f32=draw(2, 0, "w", (N, K), 0.0, 0.02, F32),
+                          gamma=draw(2, 0, "gamma", (K,), 1.0, 0.1, BF16),
+                          beta=draw(2, 0, "beta", (K,), 0.0, 0.1, BF16), eps=1e-5, act=1)
+    if c == 3:
+        T, K, N = 32, 1024, scale_n or 4096
+        return LinearCase("ln-residual-q8-T32-K1024-N4096", T, K, N, BF16, 8, BF16,
+                          x=draw(3, 0, "x", (T, K), 0.0, 1.0, BF16),
+                          w_f32=draw(3, 0, "w", (N, K), 0.0, 0.02, F32),
+                          gamma=draw(3, 0, "gamma", (K,), 1.0, 0.1, BF16),
+                          beta=draw(3, 0, "beta", (K,), 0.0, 0.1, BF16), eps=1e-5,
+                          res=draw(3, 0, "res", (T, N), 0.0, 1.0, BF16))
+    if c == 4:
+        T, K, N = 4, 4096, scale_n or 14336
+        return GateUpCase("swiglu-q4-M4-K4096-N14336", T, K, N, BF16, 4, BF16,
+                          x=draw(4, 0, "x", (T, K), 0.0, 1.0, BF16),
+                          gate=draw(4, 0, "w", (N, K), 0.0, 0.02, F32),
+                          up=draw(4, 0, "up", (N, K), 0.0, 0.02, F32))
+    raise ValueError(f"no single-call workload {c}")
+
+
+def chain_T(p: int) -> int:
+    """Rows of pass p of the 124-pass chain: 1 + (p mod 8)."""
+    return 1 + (p % CHAIN_TMAX)
+
+
+def chain_buffers() -> np.ndarray:
+    """B_0..B_124, each (8, 1024) bf16 bits, drawn N(0, 1)."""
+    return np.stack([draw(5, p, "x", (CHAIN_TMAX, CHAIN_K), 0.0, 1.0, BF16) for p in range(CHAIN_PASSES + 1)])
+
+
+def chain_pass(p: int):
+    """Per-pass (w_f32 (N, K), gamma, beta) of the chain."""
+    return (draw(5, p, "w", (CHAIN_N, CHAIN_K), 0.0, 0.02, F32),
+            draw(5, p, "gamma", (CHAIN_K,), 1.0, 0.1, BF16),
+            draw(5, p, "beta", (CHAIN_K,), 0.0, 0.1, BF16))
+
+
+def random_case(s: int, T: int, K: int, N: int, bits: int, x_dtype: int = BF16, ln: bool = False,
+                act: int = 0, res: bool = False, add: bool = False, y_dtype: Optional[int] = None,
+                x_mean: float = 0.0, w_sd: float = 0.02) -> LinearCase:
+    """A parity case of arbitrary shape, drawn like the workloads (stream ids offset by s)."""
+    c = 100 + s
+    y_dtype = x_dtype if y_dtype is None else y_dtype
+    kw = {}
+    if bits == 16:
+        kw["w_dense"] = draw(c, 0, "w", (N, K), 0.0, 1.0 / np.sqrt(K), x_dtype)
+        kw["w_dtype"] = x_dtype
+    else:
+        kw["w_f32"] = draw(c, 0, "w", (N, K), 0.0, w_sd, F32)
+    if ln:
+        kw["gamma"] = draw(c, 0, "gamma", (K,), 1.0, 0.1, x_dtype)
+        kw["beta"] = draw(c, 0, "beta", (K,), 0.0, 0.1, x_dtype)
+    if res:
+        kw["res"] = draw(c, 0, "res", (T, N), 0.0, 1.0, x_dtype)
+    if add:
+        kw["add"] = draw(c, 0, "add", (N,), 0.0, 1.0, x_dtype)
+    return LinearCase(f"rand{s}-T{T}-K{K}-N{N}-b{bits}", T, K, N, x_dtype, bits, y_dtype,
+                      x=draw(c, 0, "x", (T, K), x_mean, 1.0, x_dtype), act=act, **kw)
+
+
+def random_gateup(s: int, T: int, K: int, N: int, bits: int, x_dtype: int = BF16, ln: bool = False,
+                  y_dtype: Optional[int] = None) -> GateUpCase:
+    c = 100 + s
+    y_dtype = x_dtype if y_dtype is None else y_dtype
+    kw = {}
+    if ln:
+        kw["gamma"] = draw(c, 0, "gamma", (K,), 1.0, 0.1, x_dtype)
+        kw["beta"] = draw(c, 0, "beta", (K,), 0.0, 0.1, x_dtype)
+    if bits == 16:
+        g = draw(c, 0, "w", (N, K), 0.0, 1.0 / np.sqrt(K), x_dtype)
+        u = draw(c, 0, "up", (N, K), 0.0, 1.0 / np.sqrt(K), x_dtype)
+    else:
+        g = draw(c, 0, "w", (N, K), 0.0, 0.02, F32)
+        u = draw(c, 0, "up", (N, K), 0.0, 0.02, F32)
+    return GateUpCase(f"gu{s}-T{T}-K{K}-N{N}-b{bits}", T, K, N, x_dtype, bits, y_dtype,
+                      x=draw(c, 0, "x", (T, K), 0.0, 1.0, x_dtype), gate=g, up=u, **kw)
