@@ -1,0 +1,17 @@
+// Instantiations of the fused kernel for f16 weights (one per activation-tile count).
+#include "qlin_fused.h"
+
+namespace qlin {
+
+hipError_t launch_fused_f16(const LinParams& p, int mt, int grid, size_t lds, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_one<16, false, 1>(p, grid, lds, s);
+    case 2: return launch_one<16, false, 2>(p, grid, lds, s);
+    case 3: return launch_one<16, false, 3>(p, grid, lds, s);
+    case 4: return launch_one<16, false, 4>(p, grid, lds, s);
+    case 5: return launch_one<16, false, 5>(p, grid, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qlin

@@ -1,0 +1,310 @@
+// libqlin host side: argument validation, variant selection, launches, hipGraph chains.
+// The ABI and its conventions are documented in include/qlin.h.
+#include "qlin.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "qlin_fused.h"
+#include "qlin_internal.h"
+
+namespace {
+
+std::atomic<int64_t> g_dispatch[4];
+
+constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
+constexpr int64_t kMaxN = int64_t(1) << 28;
+constexpr int kMaxT = 32;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t dtype_size(int d) { return d == QLIN_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || !an || !bn) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+qlin_status check_weight(const qlin_weight* w, int x_dtype, bool nonempty) {
+  if (!w) return QLIN_ERR_NULL;
+  if (w->bits != 4 && w->bits != 8 && w->bits != 16) return QLIN_ERR_BITS;
+  if (w->bits != 16 && w->group_size != 64) return QLIN_ERR_BITS;
+  if (w->K <= 0 || w->K % 64 != 0 || w->K > kMaxK) return QLIN_ERR_SHAPE;
+  if (w->N < 0 || w->N > kMaxN) return QLIN_ERR_SHAPE;
+  if (w->bits == 16) {
+    if (w->dtype != x_dtype) return QLIN_ERR_DTYPE;
+  } else if (w->dtype != QLIN_F16) {
+    return QLIN_ERR_DTYPE;
+  }
+  if (nonempty && w->N > 0) {
+    if (!w->data) return QLIN_ERR_NULL;
+    if (!aligned(w->data, 16)) return QLIN_ERR_ALIGN;
+    if (w->bits != 16) {
+      if (!w->scales || !w->biases) return QLIN_ERR_NULL;
+      if (!aligned(w->scales, 2) || !aligned(w->biases, 2)) return QLIN_ERR_ALIGN;
+    }
+  }
+  return QLIN_OK;
+}
+
+qlin_status validate(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up,
+                     const qlin_ln* ln, int act, const void* res, const void* add, const void* y, int y_dtype) {
+  if (!w) return QLIN_ERR_NULL;
+  if (x_dtype != QLIN_F16 && x_dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (y_dtype != QLIN_F32 && y_dtype != QLIN_F16 && y_dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (T < 0 || T > kMaxT) return QLIN_ERR_SHAPE;
+  if (act != QLIN_ACT_NONE && act != QLIN_ACT_GELU) return QLIN_ERR_ARG;
+  const bool nonempty = T > 0;
+  qlin_status st = check_weight(w, x_dtype, nonempty);
+  if (st != QLIN_OK) return st;
+  if (up) {
+    st = check_weight(up, x_dtype, nonempty);
+    if (st != QLIN_OK) return st;
+    if (up->bits != w->bits) return QLIN_ERR_BITS;
+    if (up->dtype != w->dtype) return QLIN_ERR_DTYPE;
+    if (up->N != w->N || up->K != w->K) return QLIN_ERR_SHAPE;
+    if (act != QLIN_ACT_NONE || res || add) return QLIN_ERR_ARG;
+  }
+  if (ln) {
+    if (!(ln->eps >= 0.0f) || !std::isfinite(ln->eps)) return QLIN_ERR_ARG;
+  }
+  if (!nonempty || w->N == 0) return QLIN_OK;   // empty: a valid no-op
+  if (!x || !y) return QLIN_ERR_NULL;
+  if (!aligned(x, 16)) return QLIN_ERR_ALIGN;
+  if (!aligned(y, dtype_size(y_dtype))) return QLIN_ERR_ALIGN;
+  if (ln) {
+    if (!ln->gamma || !ln->beta) return QLIN_ERR_NULL;
+    if (!aligned(ln->gamma, 16) || !aligned(ln->beta, 16)) return QLIN_ERR_ALIGN;
+  }
+  if (res && !aligned(res, 2)) return QLIN_ERR_ALIGN;
+  if (add && !aligned(add, 2)) return QLIN_ERR_ALIGN;
+  const size_t ybytes = (size_t)T * (size_t)w->N * dtype_size(y_dtype);
+  if (overlaps(y, ybytes, x, (size_t)T * (size_t)w->K * 2)) return QLIN_ERR_ARG;
+  if (overlaps(y, ybytes, res, (size_t)T * (size_t)w->N * 2)) return QLIN_ERR_ARG;
+  return QLIN_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up,
+                   const qlin_ln* ln, int act, const void* res, const void* add, void* y, int y_dtype,
+                   hipStream_t stream) {
+  using namespace qlin;
+  LinParams p{};
+  p.x = x; p.x_dtype = x_dtype; p.T = T; p.K = (int)w->K; p.N = (int)w->N;
+  p.w[0] = w->data; p.sc[0] = static_cast<const uint16_t*>(w->scales); p.bi[0] = static_cast<const uint16_t*>(w->biases);
+  p.gateup = up != nullptr;
+  if (up) { p.w[1] = up->data; p.sc[1] = static_cast<const uint16_t*>(up->scales); p.bi[1] = static_cast<const uint16_t*>(up->biases); }
+  else { p.w[1] = p.w[0]; p.sc[1] = p.sc[0]; p.bi[1] = p.bi[0]; }
+  p.ln = ln != nullptr;
+  p.gamma = ln ? ln->gamma : nullptr; p.beta = ln ? ln->beta : nullptr; p.eps = ln ? ln->eps : 0.0f;
+  const bool bf16op = w->bits == 16 && w->dtype == QLIN_BF16;
+  if (bf16op) {            // dense bf16 weights: bf16 operands, exact 1- or 3-term activations
+    p.terms = p.ln ? 3 : 1; p.scale_act = 0; p.scale_gb = 0;
+  } else {                 // fp16 operands: 1 term when x is fp16 and there is no LN, else 2 scaled terms
+    p.terms = p.ln ? 2 : 1;
+    p.scale_act = (p.ln || x_dtype == QLIN_BF16) ? 1 : 0;
+    p.scale_gb = (p.ln && x_dtype == QLIN_BF16) ? 1 : 0;
+  }
+  p.act = act; p.res = res; p.add = add; p.y = y; p.y_dtype = y_dtype;
+  p.rows = act_rows(T, p.terms, p.ln);
+  const int mt = (p.rows + 15) / 16;
+  const int64_t row_bytes = w->K * w->bits / 8;
+  p.steps = (int)((row_bytes + 63) / 64);
+  p.chunk_steps = fused_chunk_steps(w->bits, mt, T, p.ln, p.rows, w->K);
+  p.ntiles = (int)(up ? (w->N + 7) / 8 : (w->N + 15) / 16);
+  const int grid = p.ntiles < cu_count() ? p.ntiles : cu_count();
+  const size_t lds = fused_lds_bytes(w->bits, p.rows, p.chunk_steps, w->K, mt);
+  hipError_t e;
+  if (w->bits == 4) e = launch_fused_q4(p, mt, grid, lds, stream);
+  else if (w->bits == 8) e = launch_fused_q8(p, mt, grid, lds, stream);
+  else if (bf16op) e = launch_fused_bf16(p, mt, grid, lds, stream);
+  else e = launch_fused_f16(p, mt, grid, lds, stream);
+  if (e != hipSuccess) return QLIN_ERR_HIP;
+  g_dispatch[up ? 1 : 0].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
+}  // namespace
+
+namespace qlin {
+static int step_k(int bits) { return bits == 4 ? Fmt<4>::kStepK : (bits == 8 ? Fmt<8>::kStepK : Fmt<16>::kStepK); }
+static long chunk_k(int bits, int cs, long K) { const long kc = (long)cs * step_k(bits); return kc < K ? kc : K; }
+
+int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K) {
+  const int mfma = bits == 4 ? Fmt<4>::kMfma : (bits == 8 ? Fmt<8>::kMfma : Fmt<16>::kMfma);
+  int cs = kWaves * max_steps_for(mfma, mt);
+  (void)T; (void)ln;
+  for (; cs > 1; --cs) {
+    const long kc = chunk_k(bits, cs, K);
+    const long ppl = (kc / 8 + 63) / 64;     // staged pieces per lane and row
+    if (ppl <= kPieceMax && lds_bytes_for(rows, (int)kc, mt) <= kLdsMax) break;
+  }
+  return cs;
+}
+
+size_t fused_lds_bytes(int bits, int rows, int chunk_steps, long K, int mt) {
+  return (size_t)lds_bytes_for(rows, (int)chunk_k(bits, chunk_steps, K), mt);
+}
+}  // namespace qlin
+
+struct qlin_chain {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int32_t n = 0;
+};
+
+extern "C" {
+
+qlin_status qlin_check(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up,
+                       const qlin_ln* ln, qlin_act act, const void* residual, const void* add, const void* y,
+                       qlin_dtype y_dtype) {
+  return validate(x, x_dtype, T, w, up, ln, act, residual, add, y, y_dtype);
+}
+
+qlin_status qlin_linear(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w, const qlin_ln* ln,
+                        qlin_act act, const void* residual, const void* add, void* y, qlin_dtype y_dtype,
+                        void* stream) {
+  const qlin_status st = validate(x, x_dtype, T, w, nullptr, ln, act, residual, add, y, y_dtype);
+  if (st != QLIN_OK) return st;
+  if (T == 0 || w->N == 0) return QLIN_OK;
+  return launch(x, x_dtype, T, w, nullptr, ln, act, residual, add, y, y_dtype, static_cast<hipStream_t>(stream));
+}
+
+qlin_status qlin_gateup_swiglu(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* gate,
+                               const qlin_weight* up, const qlin_ln* ln, void* y, qlin_dtype y_dtype, void* stream) {
+  if (!up) return QLIN_ERR_NULL;
+  const qlin_status st = validate(x, x_dtype, T, gate, up, ln, QLIN_ACT_NONE, nullptr, nullptr, y, y_dtype);
+  if (st != QLIN_OK) return st;
+  if (T == 0 || gate->N == 0) return QLIN_OK;
+  return launch(x, x_dtype, T, gate, up, ln, QLIN_ACT_NONE, nullptr, nullptr, y, y_dtype,
+                static_cast<hipStream_t>(stream));
+}
+
+qlin_status qlin_pack_affine(const float* w, int64_t N, int64_t K, int32_t bits, int32_t group_size, uint32_t* codes,
+                             void* scales, void* biases, qlin_dtype sb_dtype, int32_t* nonfinite_flag, void* stream) {
+  if (bits != 4 && bits != 8) return QLIN_ERR_BITS;
+  if (group_size != 64) return QLIN_ERR_BITS;
+  if (sb_dtype != QLIN_F16) return QLIN_ERR_DTYPE;
+  if (N < 0 || N > kMaxN || K <= 0 || K % 64 != 0 || K > kMaxK) return QLIN_ERR_SHAPE;
+  if (N == 0) return QLIN_OK;
+  if (!w || !codes || !scales || !biases) return QLIN_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(biases, 2)) return QLIN_ERR_ALIGN;
+  if (nonfinite_flag && !aligned(nonfinite_flag, 4)) return QLIN_ERR_ALIGN;
+  const hipError_t e = qlin::launch_pack(w, N, K, bits, codes, static_cast<uint16_t*>(scales),
+                                         static_cast<uint16_t*>(biases), nonfinite_flag, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return QLIN_ERR_HIP;
+  g_dispatch[2].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
+qlin_status qlin_unpack_affine(const qlin_weight* w, float* out, void* stream) {
+  if (!w) return QLIN_ERR_NULL;
+  const int x_dtype = w->bits == 16 ? w->dtype : QLIN_F16;
+  if (w->bits == 16 && w->dtype != QLIN_F16 && w->dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  const qlin_status st = check_weight(w, x_dtype, true);
+  if (st != QLIN_OK) return st;
+  if (w->N == 0) return QLIN_OK;
+  if (!out) return QLIN_ERR_NULL;
+  if (!aligned(out, 4)) return QLIN_ERR_ALIGN;
+  const hipError_t e = qlin::launch_unpack(w->data, static_cast<const uint16_t*>(w->scales),
+                                           static_cast<const uint16_t*>(w->biases), w->bits, w->dtype, w->N, w->K, out,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return QLIN_ERR_HIP;
+  g_dispatch[3].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
+qlin_status qlin_chain_create(const qlin_pass* passes, int32_t n_passes, qlin_dtype x_dtype, qlin_dtype y_dtype,
+                              void* capture_stream, qlin_chain** out) {
+  if (!out) return QLIN_ERR_NULL;
+  *out = nullptr;
+  if (!passes) return QLIN_ERR_NULL;
+  if (n_passes < 1) return QLIN_ERR_ARG;
+  if (!capture_stream) return QLIN_ERR_ARG;   // the null stream cannot be captured
+  for (int32_t i = 0; i < n_passes; ++i) {
+    const qlin_pass& q = passes[i];
+    qlin_ln ln{q.ln_gamma, q.ln_beta, q.ln_eps};
+    const qlin_status st = validate(q.x, x_dtype, q.T, &q.w, nullptr, q.ln_gamma ? &ln : nullptr, q.act, q.residual,
+                                    q.add, q.y, y_dtype);
+    if (st != QLIN_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(capture_stream);
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed) != hipSuccess) return QLIN_ERR_HIP;
+  qlin_status st = QLIN_OK;
+  for (int32_t i = 0; i < n_passes && st == QLIN_OK; ++i) {
+    const qlin_pass& q = passes[i];
+    qlin_ln ln{q.ln_gamma, q.ln_beta, q.ln_eps};
+    st = qlin_linear(q.x, x_dtype, q.T, &q.w, q.ln_gamma ? &ln : nullptr, static_cast<qlin_act>(q.act), q.residual,
+                     q.add, q.y, y_dtype, capture_stream);
+  }
+  hipGraph_t graph = nullptr;
+  const hipError_t ee = hipStreamEndCapture(s, &graph);
+  if (st != QLIN_OK || ee != hipSuccess || !graph) {
+    if (graph) hipGraphDestroy(graph);
+    return st != QLIN_OK ? st : QLIN_ERR_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    hipGraphDestroy(graph);
+    return QLIN_ERR_HIP;
+  }
+  qlin_chain* c = new (std::nothrow) qlin_chain;
+  if (!c) {
+    hipGraphExecDestroy(exec);
+    hipGraphDestroy(graph);
+    return QLIN_ERR_HIP;
+  }
+  c->graph = graph; c->exec = exec; c->n = n_passes;
+  *out = c;
+  return QLIN_OK;
+}
+
+qlin_status qlin_chain_launch(qlin_chain* chain, void* stream) {
+  if (!chain) return QLIN_ERR_NULL;
+  if (hipGraphLaunch(chain->exec, static_cast<hipStream_t>(stream)) != hipSuccess) return QLIN_ERR_HIP;
+  return QLIN_OK;
+}
+
+int32_t qlin_chain_passes(const qlin_chain* chain) { return chain ? chain->n : 0; }
+
+void qlin_chain_destroy(qlin_chain* chain) {
+  if (!chain) return;
+  if (chain->exec) hipGraphExecDestroy(chain->exec);
+  if (chain->graph) hipGraphDestroy(chain->graph);
+  delete chain;
+}
+
+int64_t qlin_dispatch_count(int32_t which) {
+  if (which < 0 || which > 3) return -1;
+  return g_dispatch[which].load(std::memory_order_relaxed);
+}
+
+const char* qlin_status_string(qlin_status s) {
+  switch (s) {
+    case QLIN_OK: return "ok";
+    case QLIN_ERR_NULL: return "a required pointer is NULL";
+    case QLIN_ERR_SHAPE: return "shape out of range (0 <= T <= 32, K a positive multiple of 64, N >= 0)";
+    case QLIN_ERR_DTYPE: return "unsupported or inconsistent dtype";
+    case QLIN_ERR_BITS: return "bits must be 4, 8 or 16 and group_size 64";
+    case QLIN_ERR_ALIGN: return "pointer misaligned";
+    case QLIN_ERR_HIP: return "HIP runtime error";
+    case QLIN_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

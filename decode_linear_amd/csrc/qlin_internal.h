@@ -1,0 +1,60 @@
+// Internal interface between libqlin's host code (qlin_host.cpp) and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+// Waves per workgroup of the fused kernel.  Each wave owns a fixed slice of K and keeps
+// its activation fragments in registers; the workgroup merges the slices in LDS.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
+// Arguments of one fused-linear launch (plain linear or gate/up).
+struct LinParams {
+  const void* x;          // (T, K) activations, x_dtype
+  int x_dtype;            // 1 fp16, 2 bf16
+  int T, K, N;
+  const void* w[2];       // weight rows (gate in w[0], up in w[1] for gate/up)
+  const uint16_t* sc[2];  // fp16 scales (N, K/64), quantized only
+  const uint16_t* bi[2];  // fp16 biases
+  int gateup;             // 0: y = epi(z); 1: y = silu(z_gate) * z_up
+  int ln;                 // LayerNorm prologue on/off
+  const void* gamma;
+  const void* beta;
+  float eps;
+  int terms;              // 16-bit operand terms per activation row (1, 2 or 3)
+  int scale_act;          // 1: scale activation rows into the binary16 range per wave
+  int scale_gb;           // 1: same for the gamma / beta rows
+  int act;                // 0 none, 1 GELU
+  const void* res;        // (T, N) or null
+  const void* add;        // (N,) or null
+  void* y;                // (T, N)
+  int y_dtype;            // 0 fp32, 1 fp16, 2 bf16
+  int rows;               // operand rows: terms*T (+ gamma, beta with LN)
+  int ntiles;             // 16-column output tiles (linear) or 8-column tiles (gate/up)
+  int steps;              // 64-byte steps per weight row
+  int chunk_steps;        // steps staged at once (all of them unless K is long)
+};
+
+// Rows of the activation operand: terms*T activation terms, then gamma and beta (LN).
+inline int act_rows(int T, int terms, int ln) { return terms * T + (ln ? 2 : 0); }
+
+// Launchers (one per weight format / operand type), defined in the kernel sources.
+// mt = number of 16-row activation tiles (1..7).  Return the launch error.
+hipError_t launch_fused_q4(const LinParams& p, int mt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_fused_q8(const LinParams& p, int mt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_fused_f16(const LinParams& p, int mt, int grid, size_t lds, hipStream_t s);
+hipError_t launch_fused_bf16(const LinParams& p, int mt, int grid, size_t lds, hipStream_t s);
+// Steps staged per chunk for this shape (all steps when the operand fits in registers and
+// LDS) and the dynamic LDS bytes the launch needs.
+int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K);
+size_t fused_lds_bytes(int bits, int rows, int chunk_steps, long K, int mt);
+
+hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bits, uint32_t* codes, uint16_t* scales,
+                       uint16_t* biases, int32_t* flag, hipStream_t s);
+hipError_t launch_unpack(const void* data, const uint16_t* scales, const uint16_t* biases, int bits,
+                         int dtype, int64_t N, int64_t K, float* out, hipStream_t s);
+
+}  // namespace qlin

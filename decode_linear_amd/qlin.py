@@ -1,0 +1,248 @@
+"""Python binding of libqlin (include/qlin.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels; PyTorch supplies device
+memory and the current HIP stream.  The names follow the C ABI:
+qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
+qlin_check, qlin_status_string, qlin_dispatch_count, and the chain calls
+(QlinChain wraps qlin_chain_create / launch / destroy).
+
+There is no fallback: if libqlin.so is missing or a call fails, this raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlin.so")
+
+QLIN_F32, QLIN_F16, QLIN_BF16 = 0, 1, 2
+QLIN_ACT_NONE, QLIN_ACT_GELU = 0, 1
+STATUS = {0: "QLIN_OK", -1: "QLIN_ERR_NULL", -2: "QLIN_ERR_SHAPE", -3: "QLIN_ERR_DTYPE", -4: "QLIN_ERR_BITS",
+          -5: "QLIN_ERR_ALIGN", -6: "QLIN_ERR_HIP", -7: "QLIN_ERR_ARG"}
+
+_TORCH_TO_QLIN = {torch.float32: QLIN_F32, torch.float16: QLIN_F16, torch.bfloat16: QLIN_BF16}
+_QLIN_TO_TORCH = {v: k for k, v in _TORCH_TO_QLIN.items()}
+
+
+class QlinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({qlin_status_string(status)})")
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class _Ln(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+class _Pass(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("T", ctypes.c_int32), ("w", _Weight), ("ln_gamma", ctypes.c_void_p),
+                ("ln_beta", ctypes.c_void_p), ("ln_eps", ctypes.c_float), ("act", ctypes.c_int32),
+                ("residual", ctypes.c_void_p), ("add", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqlin.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libqlin.so not found at {LIB_PATH}; build it with decode_linear_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    W, Ln = ctypes.POINTER(_Weight), ctypes.POINTER(_Ln)
+    L.qlin_linear.argtypes = [vp, i32, i32, W, Ln, i32, vp, vp, vp, i32, vp]
+    L.qlin_gateup_swiglu.argtypes = [vp, i32, i32, W, W, Ln, vp, i32, vp]
+    L.qlin_pack_affine.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp]
+    L.qlin_unpack_affine.argtypes = [W, vp, vp]
+    L.qlin_check.argtypes = [vp, i32, i32, W, W, Ln, i32, vp, vp, vp, i32]
+    L.qlin_chain_create.argtypes = [ctypes.POINTER(_Pass), i32, i32, i32, vp, ctypes.POINTER(vp)]
+    L.qlin_chain_launch.argtypes = [vp, vp]
+    L.qlin_chain_passes.argtypes = [vp]
+    L.qlin_chain_destroy.argtypes = [vp]
+    L.qlin_chain_destroy.restype = None
+    L.qlin_dispatch_count.argtypes = [i32]
+    L.qlin_dispatch_count.restype = i64
+    L.qlin_status_string.argtypes = [i32]
+    L.qlin_status_string.restype = ctypes.c_char_p
+    for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
+                 "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def qlin_status_string(status: int) -> str:
+    return lib().qlin_status_string(int(status)).decode()
+
+
+def qlin_dispatch_count(which: int) -> int:
+    return int(lib().qlin_dispatch_count(int(which)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _TORCH_TO_QLIN:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _TORCH_TO_QLIN[t.dtype]
+
+
+@dataclass
+class QWeight:
+    """A weight in the library's format.  bits 16: data (N, K) fp16/bf16; bits 8/4: data
+    (N, K*bits/32) int32 words (bit pattern of uint32), scales/biases (N, K/64) fp16."""
+    bits: int
+    N: int
+    K: int
+    data: torch.Tensor
+    scales: Optional[torch.Tensor] = None
+    biases: Optional[torch.Tensor] = None
+
+    def c(self) -> _Weight:
+        if self.bits == 16:
+            dt = _dtype(self.data)
+        else:
+            dt = QLIN_F16 if self.scales is None else _dtype(self.scales)
+        return _Weight(self.bits, 64, self.N, self.K, dt, self.data.data_ptr() if self.data.numel() else None,
+                       None if self.scales is None else self.scales.data_ptr(),
+                       None if self.biases is None else self.biases.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        n = self.data.numel() * self.data.element_size()
+        for t in (self.scales, self.biases):
+            if t is not None:
+                n += t.numel() * t.element_size()
+        return n
+
+
+def _ln(ln) -> Optional[_Ln]:
+    if ln is None:
+        return None
+    gamma, beta, eps = ln
+    return _Ln(gamma.data_ptr(), beta.data_ptr(), float(eps))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QlinError(status, where)
+
+
+def qlin_linear(x: torch.Tensor, w: QWeight, ln=None, act: int = QLIN_ACT_NONE,
+                residual: Optional[torch.Tensor] = None, add: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+    """y (T, N) = [add +] [residual +] act(LN?(x) @ W.T).  ln = (gamma, beta, eps) or None."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, w.N), dtype=out_dtype or x.dtype, device=x.device)
+    lnc = _ln(ln)
+    wc = w.c()
+    st = lib().qlin_linear(_ptr(x), _dtype(x), T, ctypes.byref(wc), None if lnc is None else ctypes.byref(lnc),
+                           int(act), _ptr(residual), _ptr(add), _ptr(out), _dtype(out), _stream(stream))
+    _check(st, "qlin_linear")
+    return out
+
+
+def qlin_gateup_swiglu(x: torch.Tensor, gate: QWeight, up: QWeight, ln=None, out: Optional[torch.Tensor] = None,
+                       out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+    """y (T, N) = silu(LN?(x) @ Wg.T) * (LN?(x) @ Wu.T)."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, gate.N), dtype=out_dtype or x.dtype, device=x.device)
+    lnc = _ln(ln)
+    gc, uc = gate.c(), up.c()
+    st = lib().qlin_gateup_swiglu(_ptr(x), _dtype(x), T, ctypes.byref(gc), ctypes.byref(uc),
+                                  None if lnc is None else ctypes.byref(lnc), _ptr(out), _dtype(out), _stream(stream))
+    _check(st, "qlin_gateup_swiglu")
+    return out
+
+
+def qlin_pack_affine(w: torch.Tensor, bits: int, flag: Optional[torch.Tensor] = None, stream=None) -> QWeight:
+    """Quantize an fp32 (N, K) device tensor to the affine group-64 format."""
+    N, K = w.shape
+    dev = w.device
+    codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.empty((N, K // 64), dtype=torch.float16, device=dev)
+    biases = torch.empty((N, K // 64), dtype=torch.float16, device=dev)
+    st = lib().qlin_pack_affine(_ptr(w), N, K, bits, 64, _ptr(codes), _ptr(scales), _ptr(biases), QLIN_F16,
+                                _ptr(flag), _stream(stream))
+    _check(st, "qlin_pack_affine")
+    return QWeight(bits, N, K, codes, scales, biases)
+
+
+def qlin_unpack_affine(w: QWeight, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp32 (N, K) = fmaf(q, s, b) (or the widened dense element)."""
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.data.device)
+    wc = w.c()
+    st = lib().qlin_unpack_affine(ctypes.byref(wc), _ptr(out), _stream(stream))
+    _check(st, "qlin_unpack_affine")
+    return out
+
+
+def qlin_check(x_ptr, x_dtype: int, T: int, w: _Weight, up: Optional[_Weight] = None, ln: Optional[_Ln] = None,
+               act: int = 0, residual=None, add=None, y_ptr=None, y_dtype: int = QLIN_BF16) -> int:
+    """Validation only (no GPU needed).  Takes raw ctypes structs / addresses."""
+    return int(lib().qlin_check(x_ptr, x_dtype, T, ctypes.byref(w), None if up is None else ctypes.byref(up),
+                                None if ln is None else ctypes.byref(ln), act, residual, add, y_ptr, y_dtype))
+
+
+class QlinChain:
+    """A hipGraph of dependent qlin_linear passes (qlin_chain_create / launch / destroy).
+
+    passes: dicts with keys x, T, w (QWeight), ln (tuple or None), act, residual, add, y."""
+
+    def __init__(self, passes: Sequence[dict], x_dtype: torch.dtype, y_dtype: torch.dtype, capture_stream=None):
+        self._keep = list(passes)
+        arr = (_Pass * len(passes))()
+        for i, ps in enumerate(passes):
+            ln = ps.get("ln")
+            arr[i] = _Pass(ps["x"].data_ptr(), ps["T"], ps["w"].c(), None if ln is None else ln[0].data_ptr(),
+                           None if ln is None else ln[1].data_ptr(), 0.0 if ln is None else float(ln[2]),
+                           int(ps.get("act", 0)), None if ps.get("residual") is None else ps["residual"].data_ptr(),
+                           None if ps.get("add") is None else ps["add"].data_ptr(), ps["y"].data_ptr())
+        self._stream = capture_stream or torch.cuda.Stream()
+        handle = ctypes.c_void_p()
+        st = lib().qlin_chain_create(arr, len(passes), _TORCH_TO_QLIN[x_dtype], _TORCH_TO_QLIN[y_dtype],
+                                     _stream(self._stream), ctypes.byref(handle))
+        _check(st, "qlin_chain_create")
+        self._h = handle
+
+    @property
+    def passes(self) -> int:
+        return int(lib().qlin_chain_passes(self._h))
+
+    def launch(self, stream=None):
+        _check(lib().qlin_chain_launch(self._h, _stream(stream)), "qlin_chain_launch")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().qlin_chain_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,183 @@
+/*
+ * qlin.h — C ABI of libqlin, the MI355X (gfx950) decode-time fused quantized linear.
+ *
+ * The operation ([p1] maya-mac src/maya_mac/mlx_kernels.py, module docstring and the
+ * `linear` docstring):
+ *
+ *     y = [add +] [res +] act( LN?(x) . dequant(W)^T )          x: (T, K), W: (N, K), y: (T, N)
+ *
+ * for a few activation rows (1 <= T <= 32) against either a dense fp16/bf16 W or affine
+ * group-quantized codes: 8-bit or 4-bit unsigned codes q with one fp16 scale s and one
+ * fp16 bias b per group of 64 consecutive k, W[n, k] = q * s[n, k/64] + b[n, k/64]
+ * ([p1] the 8-bit load of `_linear_kernel`; [p3] mlx-bun 0.0.10 -> 0.0.12,
+ * model/fused-decode-kernel.ts for the 4-bit layout).  The optional LayerNorm prologue
+ * (biased variance, eps inside the square root) is folded into the weight stream with the
+ * single-pass shifted statistics ([p1] `_linear_kernel` docstring).  The epilogue applies,
+ * in this order, exact-erf GELU, the residual row and the per-column constant ([p1] the
+ * epilogue of `_linear_kernel`).  qlin_gateup_swiglu computes silu(x.Wg^T) * (x.Wu^T) over
+ * one read of x ([p2] @mlx-bun/inference 0.0.0-stage -> 1.0.0, kernels/trellis/
+ * mixed-gate-up.ts).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc or a torch CUDA tensor's
+ *     data_ptr) unless stated otherwise; all arrays are dense and row-major.
+ *   - The caller allocates and owns every buffer; inputs are only read (borrowed).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.  Calls only
+ *     enqueue work on it and return: no allocation, no synchronization, no device query
+ *     after the first call on a device, so they may be recorded into a hipGraph.
+ *   - Arguments are validated on the host before any HIP call.  On any error the function
+ *     returns a negative qlin_status, enqueues nothing and leaves every output untouched.
+ *     Nothing is thrown across the ABI.
+ *   - Results are deterministic: the same inputs give bitwise-identical outputs (no
+ *     floating-point atomics; every cross-lane and cross-wave sum has a fixed order).
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLIN_OK = 0,
+  QLIN_ERR_NULL = -1,   /* a required pointer is NULL */
+  QLIN_ERR_SHAPE = -2,  /* T, K or N outside the accepted range */
+  QLIN_ERR_DTYPE = -3,  /* unsupported or inconsistent dtype */
+  QLIN_ERR_BITS = -4,   /* bits not in {4, 8, 16} or group_size != 64 */
+  QLIN_ERR_ALIGN = -5,  /* a pointer does not have the required alignment */
+  QLIN_ERR_HIP = -6,    /* the HIP runtime reported an error */
+  QLIN_ERR_ARG = -7     /* any other invalid argument (act code, eps, n_passes, ...) */
+} qlin_status;
+
+typedef enum { QLIN_F32 = 0, QLIN_F16 = 1, QLIN_BF16 = 2 } qlin_dtype;
+
+typedef enum { QLIN_ACT_NONE = 0, QLIN_ACT_GELU = 1 } qlin_act;
+
+/* A weight matrix W of N output rows and K input columns (y = x . W^T).
+ *   bits == 16: dense; `data` holds N*K elements of `dtype` (QLIN_F16 or QLIN_BF16, and it
+ *               must equal the activation dtype); scales and biases are ignored (may be NULL).
+ *   bits == 8 or 4: `data` holds N rows of K*bits/32 uint32 words; within a row, code k sits
+ *               in word k/(32/bits) at bits bits*(k mod (32/bits)) (low bits first).
+ *               `scales` and `biases` hold N rows of K/64 fp16 values; `dtype` must be
+ *               QLIN_F16 (the scale/bias dtype).
+ * group_size must be 64.  K must be a positive multiple of 64.
+ * Alignment: data 16 bytes; scales and biases 2 bytes. */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int64_t N;
+  int64_t K;
+  int32_t dtype;
+  const void* data;
+  const void* scales;
+  const void* biases;
+} qlin_weight;
+
+/* LayerNorm prologue parameters: gamma and beta hold K elements of the activation dtype
+ * (16-byte aligned); eps > 0 is added to the biased variance before the square root
+ * (eps == 0 is accepted too). */
+typedef struct {
+  const void* gamma;
+  const void* beta;
+  float eps;
+} qlin_ln;
+
+/* y = [add +] [res +] act( LN?(x) . dequant(w)^T )
+ *   x         (T, K) of x_dtype (QLIN_F16 or QLIN_BF16), 16-byte aligned.
+ *   T         number of activation rows, 0 <= T <= 32 (T == 0 is a no-op).
+ *   w         the weight, w->N >= 0 (N == 0 is a no-op), w->K == the row length of x.
+ *   ln        NULL for no LayerNorm, else the prologue parameters.
+ *   act       QLIN_ACT_NONE or QLIN_ACT_GELU (0.5 v (1 + erf(v / sqrt 2))).
+ *   residual  NULL or (T, N) of x_dtype, added after the activation.
+ *   add       NULL or (N,) of x_dtype, added last.
+ *   y         (T, N) of y_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16), written with one
+ *             round-to-nearest-even from an fp32 value; it must not overlap x or residual.
+ *   stream    hipStream_t as void*.
+ * Accumulation is fp32; activations enter the contraction with at least 22 significant
+ * bits.  Returns QLIN_OK once the work is enqueued. */
+qlin_status qlin_linear(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w,
+                        const qlin_ln* ln, qlin_act act, const void* residual, const void* add,
+                        void* y, qlin_dtype y_dtype, void* stream);
+
+/* y = silu(LN?(x) . gate^T) * (LN?(x) . up^T), silu(g) = g / (1 + e^-g), computed in fp32
+ * and rounded once to y_dtype.  gate and up must have the same bits, group size, N, K and
+ * dtype.  Other arguments as in qlin_linear; y is (T, N). */
+qlin_status qlin_gateup_swiglu(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* gate,
+                               const qlin_weight* up, const qlin_ln* ln, void* y, qlin_dtype y_dtype,
+                               void* stream);
+
+/* Quantize an fp32 (N, K) matrix w (device, 16-byte aligned) to the affine format above.
+ * For each row n and group of 64 consecutive k, in IEEE binary32 with ties to even:
+ *     lo = min, hi = max;  s = fp16(fl32(fl32(hi - lo) / (2^bits - 1)));  b = fp16(lo);
+ *     q = s == 0 ? 0 : clamp(rint(fl32(fl32(w - b) / s)), 0, 2^bits - 1)
+ * (the pages do not print their quantizer; this is the library's definition).  A group
+ * that holds a NaN or infinity, or whose s or b overflows fp16, is written as q = 0,
+ * s = +0, b = fp16 NaN (0x7E00), and *nonfinite_flag (a device int, may be NULL) is set
+ * to 1; the flag is never cleared by this call.
+ *   codes   (N, K*bits/32) uint32, 16-byte aligned;  scales, biases (N, K/64) of sb_dtype.
+ *   bits    4 or 8;  group_size 64;  sb_dtype QLIN_F16. */
+qlin_status qlin_pack_affine(const float* w, int64_t N, int64_t K, int32_t bits, int32_t group_size,
+                             uint32_t* codes, void* scales, void* biases, qlin_dtype sb_dtype,
+                             int32_t* nonfinite_flag, void* stream);
+
+/* Dequantize w into out (N, K) fp32 (device): out = fmaf(q, s, b) with one rounding for
+ * quantized weights, or the widened element for dense ones.  Test and diagnostic use. */
+qlin_status qlin_unpack_affine(const qlin_weight* w, float* out, void* stream);
+
+/* Validation only: returns what qlin_linear / qlin_gateup_swiglu would return for these
+ * arguments without enqueueing anything (the "is this call servable" predicate).  `up`
+ * is NULL for a plain linear.  Needs no GPU. */
+qlin_status qlin_check(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w,
+                       const qlin_weight* up, const qlin_ln* ln, qlin_act act, const void* residual,
+                       const void* add, const void* y, qlin_dtype y_dtype);
+
+/* One pass of a chain of dependent fused linears ([p1] module docstring: the depth decoder
+ * runs 124 small dependent layer passes per frame).  Fields as in qlin_linear; ln_gamma
+ * NULL means no LayerNorm. */
+typedef struct {
+  const void* x;
+  int32_t T;
+  qlin_weight w;
+  const void* ln_gamma;
+  const void* ln_beta;
+  float ln_eps;
+  int32_t act;
+  const void* residual;
+  const void* add;
+  void* y;
+} qlin_pass;
+
+typedef struct qlin_chain qlin_chain;
+
+/* Record n_passes (>= 1) fused linears, in order, into one hipGraph by stream capture on
+ * `capture_stream` (which must not be capturing already) and instantiate it.  Every pass
+ * is validated first; on error nothing is recorded and *out is NULL.  The pass array is
+ * copied; the device buffers it names must stay valid while the chain is used.  Allocates
+ * host and graph memory (a setup call, not capture-safe itself).  Returns QLIN_ERR_HIP if
+ * capture or instantiation fails. */
+qlin_status qlin_chain_create(const qlin_pass* passes, int32_t n_passes, qlin_dtype x_dtype,
+                              qlin_dtype y_dtype, void* capture_stream, qlin_chain** out);
+
+/* Launch the recorded chain once on `stream` (asynchronous). */
+qlin_status qlin_chain_launch(qlin_chain* chain, void* stream);
+
+/* Number of passes recorded in `chain` (0 for NULL). */
+int32_t qlin_chain_passes(const qlin_chain* chain);
+
+/* Release the graph and its host memory.  NULL is ignored. */
+void qlin_chain_destroy(qlin_chain* chain);
+
+/* Number of kernels this library has enqueued in this process, by entry point:
+ * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack (a test can assert a kernel ran). */
+int64_t qlin_dispatch_count(int32_t which);
+
+/* Static description of a status code. */
+const char* qlin_status_string(qlin_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

@@ -1,0 +1,168 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/qlin.h declares, and rejects bad arguments on the host before any HIP call
+(status codes only; nothing is launched, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_linear_amd import build as qbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    qbuild.ensure_built()
+    from decode_linear_amd import qlin
+    return qlin
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qlin.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlin_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
+                 "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
+                 "qlin_dispatch_count"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(q):
+    lib = q.lib()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(q):
+    for s in range(-7, 1):
+        assert q.qlin_status_string(s)
+    assert q.qlin_status_string(0) == "ok"
+
+
+# fake, suitably aligned device addresses: validation never dereferences them
+X, W, S, B, Y, G, BE, R = (0x10000 * i for i in range(1, 9))
+
+
+def _w(q, bits=8, N=256, K=1024, dtype=None, data=W, scales=S, biases=B, group=64):
+    if dtype is None:
+        dtype = q.QLIN_F16
+    return q._Weight(bits, group, N, K, dtype, data, scales, biases)
+
+
+def _chk(q, T=4, w=None, up=None, ln=None, act=0, res=None, add=None, x=X, y=Y, x_dtype=None, y_dtype=None):
+    x_dtype = q.QLIN_BF16 if x_dtype is None else x_dtype
+    y_dtype = q.QLIN_BF16 if y_dtype is None else y_dtype
+    return q.qlin_check(x, x_dtype, T, w if w is not None else _w(q), up, ln, act, res, add, y, y_dtype)
+
+
+def test_valid_calls_pass(q):
+    assert _chk(q) == 0
+    assert _chk(q, T=32, ln=q._Ln(G, BE, 1e-5), act=1, res=R, add=R + 0x100000) == 0
+    assert _chk(q, w=_w(q, bits=4)) == 0
+    assert _chk(q, w=_w(q, bits=16, dtype=q.QLIN_BF16)) == 0
+    assert _chk(q, w=_w(q), up=_w(q)) == 0
+    assert _chk(q, y_dtype=q.QLIN_F32) == 0
+
+
+def test_empty_problems_are_no_ops(q):
+    assert _chk(q, T=0, x=None, y=None) == 0
+    assert _chk(q, w=_w(q, N=0, data=None, scales=None, biases=None), x=X) == 0
+
+
+@pytest.mark.parametrize("T", [-1, 33, 1000])
+def test_bad_T(q, T):
+    assert _chk(q, T=T) == -2
+
+
+@pytest.mark.parametrize("K", [0, 32, 100, 1 << 21])
+def test_bad_K(q, K):
+    assert _chk(q, w=_w(q, K=K)) == -2
+
+
+def test_bad_N(q):
+    assert _chk(q, w=_w(q, N=-5)) == -2
+
+
+@pytest.mark.parametrize("bits", [0, 2, 3, 5, 12, 32])
+def test_bad_bits(q, bits):
+    assert _chk(q, w=_w(q, bits=bits)) == -4
+
+
+def test_bad_group(q):
+    assert _chk(q, w=_w(q, group=32)) == -4
+    assert _chk(q, w=_w(q, group=128)) == -4
+
+
+def test_dtypes(q):
+    assert _chk(q, x_dtype=q.QLIN_F32) == -3                    # activations must be 16-bit
+    assert _chk(q, x_dtype=7) == -3
+    assert _chk(q, y_dtype=5) == -3
+    assert _chk(q, w=_w(q, bits=16, dtype=q.QLIN_F16)) == -3   # dense W must match x (bf16 here)
+    assert _chk(q, w=_w(q, bits=8, dtype=q.QLIN_BF16)) == -3   # scales/biases are fp16
+
+
+def test_null_pointers(q):
+    assert _chk(q, x=None) == -1
+    assert _chk(q, y=None) == -1
+    assert _chk(q, w=_w(q, data=None)) == -1
+    assert _chk(q, w=_w(q, scales=None)) == -1
+    assert _chk(q, ln=q._Ln(None, BE, 1e-5)) == -1
+    assert q.lib().qlin_check(X, q.QLIN_BF16, 4, None, None, None, 0, None, None, Y, q.QLIN_BF16) == -1
+
+
+def test_alignment(q):
+    assert _chk(q, x=X + 2) == -5
+    assert _chk(q, w=_w(q, data=W + 4)) == -5
+    assert _chk(q, w=_w(q, scales=S + 1)) == -5
+    assert _chk(q, ln=q._Ln(G + 8, BE, 1e-5)) == -5
+    assert _chk(q, y=Y + 1) == -5
+    assert _chk(q, y=Y + 2, y_dtype=q.QLIN_F32) == -5
+
+
+def test_bad_act_eps_and_gateup_extras(q):
+    assert _chk(q, act=2) == -7
+    assert _chk(q, ln=q._Ln(G, BE, -1.0)) == -7
+    assert _chk(q, ln=q._Ln(G, BE, float("nan"))) == -7
+    assert _chk(q, w=_w(q), up=_w(q), act=1) == -7
+    assert _chk(q, w=_w(q), up=_w(q), res=R) == -7
+
+
+def test_gateup_shape_mismatch(q):
+    assert _chk(q, w=_w(q), up=_w(q, N=128)) == -2
+    assert _chk(q, w=_w(q), up=_w(q, bits=4)) == -4
+
+
+def test_output_overlapping_input_rejected(q):
+    assert _chk(q, y=X + 16) == -7
+    assert _chk(q, res=Y, y=Y) == -7
+
+
+def test_invalid_linear_call_returns_before_any_hip_call(q):
+    # an invalid call goes through the real entry point without needing a device
+    w = _w(q, K=100)
+    st = q.lib().qlin_linear(X, q.QLIN_BF16, 4, ctypes.byref(w), None, 0, None, None, Y, q.QLIN_BF16, None)
+    assert st == -2
+    st = q.lib().qlin_pack_affine(None, 4, 64, 3, 64, None, None, None, q.QLIN_F16, None, None)
+    assert st == -4
+    st = q.lib().qlin_pack_affine(None, 4, 64, 8, 64, None, None, None, q.QLIN_F16, None, None)
+    assert st == -1
+
+
+def test_chain_argument_errors(q):
+    h = ctypes.c_void_p()
+    assert q.lib().qlin_chain_create(None, 1, 2, 2, None, ctypes.byref(h)) == -1
+    arr = (q._Pass * 1)()
+    assert q.lib().qlin_chain_create(arr, 0, 2, 2, ctypes.c_void_p(1), ctypes.byref(h)) == -7
+    assert q.lib().qlin_chain_passes(None) == 0
+    q.lib().qlin_chain_destroy(None)
+
+
+def test_dispatch_counter_range(q):
+    assert q.qlin_dispatch_count(4) == -1
+    assert q.qlin_dispatch_count(0) >= 0
