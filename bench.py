@@ -1,0 +1,298 @@
+"""Benchmark of the decode-time fused quantized linear on one MI355X.
+
+Metric: weight-stream HBM GB/s (and % of the 8 TB/s MI355X peak) and us per fused call.
+The headline workload is the largest single call, the 4-bit SwiGLU gate+up projection
+(M=4 rows, K=4096, N=14336 per projection, affine group 64, fp16 scale/bias).  One
+"step" is one qlin_gateup_swiglu call over one batch of synthetic input.
+
+Weight bytes per call are the algorithmic weight stream: codes + scales + biases of both
+projections, each byte read once (activations and outputs are reported separately).
+Weights rotate over enough copies to total >= 1 GiB, so the 256 MB Infinity Cache cannot
+serve them; everything is resident in HBM before the timed region.  Time comes from HIP
+events recorded on the stream the kernels are launched on, bracketing the timed steps
+(warmup steps first), with device synchronization on both sides.
+
+Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
+with 32 rows) and the 124-pass LN+linear chain (hipGraph replay vs eager launches), and a
+CPU baseline: the fp64 oracle timed on the host on a bounded sample of the workload.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--only-main]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ROTATE_BYTES = 1 << 30         # weights rotate over at least this many bytes
+METRIC = "weight-stream HBM GB/s and % of MI355X peak; µs per fused linear call"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-main", action="store_true", help="time only the headline workload")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="instead: run a plain device copy of this many bytes (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _time_calls(fn, n_copies, steps, warmup):
+    """Run fn(i) for warmup then timed steps (i cycles over the weight copies); returns
+    total ms of the timed steps from events on the current stream."""
+    torch = _torch()
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn((warmup + i) % n_copies)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def _rotated(make, nbytes):
+    """Enough independent copies of a weight set to total >= ROTATE_BYTES."""
+    n = max(2, -(-ROTATE_BYTES // nbytes))
+    first = make()
+    return [first] + [tuple(w.clone() for w in first) if isinstance(first, tuple) else first.clone()
+                      for _ in range(n - 1)]
+
+
+def _clone_q(q):
+    from decode_linear_amd import QWeight
+    return QWeight(q.bits, q.N, q.K, q.data.clone(), None if q.scales is None else q.scales.clone(),
+                   None if q.biases is None else q.biases.clone())
+
+
+def _dev(bits_arr, dtype):
+    torch = _torch()
+    import synth
+    if dtype == synth.F32:
+        return torch.from_numpy(np.ascontiguousarray(bits_arr, np.float32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(bits_arr, np.uint16).view(np.int16))
+    return t.view(torch.float16 if dtype == synth.F16 else torch.bfloat16).cuda()
+
+
+def _pack(w_f32, bits):
+    from decode_linear_amd import qlin_pack_affine
+    torch = _torch()
+    wd = torch.from_numpy(w_f32).cuda()
+    q = qlin_pack_affine(wd, bits)
+    del wd
+    return q
+
+
+def bench_swiglu(steps, warmup):
+    import synth
+    from decode_linear_amd import qlin_gateup_swiglu
+    torch = _torch()
+    case = synth.workload(4)
+    g0, u0 = _pack(case.gate, 4), _pack(case.up, 4)
+    del case.gate, case.up
+    wbytes = g0.nbytes + u0.nbytes
+    n_copies = max(2, -(-ROTATE_BYTES // wbytes))
+    weights = [(g0, u0)] + [(_clone_q(g0), _clone_q(u0)) for _ in range(n_copies - 1)]
+    x = _dev(case.x, case.x_dtype)
+    y = torch.empty((case.T, case.N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        g, u = weights[i]
+        qlin_gateup_swiglu(x, g, u, out=y)
+
+    ms = _time_calls(step, n_copies, steps, warmup)
+    us = ms * 1e3 / steps
+    other = case.x.size * 2 + y.numel() * 2
+    return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=4, weight_bytes=wbytes, other_bytes=other,
+                copies=n_copies, us=us, gbs=wbytes / (us * 1e-6) / 1e9)
+
+
+def bench_linear(c, steps, warmup):
+    import synth
+    from decode_linear_amd import QWeight, qlin_linear
+    torch = _torch()
+    case = synth.workload(c)
+    if case.bits == 16:
+        q0 = QWeight(16, case.N, case.K, _dev(case.w_dense, case.w_dtype))
+    else:
+        q0 = _pack(case.w_f32, case.bits)
+    wbytes = q0.nbytes
+    n_copies = max(2, -(-ROTATE_BYTES // wbytes))
+    weights = [q0] + [_clone_q(q0) for _ in range(n_copies - 1)]
+    x = _dev(case.x, case.x_dtype)
+    ln = None if case.gamma is None else (_dev(case.gamma, case.x_dtype), _dev(case.beta, case.x_dtype), case.eps)
+    res = None if case.res is None else _dev(case.res, case.x_dtype)
+    y = torch.empty((case.T, case.N), dtype=torch.float16 if case.y_dtype == synth.F16 else torch.bfloat16,
+                    device="cuda")
+
+    def step(i):
+        qlin_linear(x, weights[i], ln=ln, act=case.act, residual=res, out=y)
+
+    ms = _time_calls(step, n_copies, steps, warmup)
+    us = ms * 1e3 / steps
+    return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=case.bits, weight_bytes=wbytes, copies=n_copies,
+                us=us, gbs=wbytes / (us * 1e-6) / 1e9)
+
+
+def bench_chain(replays, warmup):
+    """124 dependent LN + linear passes (8-bit, K=N=1024, T = 1 + p mod 8): graph replay
+    and eager launches, rotated over >= 1 GiB of chain copies."""
+    import synth
+    from decode_linear_amd import QlinChain, qlin_linear
+    torch = _torch()
+    P = synth.CHAIN_PASSES
+    B0 = _dev(synth.chain_buffers(), synth.BF16)
+    base = []
+    for p in range(P):
+        w, g, b = synth.chain_pass(p)
+        base.append((_pack(w, 8), _dev(g, synth.BF16), _dev(b, synth.BF16)))
+    chain_bytes = sum(q.nbytes for q, _, _ in base)
+    n_copies = max(2, -(-ROTATE_BYTES // chain_bytes))
+    copies = [base] + [[(_clone_q(q), g, b) for q, g, b in base] for _ in range(n_copies - 1)]
+    bufs = [B0.clone() for _ in range(n_copies)]
+    chains = []
+    for cp, B in zip(copies, bufs):
+        ps = [dict(x=B[p, :synth.chain_T(p)], T=synth.chain_T(p), w=q, ln=(g, b, 1e-5), y=B[p + 1, :synth.chain_T(p)])
+              for p, (q, g, b) in enumerate(cp)]
+        chains.append(QlinChain(ps, torch.bfloat16, torch.bfloat16))
+    ms_graph = _time_calls(lambda i: chains[i].launch(), n_copies, replays, warmup)
+
+    def eager(i):
+        B = bufs[i]
+        for p, (q, g, b) in enumerate(copies[i]):
+            T = synth.chain_T(p)
+            qlin_linear(B[p, :T], q, ln=(g, b, 1e-5), out=B[p + 1, :T])
+
+    ms_eager = _time_calls(eager, n_copies, max(1, replays // 2), max(1, warmup // 2))
+    for ch in chains:
+        ch.close()
+    us_graph = ms_graph * 1e3 / replays / P
+    us_eager = ms_eager * 1e3 / max(1, replays // 2) / P
+    per_pass = chain_bytes / P
+    return dict(name="chain-124-ln-q8-K1024-N1024", passes=P, weight_bytes_per_pass=per_pass, copies=n_copies,
+                us_per_pass_graph=us_graph, us_per_pass_eager=us_eager,
+                us_per_frame_graph=us_graph * P, gbs_graph=per_pass / (us_graph * 1e-6) / 1e9)
+
+
+def cpu_baseline(target_s):
+    """The oracle (plain fp64 C++, untuned) on the host: the SwiGLU workload restricted to
+    its first Ns output rows per projection, called repeatedly from one thread per core
+    until about target_s seconds of wall time; reported in weight GB/s of that sample."""
+    import oracle
+    import synth
+    case = synth.workload(4, scale_n=1024)      # same distributions; N cut to the sample
+    gw = oracle.pack_affine(case.gate, 4)
+    uw = oracle.pack_affine(case.up, 4)
+    Ns, K = case.N, case.K
+    wbytes = 2 * (Ns * K // 2 + 2 * Ns * (K // 64) * 2)
+    t0 = time.time()
+    oracle.gateup(case.x, case.x_dtype, 4, gw[:3], uw[:3])
+    one = time.time() - t0
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    per_thread = max(1, int(target_s / max(one, 1e-3) / 1.5))
+    done = [0] * threads
+
+    def work(k):
+        for _ in range(per_thread):
+            oracle.gateup(case.x, case.x_dtype, 4, gw[:3], uw[:3])
+            done[k] += 1
+
+    t0 = time.time()
+    ts = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    wall = time.time() - t0
+    calls = sum(done)
+    return {"value": round(calls * wbytes / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"SwiGLU workload cut to N={Ns} rows per projection (K=4096, 4-bit): {calls} oracle calls "
+                      f"on {threads} host threads in {wall:.1f} s; {one * 1e3:.0f} ms per call single-threaded",
+            "us_per_call_full_workload_est": round(one * (14336 / Ns) * 1e6, 1)}
+
+
+def copy_probe(nbytes):
+    torch = _torch()
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}))
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": a.gpus}))
+        sys.exit(2)
+    from decode_linear_amd import build
+    build.ensure_built()
+    torch = _torch()
+    torch.cuda.init()
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
+    main_r = bench_swiglu(a.steps, a.warmup)
+    extra = {}
+    if not a.only_main:
+        for c in (1, 2, 3):
+            r = bench_linear(c, a.steps, a.warmup)
+            extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
+            extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
+        ch = bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))
+        extra[ch["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ch.items() if k != "name"}
+    us = main_r["us"]
+    achieved = main_r["weight_bytes"] / (us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(main_r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": main_r["name"], "rows": main_r["T"], "K": main_r["K"], "N_per_projection": main_r["N"],
+                   "weights": "4-bit affine, group 64, fp16 scale/bias", "activations": "bf16",
+                   "weight_bytes_per_call": main_r["weight_bytes"], "rotation_copies": main_r["copies"]},
+        "us_per_call": round(us, 3),
+        "pct_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if extra:
+        line["workloads"] = extra
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

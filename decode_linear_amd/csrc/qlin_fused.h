@@ -98,14 +98,22 @@ __device__ __forceinline__ uint32_t bytes_to_h2(uint32_t d, uint32_t sel) {
   return __builtin_bit_cast(uint32_t, v);
 }
 // Nibbles 0 and 4 of d (bits 0-3 and 16-19) -> fp16 integers.
+// (a & mask) | magic as one v_and_or_b32.  gfx9 VOP3 cannot encode 32-bit literals, so
+// without this the compiler emits a separate v_and and v_or; the mask goes in an SGPR and
+// the magic constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
 __device__ __forceinline__ uint32_t nib_lo_to_h2(uint32_t d) {
-  const uint32_t h = (d & 0x000F000Fu) | 0x64006400u;
+  const uint32_t h = and_or(d, 0x000F000Fu, 0x64006400u);
   const h2_t v = __builtin_bit_cast(h2_t, h) - (h2_t){(_Float16)1024.0f, (_Float16)1024.0f};
   return __builtin_bit_cast(uint32_t, v);
 }
 // Nibbles 1 and 5 (bits 4-7 and 20-23): 1024 + 16 n, scaled back exactly: (1024+16n)/16 - 64.
 __device__ __forceinline__ uint32_t nib_hi_to_h2(uint32_t d) {
-  const uint32_t h = (d & 0x00F000F0u) | 0x64006400u;
+  const uint32_t h = and_or(d, 0x00F000F0u, 0x64006400u);
   const h2_t v = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, h), (h2_t){(_Float16)0.0625f, (_Float16)0.0625f},
                                            (h2_t){(_Float16)-64.0f, (_Float16)-64.0f});
   return __builtin_bit_cast(uint32_t, v);
@@ -150,6 +158,24 @@ template <bool BF16OP> __device__ __forceinline__ float op_bits_to_float(uint32_
   else return half_bits_to_float(h);
 }
 
+// Global-memory pointers: loads through them are global_load (vmcnt only), never flat.
+#define QLIN_GLOBAL __attribute__((address_space(1)))
+template <typename T> using gptr = T QLIN_GLOBAL*;
+
+// Zero-filled device memory that masked-off lanes load from, so that every path through the
+// tile loader issues the same loads (the compiler's wait counting stays exact across tiles).
+// 1 KiB: every per-step offset of a tile's loads (at most 8 steps of 64 bytes plus a lane's
+// 48) stays inside it.
+static __device__ __attribute__((aligned(64))) uint32_t g_zero16[256];
+
+// Pick one of two pointers without indexing the kernel-argument struct by a per-lane value
+// (that would turn into a vector load of the pointer and a full memory wait).
+template <typename P>
+__device__ __forceinline__ gptr<P> pick(P* a, P* b, int second) {
+  const uintptr_t ua = reinterpret_cast<uintptr_t>(a), ub = reinterpret_cast<uintptr_t>(b);
+  return reinterpret_cast<gptr<P>>(ua + (uintptr_t)second * (ub - ua));
+}
+
 __device__ __forceinline__ void store_out(void* y, int dtype, long idx, float v) {
   if (dtype == 0) reinterpret_cast<float*>(y)[idx] = v;
   else if (dtype == 1) reinterpret_cast<_Float16*>(y)[idx] = (_Float16)v;
@@ -159,24 +185,42 @@ __device__ __forceinline__ void store_out(void* y, int dtype, long idx, float v)
 
 // Group sums of operands reach 64 * 2^15; they enter the bias MFMA scaled by 2^-kGsumShift.
 constexpr int kGsumShift = 7;
-// 8-element pieces of one staged row per lane (so a chunk spans at most 8*64*8 = 4096 k).
-constexpr int kPieceMax = 8;
+// 8-element pieces one thread stages (a chunk holds at most kThreads * kPieceMax pieces).
+constexpr int kPieceMax = 12;
 // Padding of a staged operand row in LDS (elements), against bank conflicts between rows.
 constexpr int kRowPad = 8;
-// LDS header: LN sums S1, S2 of up to 32 rows, then one scale exponent per operand row.
+// LDS header: LN sums S1, S2 of up to 32 rows, one scale exponent per operand row, and the
+// maximum |value| of each source row (34 at most) during staging.
 constexpr int kStatFloats = 64;
 constexpr int kExpInts = 128;
-constexpr int kHeaderBytes = (kStatFloats + kExpInts) * 4;
+constexpr int kRowMax = 64;
+constexpr int kHeaderBytes = (kStatFloats + kExpInts + kRowMax) * 4;
 // Largest dynamic LDS a launch may ask for (gfx950 has 160 KiB per CU).
 constexpr int kLdsMax = 160 * 1024;
 
 __host__ __device__ constexpr int op_pitch(int kc) { return kc + kRowPad; }
-// Bytes of the region holding the staged operand rows and their group sums.
+// Bytes of the region holding the staged operand rows, their group sums and the per-group
+// LN partial sums of the (at most 32) activation rows.
 __host__ __device__ constexpr long staging_bytes(int rows, int kc) {
-  return (long)rows * op_pitch(kc) * 2 + (long)rows * (kc / 64) * 4;
+  return (long)rows * op_pitch(kc) * 2 + (long)rows * (kc / 64) * 4 + 32L * (kc / 64) * 2 * 4;
 }
 // Bytes of the region holding the double-buffered per-wave partial tiles.
 __host__ __device__ constexpr long merge_bytes(int mt) { return 2L * kWaves * mt * 256 * 4; }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global memory, which
+// makes every wave wait for its in-flight weight prefetch at each tile; nothing in this
+// kernel communicates through global memory, so the LDS fence is all that is needed.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Output slot of thread tid for a tile: outputs 0..63 go to wave (tile mod 8), so the
+// epilogue work rotates over the waves instead of always landing on wave 0.
+__device__ __forceinline__ int out_slot(int tid, int tile) {
+  return (tid + kThreads - 64 * (tile % kWaves)) % kThreads;
+}
 
 // Wave-wide fixed-order reductions (xor butterfly over all 64 lanes).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -211,86 +255,90 @@ struct Fused {
   // ---- staging: source rows -> operand rows in LDS ----------------------------------
   // Source row rho: rho < T is x row rho; with LN, rho == T is gamma and T + 1 is beta.
   // Operand rows: terms*t + term for activation row t, then gamma (terms*T), beta (+1).
-  // Round r: wave w stages source row 8r + w; lane l holds pieces l, l + 64, ... (8 k each).
-  __device__ __forceinline__ static void stage(const LinParams& p, float* stat, int* ex, uint16_t* op, float* gsum,
-                                               int kc0, int kc, bool stats, int wv, int lane) {
+  // All threads share the (row, 8-element piece) pairs of the chunk: thread tid takes pieces
+  // tid, tid + kThreads, ...; the 8 pieces of a 64-wide group sit in 8 consecutive lanes.
+  // Pass 1 loads every piece, takes the row maxima (LDS atomicMax on the bit pattern of a
+  // non-negative float: order-independent) and the per-group shifted LN sums; pass 2
+  // converts with the row's power-of-two scale and writes the operand rows and group sums.
+  __device__ __forceinline__ static void stage(const LinParams& p, float* stat, int* ex, unsigned* rowmax, float* spart,
+                                               uint16_t* op, float* gsum, int kc0, int kc, bool stats, int tid) {
     constexpr int NT = BF16OP ? 3 : 2;          // terms the operand type can need
     const int T = p.T, terms = p.terms;
     const int srows = T + (p.ln ? 2 : 0);
     const int ppr = kc / 8;                     // pieces per row (a multiple of 8)
+    const int total = srows * ppr;
     const int pitch = op_pitch(kc);
     const int gpr = kc / 64;
-    for (int rho = wv; rho < srows; rho += kWaves) {
-      const bool act = rho < T;
-      const bool mulg = act && p.ln;
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(act ? p.x : (rho == T ? p.gamma : p.beta)) +
-                            (act ? (long)rho * p.K : 0) + kc0;
-      const uint16_t* gam = reinterpret_cast<const uint16_t*>(p.gamma) + kc0;
-      u4_t raw[kPieceMax], graw[kPieceMax];
+    const uint16_t* x16 = reinterpret_cast<const uint16_t*>(p.x);
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.gamma);
+    const uint16_t* b16 = reinterpret_cast<const uint16_t*>(p.beta);
+    u4_t raw[kPieceMax], graw[kPieceMax];
 #pragma unroll
-      for (int u = 0; u < kPieceMax; ++u) {
-        const int pc = lane + 64 * u;
-        raw[u] = (u4_t){0u, 0u, 0u, 0u};
-        graw[u] = (u4_t){0u, 0u, 0u, 0u};
-        if (pc < ppr) {
-          raw[u] = *reinterpret_cast<const u4_t*>(src + 8 * pc);
-          if (mulg) graw[u] = *reinterpret_cast<const u4_t*>(gam + 8 * pc);
-        }
+    for (int u = 0; u < kPieceMax; ++u) {
+      const int idx = tid + kThreads * u;
+      if (idx < total) {
+        const int row = idx / ppr, pc = idx - (idx / ppr) * ppr;
+        const bool act = row < T;
+        const gptr<const uint16_t> src = pick(act ? x16 : g16, b16, (!act && row != T) ? 1 : 0) +
+                                         (act ? (long)row * p.K : 0) + kc0 + 8 * pc;
+        raw[u] = *reinterpret_cast<gptr<const u4_t>>(src);
+        if (act && p.ln) graw[u] = *reinterpret_cast<gptr<const u4_t>>(pick(g16, g16, 0) + kc0 + 8 * pc);
       }
-      const float x0 = mulg ? elem_to_float(reinterpret_cast<const uint16_t*>(p.x)[(long)rho * p.K], p.x_dtype) : 0.0f;
-      // The passes below walk the pieces one per iteration (not unrolled, to bound register
-      // use) and rotate the arrays by one slot each time; after kPieceMax steps they are back.
-      auto rotate = [&]() {
-        const u4_t r0 = raw[0], g0 = graw[0];
+    }
+    // pass 1
 #pragma unroll
-        for (int i = 0; i + 1 < kPieceMax; ++i) { raw[i] = raw[i + 1]; graw[i] = graw[i + 1]; }
-        raw[kPieceMax - 1] = r0;
-        graw[kPieceMax - 1] = g0;
-      };
-      // pass 1: row max (for the scale) and the shifted LayerNorm sums
-      float amax = 0.0f, s1 = 0.0f, s2 = 0.0f;
-#pragma unroll 1
-      for (int u = 0; u < kPieceMax; ++u) {
-        if (lane + 64 * u < ppr) {
-          float a[8], g[8];
-          unpack8(raw[0], p.x_dtype, a);
-          unpack8(graw[0], p.x_dtype, g);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const float d = a[jj] - x0;
-            const float v = mulg ? d * g[jj] : a[jj];
-            amax = fmaxf(amax, fabsf(v));
-            if (mulg) { s1 += d; s2 += d * d; }
-          }
-        }
-        rotate();
-      }
-      amax = wave_max(amax);
-      if (mulg && stats) {
-        s1 = wave_sum(s1);
-        s2 = wave_sum(s2);
-        if (lane == 0) { stat[2 * rho] += s1; stat[2 * rho + 1] += s2; }
-      }
-      const bool need = act ? p.scale_act : p.scale_gb;
-      int e = 0;
-      if (need && amax > 0.0f && amax < __builtin_inff()) {
-        e = 14 - ilogbf(amax);
-        e = e > 126 ? 126 : (e < -126 ? -126 : e);
-      }
-      const float scl = ldexpf(1.0f, e);
-      const int r0 = act ? terms * rho : terms * T + (rho - T);
-      const int nterm = act ? terms : 1;
-      if (lane == 0)
-        for (int term = 0; term < nterm; ++term) ex[r0 + term] = e;
-      // pass 2: operand terms in MFMA slot order, and their per-group sums
-#pragma unroll 1
-      for (int u = 0; u < kPieceMax; ++u) {
-        const int pc = lane + 64 * u;
-        const bool live = pc < ppr;
+    for (int u = 0; u < kPieceMax; ++u) {
+      const int idx = tid + kThreads * u;
+      if (kThreads * u < total) {                      // uniform: some lane of the block is live
+        const bool live = idx < total;
+        const int row = live ? idx / ppr : 0, pc = idx - row * ppr;
+        const bool mulg = row < T && p.ln;
+        const float x0 = mulg ? elem_to_float(x16[(long)row * p.K], p.x_dtype) : 0.0f;
         float a[8], g[8];
-        unpack8(raw[0], p.x_dtype, a);
-        unpack8(graw[0], p.x_dtype, g);
-        rotate();
+        unpack8(raw[u], p.x_dtype, a);
+        unpack8(graw[u], p.x_dtype, g);
+        float amax = 0.0f, s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float d = a[jj] - x0;
+          amax = fmaxf(amax, fabsf(mulg ? d * g[jj] : a[jj]));
+          s1 += d;
+          s2 += d * d;
+        }
+        if (live) atomicMax(rowmax + row, __builtin_bit_cast(unsigned, amax));
+        if (p.ln && stats) {
+          s1 += __shfl_xor(s1, 1); s1 += __shfl_xor(s1, 2); s1 += __shfl_xor(s1, 4);
+          s2 += __shfl_xor(s2, 1); s2 += __shfl_xor(s2, 2); s2 += __shfl_xor(s2, 4);
+          if (live && mulg && (pc & 7) == 0) { spart[(row * gpr + pc / 8) * 2] = s1; spart[(row * gpr + pc / 8) * 2 + 1] = s2; }
+        }
+      }
+    }
+    lds_barrier();
+    // pass 2
+#pragma unroll
+    for (int u = 0; u < kPieceMax; ++u) {
+      const int idx = tid + kThreads * u;
+      if (kThreads * u < total) {
+        const bool live = idx < total;
+        const int row = live ? idx / ppr : 0, pc = idx - row * ppr;
+        const bool act = row < T;
+        const bool mulg = act && p.ln;
+        const float x0 = mulg ? elem_to_float(x16[(long)row * p.K], p.x_dtype) : 0.0f;
+        const float amax = __builtin_bit_cast(float, rowmax[row]);
+        const bool need = act ? p.scale_act : p.scale_gb;
+        int e = 0;
+        if (need && amax > 0.0f && amax < __builtin_inff()) {
+          e = 14 - ilogbf(amax);
+          e = e > 126 ? 126 : (e < -126 ? -126 : e);
+        }
+        const float scl = ldexpf(1.0f, e);
+        const int r0 = act ? terms * row : terms * T + (row - T);
+        const int nterm = act ? terms : 1;
+        if (live && pc == 0)
+          for (int term = 0; term < nterm; ++term) ex[r0 + term] = e;
+        float a[8], g[8];
+        unpack8(raw[u], p.x_dtype, a);
+        unpack8(graw[u], p.x_dtype, g);
         uint32_t el[NT][8];
         float ts[NT];
 #pragma unroll
@@ -324,17 +372,23 @@ struct Fused {
           }
         }
         if constexpr (QUANT) {
-          // the 8 pieces of a group sit in 8 consecutive lanes
 #pragma unroll
           for (int term = 0; term < NT; ++term) {
             float t = ts[term];
             t += __shfl_xor(t, 1);
             t += __shfl_xor(t, 2);
             t += __shfl_xor(t, 4);
-            if (term < nterm && live && (lane & 7) == 0) gsum[(r0 + term) * gpr + pc / 8] = t;
+            if (term < nterm && live && (pc & 7) == 0) gsum[(r0 + term) * gpr + pc / 8] = t;
           }
         }
       }
+    }
+    // LayerNorm sums of each activation row, in group order
+    if (p.ln && stats && tid < T) {
+      float s1 = 0.0f, s2 = 0.0f;
+      for (int g = 0; g < gpr; ++g) { s1 += spart[(tid * gpr + g) * 2]; s2 += spart[(tid * gpr + g) * 2 + 1]; }
+      stat[2 * tid] += s1;
+      stat[2 * tid + 1] += s2;
     }
   }
 
@@ -386,82 +440,156 @@ struct Fused {
     else { proj = 0; n = tile * 16 + li; }
   }
 
+  // Registers a tile's loads land in.  Loaded values are not combined here: consuming one
+  // would make the compiler wait for every load issued before it, the prefetch included.
+  struct TileRegs {
+    u4_t dw[MAXS];          // 16 code bytes per step
+    uint32_t sc[MAXS];      // fp16 scale bits of the step's groups, packed (group g in bits 16g)
+    uint32_t bi[MAXS];      // fp16 bias bits, packed the same way
+  };
+
+  // Epilogue inputs of the output this thread finishes, out_slot(tid, tile) = (t, col):
+  // residual[t, n] and constant[n] of a linear tile (zeros when absent or out of range).
+  struct EpiRegs {
+    uint16_t res, add;
+  };
+  __device__ __forceinline__ static void load_epi(const LinParams& p, int tile, EpiRegs& e) {
+    const gptr<const uint16_t> z16 = pick(reinterpret_cast<const uint16_t*>(g_zero16),
+                                          reinterpret_cast<const uint16_t*>(g_zero16), 0);
+    const int q = out_slot(threadIdx.x, tile);
+    const int t = q >> 4, on = tile * 16 + (q & 15);
+    const bool mine = !p.gateup && tile < p.ntiles && t < p.T && on < p.N;
+    const gptr<const uint16_t> rp = pick(reinterpret_cast<const uint16_t*>(p.res), reinterpret_cast<const uint16_t*>(p.res), 0);
+    const gptr<const uint16_t> ap = pick(reinterpret_cast<const uint16_t*>(p.add), reinterpret_cast<const uint16_t*>(p.add), 0);
+    e.res = *((mine && p.res) ? rp + (long)t * p.N + on : z16);
+    e.add = *((mine && p.add) ? ap + on : z16);
+  }
+
   // Issue the loads of a tile's codes, scales and biases for steps [s_lo, s_lo + nsw).
+  // One base address per lane and tile, then immediate offsets per step.  A lane with no
+  // row (n >= N, or a tile past the last) streams from the zero buffer instead, so every
+  // tile issues the same loads; steps >= nsw (uniform) are skipped.  Rows must consist of
+  // whole 64-byte steps (4-bit K = 64 mod 128 goes through the chunked variant).
+  template <bool CHECKED = false>
   __device__ __forceinline__ static void load_tile(const LinParams& p, int tile, int s_lo, int nsw, int c, int li,
-                                                   u4_t dw[MAXS], uint32_t sb[MAXS], u4_t& bfr) {
+                                                   TileRegs& r) {
     int proj, n;
     tile_row(p, tile, li, proj, n);
-    const bool valid = n < p.N;
+    const bool valid = tile < p.ntiles && n < p.N;
     const long row_bytes = (long)p.K * BITS / 8;
-    const char* wrow = reinterpret_cast<const char*>(p.w[proj]) + (long)n * row_bytes;
     const int G = p.K / 64;
+    const gptr<const char> zero = pick(reinterpret_cast<const char*>(g_zero16), reinterpret_cast<const char*>(g_zero16), 0);
+    const gptr<const char> wb = pick(reinterpret_cast<const char*>(p.w[0]), reinterpret_cast<const char*>(p.w[1]), proj);
+    __builtin_amdgcn_sched_barrier(0);
+    const gptr<const char> cb = valid ? wb + (long)n * row_bytes + (long)s_lo * 64 + 16 * c : zero + 16 * c;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
-      dw[s] = (u4_t){0u, 0u, 0u, 0u};
-      const long off = (long)(s_lo + s) * 64 + 16 * c;
-      if (s < nsw && valid && off < row_bytes) dw[s] = *reinterpret_cast<const u4_t*>(wrow + off);
-      if constexpr (QUANT) {
-        sb[s] = 0u;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const int grp = (s_lo + s) * NG + g;
-          if (s < nsw && valid && grp < G) sb[s] |= (uint32_t)p.sc[proj][(long)n * G + grp] << (16 * g);
-        }
+      // steps >= nsw (uniform) read the zero buffer: no branch, so the whole batch issues
+      // back to back and the wait counts stay exact
+      const gptr<const char> a = s < nsw ? cb + s * 64 : zero + 16 * c;
+      if constexpr (CHECKED) {   // a row may end half-way through its last step
+        const bool in = (long)(s_lo + s) * 64 + 16 * c < row_bytes;
+        r.dw[s] = *reinterpret_cast<gptr<const u4_t>>(in ? a : zero + 16 * c);
+      } else {
+        r.dw[s] = *reinterpret_cast<gptr<const u4_t>>(a);
       }
     }
     if constexpr (QUANT) {
-      // B operand of the bias product: slot j of lane group c = bias of group 8*(c&1) + j
-      uint32_t el[8];
+      // A step's scales (biases) are NG consecutive fp16 values: 4-bit steps load them as one
+      // aligned dword (K is a multiple of 128 here, so n*G + 2*s is even), 8-bit as a ushort.
+      // They stay packed until compute_tile; splitting them here would make the compiler wait.
+      const gptr<const uint16_t> zh = pick(reinterpret_cast<const uint16_t*>(g_zero16),
+                                           reinterpret_cast<const uint16_t*>(g_zero16), 0);
+      const long go = (long)n * G + (long)s_lo * NG;
+      const gptr<const uint16_t> sbase = valid ? pick(p.sc[0], p.sc[1], proj) + go : zh;
+      const gptr<const uint16_t> bbase = valid ? pick(p.bi[0], p.bi[1], proj) + go : zh;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gi = 8 * (c & 1) + j;
-        const int grp = s_lo * NG + gi;
-        el[j] = (valid && gi < nsw * NG && grp < G) ? (uint32_t)p.bi[proj][(long)n * G + grp] : 0u;
+      for (int s = 0; s < MAXS; ++s) {
+        const bool live = s < nsw;
+        if constexpr (CHECKED) {
+          // rows may end half-way through a step: fetch each group on its own
+          uint32_t sv = 0u, bv = 0u;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const bool in = live && (s_lo + s) * NG + g < G;
+            sv |= (uint32_t)*(in ? sbase + s * NG + g : zh) << (16 * g);
+            bv |= (uint32_t)*(in ? bbase + s * NG + g : zh) << (16 * g);
+          }
+          r.sc[s] = sv;
+          r.bi[s] = bv;
+        } else if constexpr (NG == 2) {
+          r.sc[s] = *reinterpret_cast<gptr<const uint32_t>>(live ? sbase + 2 * s : zh);
+          r.bi[s] = *reinterpret_cast<gptr<const uint32_t>>(live ? bbase + 2 * s : zh);
+        } else {
+          r.sc[s] = *(live ? sbase + s : zh);
+          r.bi[s] = *(live ? bbase + s : zh);
+        }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bfr[r] = el[2 * r] | (el[2 * r + 1] << 16);
     }
+    // keep the batch together: nothing from the surrounding compute moves in between
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Stream one tile's loaded codes through the fragments into acc.
-  __device__ __forceinline__ void compute_tile(int nsw, const u4_t dw[MAXS], const uint32_t sb[MAXS], const u4_t bfr,
-                                               f4_t acc[MT]) {
+  __device__ __forceinline__ void compute_tile(int nsw, int c, const TileRegs& r, f4_t acc[MT]) {
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
       if (s < nsw) {
-        u4_t d = dw[s];
+        u4_t d = r.dw[s];
         if constexpr (BITS == 4) {
           const auto r01 = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
           const auto r23 = __builtin_amdgcn_permlane32_swap(d[2], d[3], false, false);
           d[0] = r01[0]; d[1] = r01[1]; d[2] = r23[0]; d[3] = r23[1];
         }
         if constexpr (QUANT) {
+          // every group's partial first (independent accumulators), then the scale FMAs
+          f4_t cg[NG][MT];
 #pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            f4_t cg[MT];
+          for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) cg[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+            for (int mt = 0; mt < MT; ++mt) cg[g][mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int qq = 0; qq < NM / NG; ++qq) {
+          for (int qq = 0; qq < NM / NG; ++qq)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
               const int q = g * (NM / NG) + qq;
               const u4_t b = convert_codes<BITS>(d, q);
 #pragma unroll
-              for (int mt = 0; mt < MT; ++mt) cg[mt] = mfma<BF16OP>(afrag[s][q][mt], b, cg[mt]);
+              for (int mt = 0; mt < MT; ++mt) cg[g][mt] = mfma<BF16OP>(afrag[s][q][mt], b, cg[g][mt]);
             }
-            const float sf = half_bits_to_float((sb[s] >> (16 * g)) & 0xFFFFu);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const float sf = half_bits_to_float((r.sc[s] >> (16 * g)) & 0xFFFFu);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(sf, cg[mt][v], acc[mt][v]);
+              for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(sf, cg[g][mt][v], acc[mt][v]);
           }
         } else {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma<BF16OP>(afrag[s][0][mt], d, acc[mt]);
         }
+      } else {
+        // unused step: still read its (zero) registers, so that no path leaves a load unread
+        // (the compiler would drain every outstanding load, the prefetch too, before reusing them)
+        asm volatile("" ::"v"(r.dw[s]), "v"(r.sc[s]), "v"(r.bi[s]));
       }
     }
     if constexpr (QUANT) {
       // sum_g b[n, g] * (sum of group g's operands): one MFMA per row tile
+      // slot j of lane group c is the bias of this wave's group 8*(c&1) + j
+      uint32_t el[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // groups past this wave's slice get 0 (their loads were skipped)
+        const uint32_t lo = (j < MAXS * NG && j < nsw * NG) ? (r.bi[j / NG] >> (16 * (j % NG))) & 0xFFFFu : 0u;
+        const uint32_t hi = (8 + j < MAXS * NG && 8 + j < nsw * NG)
+                                ? (r.bi[(8 + j) / NG] >> (16 * ((8 + j) % NG))) & 0xFFFFu : 0u;
+        el[j] = (c & 1) ? hi : lo;
+      }
+      u4_t bfr;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) bfr[w] = el[2 * w] | (el[2 * w + 1] << 16);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const f4_t cb = mfma<false>(gfrag[mt], bfr, (f4_t){0.0f, 0.0f, 0.0f, 0.0f});
@@ -499,16 +627,19 @@ __device__ __forceinline__ float folded(const LinParams& p, const float* red, co
 }
 
 // Epilogue and store of one tile ([p1] `_linear_kernel`: GELU, then residual, then constant).
+// Thread tid finishes output slot out_slot(tid, tile).
 template <int MT>
-__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* stat, int buf, int tile, int tid) {
+__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* stat, int buf, int tile, int tid,
+                                         uint32_t res_bits, uint32_t add_bits) {
+  tid = out_slot(tid, tile);
   if (!p.gateup) {
     if (tid < p.T * 16) {
       const int t = tid >> 4, col = tid & 15, n = tile * 16 + col;
       if (n < p.N) {
         float v = folded<MT>(p, red, stat, buf, t, col);
         if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
-        if (p.res) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.res)[(long)t * p.N + n], p.x_dtype);
-        if (p.add) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.add)[n], p.x_dtype);
+        if (p.res) v += elem_to_float(res_bits, p.x_dtype);
+        if (p.add) v += elem_to_float(add_bits, p.x_dtype);
         store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
       }
     }
@@ -524,20 +655,19 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
   }
 }
 
-template <int BITS, bool BF16OP, int MT>
+template <int BITS, bool BF16OP, int MT, bool CHUNKED>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   using S = Fused<BITS, BF16OP, MT>;
-  constexpr int MAXS = S::MAXS;
   constexpr int STEPK = S::STEPK;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   float* stat = reinterpret_cast<float*>(lds_raw);
   int* ex = reinterpret_cast<int*>(lds_raw + kStatFloats * 4);
+  unsigned* rowmax = reinterpret_cast<unsigned*>(lds_raw + (kStatFloats + kExpInts) * 4);
   unsigned char* region = lds_raw + kHeaderBytes;
   float* red = reinterpret_cast<float*>(region);
 
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, c = lane >> 4, li = lane & 15;
-  const int nchunks = (p.steps + p.chunk_steps - 1) / p.chunk_steps;
-  const bool single = nchunks == 1;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane >> 4, li = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   auto slice = [&](int ch, int& cs0, int& s_lo, int& nsw) {
     cs0 = ch * p.chunk_steps;
@@ -553,57 +683,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     const int kc = min(p.chunk_steps * STEPK, p.K - kc0);
     uint16_t* op = reinterpret_cast<uint16_t*>(region);
     float* gsum = reinterpret_cast<float*>(region + (long)p.rows * op_pitch(kc) * 2);
-    S::stage(p, stat, ex, op, gsum, kc0, kc, stats, wv, lane);
-    __syncthreads();
+    float* spart = gsum + (long)p.rows * (kc / 64);
+    if (tid < kRowMax) rowmax[tid] = 0u;
+    lds_barrier();
+    S::stage(p, stat, ex, rowmax, spart, op, gsum, kc0, kc, stats, tid);
+    lds_barrier();
     st.load_frags(p, ex, op, gsum, kc0, kc, cs0, s_lo, nsw, c, li);
-    __syncthreads();
+    lds_barrier();
   };
-
-  if (tid < kStatFloats) stat[tid] = 0.0f;
-  __syncthreads();
-
-  int cs0, s_lo, nsw;
-  slice(0, cs0, s_lo, nsw);
-  u4_t cur[MAXS], nxt[MAXS], bfc, bfn;
-  uint32_t sbc[MAXS], sbn[MAXS];
-  int tile = blockIdx.x;
-  if (single) S::load_tile(p, tile, s_lo, nsw, c, li, cur, sbc, bfc);   // the weight stream starts first
-  bool first = true;
-  int buf = 0;
-  for (; tile < p.ntiles; tile += gridDim.x, buf ^= 1) {
-    f4_t acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-    // With one chunk the fragments are built once and each tile's loads go out one tile
-    // ahead.  Long K rebuilds them per chunk; acc stays in the current chunk's scaled
-    // units, and switching chunks multiplies by a ratio of powers of two (exact).
-    for (int ch = 0; ch < nchunks; ++ch) {
-      if (!single || first) {
-        float prev[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) prev[mt][j] = st.unscale[mt][j];
-        if (!first) __syncthreads();   // the previous tile's merge has been read
-        prepare(ch, first, cs0, s_lo, nsw);
-        if (!single) {
-          S::load_tile(p, tile, s_lo, nsw, c, li, cur, sbc, bfc);
-          if (ch > 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mt][j] *= prev[mt][j] / st.unscale[mt][j];
-          }
-        }
-      }
-      if (single) {
-        const int next = tile + gridDim.x;
-        if (next < p.ntiles) S::load_tile(p, next, s_lo, nsw, c, li, nxt, sbn, bfn);
-      }
-      st.compute_tile(nsw, cur, sbc, bfc, acc);
-    }
-    first = false;
-    // merge the waves' partials in LDS (double-buffered by tile parity), then finish
+  // Merge the waves' partials of a tile in LDS (double-buffered by tile parity), finish it.
+  auto merge_finish = [&](const f4_t acc[MT], int tile, int buf, const typename S::EpiRegs& e) {
     float* rb = red + (buf * kWaves + wv) * MT * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -612,12 +701,92 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       for (int j = 0; j < 4; ++j) v[j] = acc[mt][j] * st.unscale[mt][j];
       *reinterpret_cast<f4_t*>(rb + mt * 256 + lane * 4) = v;
     }
-    __syncthreads();
-    finalize<MT>(p, red, stat, buf, tile, tid);
-    if (single) {
+    // Every lane reads its residual and constant here, used or not: a loaded register left
+    // unread on some path makes the compiler drain all loads (the prefetch too) before the
+    // register is reused.
+    const uint32_t res_bits = e.res, add_bits = e.add;
+    asm volatile("" ::"v"(res_bits), "v"(add_bits));
+    lds_barrier();
+    finalize<MT>(p, red, stat, buf, tile, tid, res_bits, add_bits);
+  };
+
+  if (tid < kStatFloats) stat[tid] = 0.0f;
+  lds_barrier();
+
+  int cs0, s_lo, nsw;
+  if constexpr (!CHUNKED) {
+    // All of K fits: build the fragments once, then stream tiles with the next tile's loads
+    // always in flight.  Two register sets alternate (no copy at the end of an iteration,
+    // which would make the compiler wait for the prefetch).
+    slice(0, cs0, s_lo, nsw);
+    typename S::TileRegs ra, rb;
+    int tile = blockIdx.x;
+    S::load_tile(p, tile, s_lo, nsw, c, li, ra);   // the weight stream starts before staging
+    prepare(0, true, cs0, s_lo, nsw);
+    int buf = 0;
+    for (;;) {
+      // epilogue inputs are loaded and used within one half: a load still in flight across
+      // the loop edge would make the compiler drain the prefetch at the top of the loop
+      typename S::EpiRegs e;
+      S::load_epi(p, tile, e);
+      const int t1 = tile + gridDim.x;
+      S::load_tile(p, t1, s_lo, nsw, c, li, rb);   // past the last tile this loads zeros
+      {
+        f4_t acc[MT];
 #pragma unroll
-      for (int s = 0; s < MAXS; ++s) { cur[s] = nxt[s]; sbc[s] = sbn[s]; }
-      bfc = bfn;
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+        st.compute_tile(nsw, c, ra, acc);
+        merge_finish(acc, tile, buf, e);
+      }
+      tile = t1;
+      buf ^= 1;
+      if (tile >= p.ntiles) break;
+      S::load_epi(p, tile, e);
+      const int t2 = tile + gridDim.x;
+      S::load_tile(p, t2, s_lo, nsw, c, li, ra);
+      {
+        f4_t acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+        st.compute_tile(nsw, c, rb, acc);
+        merge_finish(acc, tile, buf, e);
+      }
+      tile = t2;
+      buf ^= 1;
+      if (tile >= p.ntiles) break;
+    }
+  } else {
+    // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
+    // units; switching chunks multiplies by a ratio of powers of two (exact).
+    const int nchunks = (p.steps + p.chunk_steps - 1) / p.chunk_steps;
+    bool first = true;
+    int buf = 0;
+    for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x, buf ^= 1) {
+      f4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      typename S::TileRegs r;
+      for (int ch = 0; ch < nchunks; ++ch) {
+        float prev[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) prev[mt][j] = st.unscale[mt][j];
+        if (!first || ch > 0) lds_barrier();   // earlier readers of the LDS region are done
+        prepare(ch, first, cs0, s_lo, nsw);
+        S::template load_tile<true>(p, tile, s_lo, nsw, c, li, r);
+        if (ch > 0) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mt][j] *= prev[mt][j] / st.unscale[mt][j];
+        }
+        st.compute_tile(nsw, c, r, acc);
+      }
+      first = false;
+      typename S::EpiRegs e;
+      S::load_epi(p, tile, e);
+      merge_finish(acc, tile, buf, e);
     }
   }
 }
@@ -627,18 +796,26 @@ __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
   return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt));
 }
 
-template <int BITS, bool BF16OP, int MT>
-hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
+template <int BITS, bool BF16OP, int MT, bool CHUNKED>
+hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // Above 64 KiB of dynamic LDS the kernel must opt in once (a host-side attribute).
   static bool opted_in = false;
   if (!opted_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
     opted_in = true;
   }
-  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT>), dim3(grid), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED>), dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
+}
+
+template <int BITS, bool BF16OP, int MT>
+hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
+  // The streaming variant needs all of K staged at once and rows of whole 64-byte steps.
+  const bool whole_steps = ((long)p.K * BITS / 8) % 64 == 0;
+  return (p.chunk_steps >= p.steps && whole_steps) ? launch_variant<BITS, BF16OP, MT, false>(p, grid, lds, s)
+                                                   : launch_variant<BITS, BF16OP, MT, true>(p, grid, lds, s);
 }
 
 }  // namespace qlin

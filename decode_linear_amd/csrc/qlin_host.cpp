@@ -147,11 +147,11 @@ static long chunk_k(int bits, int cs, long K) { const long kc = (long)cs * step_
 int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K) {
   const int mfma = bits == 4 ? Fmt<4>::kMfma : (bits == 8 ? Fmt<8>::kMfma : Fmt<16>::kMfma);
   int cs = kWaves * max_steps_for(mfma, mt);
-  (void)T; (void)ln;
+  const long srows = T + (ln ? 2 : 0);
   for (; cs > 1; --cs) {
     const long kc = chunk_k(bits, cs, K);
-    const long ppl = (kc / 8 + 63) / 64;     // staged pieces per lane and row
-    if (ppl <= kPieceMax && lds_bytes_for(rows, (int)kc, mt) <= kLdsMax) break;
+    const long pieces = srows * (kc / 8);   // staged 8-element pieces, shared by all threads
+    if (pieces <= (long)kThreads * kPieceMax && lds_bytes_for(rows, (int)kc, mt) <= kLdsMax) break;
   }
   return cs;
 }
