@@ -90,54 +90,37 @@ __device__ __forceinline__ void load8(const void* base, int dtype, long idx, flo
 }
 
 // ---- code conversion to fp16 operand pairs ------------------------------------------
-// Byte pair of an 8-bit word -> two fp16 integers.  v_perm puts code bytes under the
-// exponent byte 0x64 (fp16 1024 has unit spacing), then 1024 is subtracted exactly.
-__device__ __forceinline__ uint32_t bytes_to_h2(uint32_t d, uint32_t sel) {
-  const uint32_t h = __builtin_amdgcn_perm(0x64646464u, d, sel);
-  const h2_t v = __builtin_bit_cast(h2_t, h) - (h2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-  return __builtin_bit_cast(uint32_t, v);
-}
-// Nibbles 0 and 4 of d (bits 0-3 and 16-19) -> fp16 integers.
-// (a & mask) | magic as one v_and_or_b32.  gfx9 VOP3 cannot encode 32-bit literals, so
-// without this the compiler emits a separate v_and and v_or; the mask goes in an SGPR and
-// the magic constant in a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
-}
-__device__ __forceinline__ uint32_t nib_lo_to_h2(uint32_t d) {
-  const uint32_t h = and_or(d, 0x000F000Fu, 0x64006400u);
-  const h2_t v = __builtin_bit_cast(h2_t, h) - (h2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-  return __builtin_bit_cast(uint32_t, v);
-}
-// Nibbles 1 and 5 (bits 4-7 and 20-23): 1024 + 16 n, scaled back exactly: (1024+16n)/16 - 64.
-__device__ __forceinline__ uint32_t nib_hi_to_h2(uint32_t d) {
-  const uint32_t h = and_or(d, 0x00F000F0u, 0x64006400u);
-  const h2_t v = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, h), (h2_t){(_Float16)0.0625f, (_Float16)0.0625f},
-                                           (h2_t){(_Float16)-64.0f, (_Float16)-64.0f});
-  return __builtin_bit_cast(uint32_t, v);
-}
-
+// Codes enter the MFMA as fp16 subnormals: the bit pattern q (q < 1024) is the value
+// q * 2^-24 exactly, and the matrix cores take fp16 subnormal inputs exactly.  So a mask
+// or a byte permute is the whole conversion; the 2^-24 is undone with the row scale.
+// 4-bit: nibbles 0 and 4 of r (bits 0-3, 16-19) give n * 2^-24; nibbles 1 and 5 (bits 4-7,
+// 20-23) give 16 n * 2^-24, and the activations of those slots are staged divided by 16.
 template <int BITS>
 __device__ __forceinline__ u4_t convert_codes(const u4_t d, int q) {
   u4_t b;
   if constexpr (BITS == 8) {
     const uint32_t da = d[2 * q], db = d[2 * q + 1];
-    b[0] = bytes_to_h2(da, 0x04010400u);
-    b[1] = bytes_to_h2(da, 0x04030402u);
-    b[2] = bytes_to_h2(db, 0x04010400u);
-    b[3] = bytes_to_h2(db, 0x04030402u);
+    b[0] = __builtin_amdgcn_perm(0u, da, 0x0C010C00u);   // bytes 0, 1 -> low byte of each half
+    b[1] = __builtin_amdgcn_perm(0u, da, 0x0C030C02u);   // bytes 2, 3
+    b[2] = __builtin_amdgcn_perm(0u, db, 0x0C010C00u);
+    b[3] = __builtin_amdgcn_perm(0u, db, 0x0C030C02u);
   } else if constexpr (BITS == 4) {
     const uint32_t r = d[(q & 1) * 2 + (q >> 1)];
-    b[0] = nib_lo_to_h2(r);
-    b[1] = nib_hi_to_h2(r);
-    b[2] = nib_lo_to_h2(r >> 8);
-    b[3] = nib_hi_to_h2(r >> 8);
+    b[0] = r & 0x000F000Fu;
+    b[1] = r & 0x00F000F0u;
+    b[2] = (r >> 8) & 0x000F000Fu;
+    b[3] = (r >> 8) & 0x00F000F0u;
   } else {
     b = d;
   }
   return b;
+}
+// Scale of the quantized MFMA partials: codes enter as q * 2^-24.
+constexpr float kCodeScale = 0x1p-24f;
+// 4-bit operand slots fed by the high nibble of a byte (value 16 q * 2^-24) carry their
+// activation divided by 16.
+template <int BITS> __device__ __forceinline__ constexpr bool slot_hi_nibble(int j) {
+  return BITS == 4 && ((j >> 1) & 1) != 0;
 }
 
 template <bool BF16OP>
@@ -194,8 +177,10 @@ constexpr int kRowPad = 8;
 constexpr int kStatFloats = 64;
 constexpr int kExpInts = 128;
 constexpr int kRowMax = 64;
-constexpr int kHeaderBytes = (kStatFloats + kExpInts + kRowMax) * 4;
+constexpr int kHeaderBytes = (2 * kStatFloats + kExpInts + 2 * kRowMax) * 4;   // sums, moments, exps, max, x[t, 0]
 // Largest dynamic LDS a launch may ask for (gfx950 has 160 KiB per CU).
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kLdsMax = 160 * 1024;
 
 __host__ __device__ constexpr int op_pitch(int kc) { return kc + kRowPad; }
@@ -220,6 +205,34 @@ __device__ __forceinline__ void lds_barrier() {
 // epilogue work rotates over the waves instead of always landing on wave 0.
 __device__ __forceinline__ int out_slot(int tid, int tile) {
   return (tid + kThreads - 64 * (tile % kWaves)) % kThreads;
+}
+
+// Reductions over aligned groups of 8 lanes with DPP moves (lane i sees lane i^1, then i^2
+// within quads, then the mirrored half of its 8-lane row).  Every lane of a group ends with
+// the same value: each step adds two operands that are equal on both partner lanes.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm 1,0,3,2
+  v += dpp_f<0x4E>(v);    // quad_perm 2,3,0,1
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  return v;
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return v;
+}
+// Operand-row scale exponent for a row maximum amax: 2^e * amax lies in [2^14, 2^15) (e
+// clamped to +-126; 0 for a zero or non-finite maximum).
+__device__ __forceinline__ int row_exponent(float amax) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, amax);
+  const int be = (int)(b >> 23) & 0xFF;   // amax >= 0; a subnormal maximum clamps to 126 below
+  if (b == 0u || be == 0xFF) return 0;
+  const int e = 14 - (be - 127);
+  return e > 126 ? 126 : (e < -126 ? -126 : e);
 }
 
 // Wave-wide fixed-order reductions (xor butterfly over all 64 lanes).
@@ -260,107 +273,179 @@ struct Fused {
   // Pass 1 loads every piece, takes the row maxima (LDS atomicMax on the bit pattern of a
   // non-negative float: order-independent) and the per-group shifted LN sums; pass 2
   // converts with the row's power-of-two scale and writes the operand rows and group sums.
-  __device__ __forceinline__ static void stage(const LinParams& p, float* stat, int* ex, unsigned* rowmax, float* spart,
-                                               uint16_t* op, float* gsum, int kc0, int kc, bool stats, int tid) {
-    constexpr int NT = BF16OP ? 3 : 2;          // terms the operand type can need
-    const int T = p.T, terms = p.terms;
+  // Raw 16-byte pieces of the staged rows (x, gamma, beta) and the gamma piece of each x piece
+  // (ones where no LayerNorm multiplies the piece).
+  struct StageRegs {
+    u4_t raw[kPieceMax], graw[kPieceMax];
+  };
+  __device__ __forceinline__ static void stage_load(const LinParams& p, int kc0, int kc, int tid, StageRegs& sr) {
+    // piece indexing is recomputed at each call (not hoisted out of the chunk loop, where a
+    // dozen live addresses would crowd out the fragments)
+    asm volatile("" : "+v"(tid));
+    const int T = p.T;
     const int srows = T + (p.ln ? 2 : 0);
     const int ppr = kc / 8;                     // pieces per row (a multiple of 8)
     const int total = srows * ppr;
-    const int pitch = op_pitch(kc);
-    const int gpr = kc / 64;
     const uint16_t* x16 = reinterpret_cast<const uint16_t*>(p.x);
     const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.gamma);
     const uint16_t* b16 = reinterpret_cast<const uint16_t*>(p.beta);
-    u4_t raw[kPieceMax], graw[kPieceMax];
+    const uint32_t one = p.x_dtype == 1 ? 0x3C003C00u : 0x3F803F80u;
 #pragma unroll
     for (int u = 0; u < kPieceMax; ++u) {
       const int idx = tid + kThreads * u;
+      sr.graw[u] = (u4_t){one, one, one, one};
       if (idx < total) {
         const int row = idx / ppr, pc = idx - (idx / ppr) * ppr;
         const bool act = row < T;
         const gptr<const uint16_t> src = pick(act ? x16 : g16, b16, (!act && row != T) ? 1 : 0) +
                                          (act ? (long)row * p.K : 0) + kc0 + 8 * pc;
-        raw[u] = *reinterpret_cast<gptr<const u4_t>>(src);
-        if (act && p.ln) graw[u] = *reinterpret_cast<gptr<const u4_t>>(pick(g16, g16, 0) + kc0 + 8 * pc);
+        sr.raw[u] = *reinterpret_cast<gptr<const u4_t>>(src);
+        if (act && p.ln) sr.graw[u] = *reinterpret_cast<gptr<const u4_t>>(pick(g16, g16, 0) + kc0 + 8 * pc);
       }
     }
-    // pass 1
+  }
+
+  // Staging proper.  Pass 1 takes, per source row, the maximum |value| (after the LN shift
+  // and gamma) with LDS atomics on the bit patterns (non-negative floats order like their
+  // bits), and per 64-wide group the LN partial sums of (x - x[t,0]) and its square.  Pass 2
+  // scales each row by 2^e (row_exponent), splits it into terms of the operand type (hi, lo for
+  // fp16; hi, mid, lo for bf16) and writes them, in slot order, to the operand rows together
+  // with the group sums of each term.  The body is instantiated per input type and for
+  // single-term rows, so that no per-element test remains.
+  __device__ __forceinline__ static void stage_compute(const LinParams& p, float* stat, int* ex, unsigned* rowmax,
+                                                       float* x0s, float* spart, uint16_t* op, float* gsum, int kc0,
+                                                       int kc, bool stats, int tid, const StageRegs& sr) {
+    asm volatile("" : "+v"(tid));   // as in stage_load
+    if (p.x_dtype == 1) {
+      if (p.terms == 1) stage_body<1, true>(p, stat, ex, rowmax, x0s, spart, op, gsum, kc0, kc, stats, tid, sr);
+      else stage_body<1, false>(p, stat, ex, rowmax, x0s, spart, op, gsum, kc0, kc, stats, tid, sr);
+    } else {
+      if (p.terms == 1) stage_body<2, true>(p, stat, ex, rowmax, x0s, spart, op, gsum, kc0, kc, stats, tid, sr);
+      else stage_body<2, false>(p, stat, ex, rowmax, x0s, spart, op, gsum, kc0, kc, stats, tid, sr);
+    }
+  }
+
+  template <int XDT>
+  __device__ __forceinline__ static void unpack_t(const u4_t raw, float v[8]) {
 #pragma unroll
-    for (int u = 0; u < kPieceMax; ++u) {
-      const int idx = tid + kThreads * u;
-      if (kThreads * u < total) {                      // uniform: some lane of the block is live
-        const bool live = idx < total;
-        const int row = live ? idx / ppr : 0, pc = idx - row * ppr;
-        const bool mulg = row < T && p.ln;
-        const float x0 = mulg ? elem_to_float(x16[(long)row * p.K], p.x_dtype) : 0.0f;
-        float a[8], g[8];
-        unpack8(raw[u], p.x_dtype, a);
-        unpack8(graw[u], p.x_dtype, g);
-        float amax = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = (raw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      v[j] = XDT == 1 ? half_bits_to_float(h) : __builtin_bit_cast(float, h << 16);
+    }
+  }
+
+  template <int XDT, bool ONE>
+  __device__ __forceinline__ static void stage_body(const LinParams& p, float* stat, int* ex, unsigned* rowmax,
+                                                    float* x0s, float* spart, uint16_t* op, float* gsum, int kc0,
+                                                    int kc, bool stats, int tid, const StageRegs& sr) {
+    constexpr int NT = ONE ? 1 : (BF16OP ? 3 : 2);   // terms of an activation row
+    const int T = p.T;
+    const int srows = T + (p.ln ? 2 : 0);
+    const int ppr = kc / 8;
+    const int total = srows * ppr;
+    const int pitch = op_pitch(kc);
+    const int gpr = kc / 64;
+    // idx / ppr as a multiply-high: exact while idx * ppr < 2^32
+    const uint32_t magic = 0xFFFFFFFFu / (uint32_t)ppr + 1u;
+    // the shift x[t, 0] of the LN sums: published by the piece that holds it (the first
+    // chunk's), kept in LDS for the later chunks
+    if (p.ln && kc0 == 0) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float d = a[jj] - x0;
-          amax = fmaxf(amax, fabsf(mulg ? d * g[jj] : a[jj]));
-          s1 += d;
-          s2 += d * d;
-        }
-        if (live) atomicMax(rowmax + row, __builtin_bit_cast(unsigned, amax));
-        if (p.ln && stats) {
-          s1 += __shfl_xor(s1, 1); s1 += __shfl_xor(s1, 2); s1 += __shfl_xor(s1, 4);
-          s2 += __shfl_xor(s2, 1); s2 += __shfl_xor(s2, 2); s2 += __shfl_xor(s2, 4);
-          if (live && mulg && (pc & 7) == 0) { spart[(row * gpr + pc / 8) * 2] = s1; spart[(row * gpr + pc / 8) * 2 + 1] = s2; }
+      for (int u = 0; u < kPieceMax; ++u) {
+        const int idx = tid + kThreads * u;
+        if (kThreads * u < total && idx < total && idx % ppr == 0 && idx / ppr < T)
+          x0s[idx / ppr] = XDT == 1 ? half_bits_to_float(sr.raw[u][0] & 0xFFFFu)
+                                    : __builtin_bit_cast(float, sr.raw[u][0] << 16);
+      }
+      lds_barrier();
+    }
+    // pass 1: row maxima (only rows that are scaled) and LN sums
+    if (p.ln || p.scale_act) {
+#pragma unroll
+      for (int u = 0; u < kPieceMax; ++u) {
+        if (kThreads * u < total) {                    // uniform: some lane of the block is live
+          const int idx = tid + kThreads * u;
+          const bool live = idx < total;
+          const int row = live ? (int)__umulhi((uint32_t)idx, magic) : 0, pc = idx - row * ppr;
+          float a[8];
+          unpack_t<XDT>(sr.raw[u], a);
+          float amax = 0.0f;
+          if (p.ln) {
+            const bool lnr = row < T;
+            const float x0 = lnr ? x0s[row] : 0.0f;
+            float g[8];
+            unpack_t<XDT>(sr.graw[u], g);
+            float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const float d = a[jj] - x0;
+              amax = fmaxf(amax, fabsf(d * g[jj]));
+              s1 += d;
+              s2 += d * d;
+            }
+            if (stats) {
+              s1 = sum8(s1);
+              s2 = sum8(s2);
+              if (live && lnr && (pc & 7) == 0) {
+                spart[(row * gpr + pc / 8) * 2] = s1;
+                spart[(row * gpr + pc / 8) * 2 + 1] = s2;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) amax = fmaxf(amax, fabsf(a[jj]));
+          }
+          amax = max8(amax);
+          if (live && (pc & 7) == 0) atomicMax(rowmax + row, __builtin_bit_cast(unsigned, amax));
         }
       }
+      lds_barrier();
     }
-    lds_barrier();
     // pass 2
 #pragma unroll
     for (int u = 0; u < kPieceMax; ++u) {
-      const int idx = tid + kThreads * u;
       if (kThreads * u < total) {
+        const int idx = tid + kThreads * u;
         const bool live = idx < total;
-        const int row = live ? idx / ppr : 0, pc = idx - row * ppr;
+        const int row = live ? (int)__umulhi((uint32_t)idx, magic) : 0, pc = idx - row * ppr;
         const bool act = row < T;
-        const bool mulg = act && p.ln;
-        const float x0 = mulg ? elem_to_float(x16[(long)row * p.K], p.x_dtype) : 0.0f;
-        const float amax = __builtin_bit_cast(float, rowmax[row]);
         const bool need = act ? p.scale_act : p.scale_gb;
-        int e = 0;
-        if (need && amax > 0.0f && amax < __builtin_inff()) {
-          e = 14 - ilogbf(amax);
-          e = e > 126 ? 126 : (e < -126 ? -126 : e);
+        const int e = need ? row_exponent(__builtin_bit_cast(float, rowmax[row])) : 0;
+        const float scl = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+        const int r0 = act ? NT * row : NT * T + (row - T);
+        const int nterm = act ? NT : 1;
+        if (live && pc == 0) {
+#pragma unroll
+          for (int term = 0; term < NT; ++term)
+            if (term < nterm) ex[r0 + term] = e;
         }
-        const float scl = ldexpf(1.0f, e);
-        const int r0 = act ? terms * row : terms * T + (row - T);
-        const int nterm = act ? terms : 1;
-        if (live && pc == 0)
-          for (int term = 0; term < nterm; ++term) ex[r0 + term] = e;
-        float a[8], g[8];
-        unpack8(raw[u], p.x_dtype, a);
-        unpack8(graw[u], p.x_dtype, g);
+        float v[8];
+        unpack_t<XDT>(sr.raw[u], v);
+        if (p.ln) {
+          const float x0 = act ? x0s[row] : 0.0f;
+          float g[8];
+          unpack_t<XDT>(sr.graw[u], g);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) v[jj] = (v[jj] - x0) * g[jj];
+        }
         uint32_t el[NT][8];
         float ts[NT];
 #pragma unroll
         for (int term = 0; term < NT; ++term) ts[term] = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const int kj = slot_k<BITS>(jj);
-          const float v = mulg ? (a[kj] - x0) * g[kj] : a[kj];
-          const float sv = v * scl;
-          if constexpr (BF16OP) {
-            const uint32_t hi = to_op_bits<true>(sv);
-            const float r1 = sv - op_bits_to_float<true>(hi);
-            const uint32_t mid = to_op_bits<true>(r1);
-            const uint32_t lo = to_op_bits<true>(r1 - op_bits_to_float<true>(mid));
-            el[0][jj] = hi; el[1][jj] = mid; el[2][jj] = lo;
-          } else {
-            const uint32_t hi = to_op_bits<false>(sv);
-            el[0][jj] = hi;
-            el[1][jj] = to_op_bits<false>(sv - op_bits_to_float<false>(hi));
+          const float sv = v[slot_k<BITS>(jj)] * (slot_hi_nibble<BITS>(jj) ? scl * 0.0625f : scl);
+          const uint32_t hi = to_op_bits<BF16OP>(sv);
+          el[0][jj] = hi;
+          if constexpr (NT >= 2) {
+            const float r1 = sv - op_bits_to_float<BF16OP>(hi);
+            const uint32_t mid = to_op_bits<BF16OP>(r1);
+            el[1][jj] = mid;
+            if constexpr (NT == 3) el[2][jj] = to_op_bits<BF16OP>(r1 - op_bits_to_float<BF16OP>(mid));
           }
 #pragma unroll
-          for (int term = 0; term < NT; ++term) ts[term] += op_bits_to_float<BF16OP>(el[term][jj]);
+          for (int term = 0; term < NT; ++term)   // group sums of the values as represented, unscaled by 1/16
+            ts[term] += op_bits_to_float<BF16OP>(el[term][jj]) * (slot_hi_nibble<BITS>(jj) ? 16.0f : 1.0f);
         }
 #pragma unroll
         for (int term = 0; term < NT; ++term) {
@@ -374,13 +459,14 @@ struct Fused {
         if constexpr (QUANT) {
 #pragma unroll
           for (int term = 0; term < NT; ++term) {
-            float t = ts[term];
-            t += __shfl_xor(t, 1);
-            t += __shfl_xor(t, 2);
-            t += __shfl_xor(t, 4);
+            const float t = sum8(ts[term]);
             if (term < nterm && live && (pc & 7) == 0) gsum[(r0 + term) * gpr + pc / 8] = t;
           }
         }
+      } else {
+        // pieces past the chunk were loaded on some paths: read them on this one too, or the
+        // compiler drains every load in flight before reusing their registers
+        asm volatile("" ::"v"(sr.raw[u]), "v"(sr.graw[u]));
       }
     }
     // LayerNorm sums of each activation row, in group order
@@ -413,7 +499,7 @@ struct Fused {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = 16 * mt + 4 * c + v;
-        unscale[mt][v] = r < R ? ldexpf(1.0f, -ex[r]) : 1.0f;
+        unscale[mt][v] = r < R ? ldexpf(1.0f, (QUANT ? 24 : 0) - ex[r]) : 1.0f;   // QUANT: undo kCodeScale
       }
       if constexpr (QUANT) {
         const int r = 16 * mt + li;
@@ -461,8 +547,10 @@ struct Fused {
     const bool mine = !p.gateup && tile < p.ntiles && t < p.T && on < p.N;
     const gptr<const uint16_t> rp = pick(reinterpret_cast<const uint16_t*>(p.res), reinterpret_cast<const uint16_t*>(p.res), 0);
     const gptr<const uint16_t> ap = pick(reinterpret_cast<const uint16_t*>(p.add), reinterpret_cast<const uint16_t*>(p.add), 0);
-    e.res = *((mine && p.res) ? rp + (long)t * p.N + on : z16);
-    e.add = *((mine && p.add) ? ap + on : z16);
+    e.res = 0;
+    e.add = 0;
+    if (p.res) e.res = *(mine ? rp + (long)t * p.N + on : z16);   // uniform: no loads without inputs
+    if (p.add) e.add = *(mine ? ap + on : z16);
   }
 
   // Issue the loads of a tile's codes, scales and biases for steps [s_lo, s_lo + nsw).
@@ -470,7 +558,7 @@ struct Fused {
   // row (n >= N, or a tile past the last) streams from the zero buffer instead, so every
   // tile issues the same loads; steps >= nsw (uniform) are skipped.  Rows must consist of
   // whole 64-byte steps (4-bit K = 64 mod 128 goes through the chunked variant).
-  template <bool CHECKED = false>
+  template <bool CHECKED = false, bool SB = true>
   __device__ __forceinline__ static void load_tile(const LinParams& p, int tile, int s_lo, int nsw, int c, int li,
                                                    TileRegs& r) {
     int proj, n;
@@ -494,7 +582,7 @@ struct Fused {
         r.dw[s] = *reinterpret_cast<gptr<const u4_t>>(a);
       }
     }
-    if constexpr (QUANT) {
+    if constexpr (QUANT && SB) {
       // A step's scales (biases) are NG consecutive fp16 values: 4-bit steps load them as one
       // aligned dword (K is a multiple of 128 here, so n*G + 2*s is even), 8-bit as a ushort.
       // They stay packed until compute_tile; splitting them here would make the compiler wait.
@@ -530,12 +618,49 @@ struct Fused {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Stream one tile's loaded codes through the fragments into acc.
-  __device__ __forceinline__ void compute_tile(int nsw, int c, const TileRegs& r, f4_t acc[MT]) {
+  // ---- scales and biases of a tile through an LDS ring (streaming variant) ----------
+  // The workgroup fetches a tile's scales and biases with one coalesced 16-byte load per
+  // thread, a tile ahead, and parks them in a ring slot: [scales, biases][16 rows][pitch].
+  // Per-lane loads of a few bytes from 16 rows each would cost as much memory-pipeline time
+  // as the codes themselves.  Needs G = K / 64 a multiple of 8 (rows of whole 16-byte
+  // chunks) and G <= 128 (one chunk per thread).
+  __host__ __device__ static constexpr int sb_pitch(int G) { return 2 * G + 4; }   // bytes; +4 spreads rows over banks
+  __host__ __device__ static constexpr int sb_slot_bytes(int G) { return 32 * sb_pitch(G); }
+  struct SbRegs {
+    u4_t v;
+  };
+  __device__ __forceinline__ static void sb_issue(const LinParams& p, int tile, int tid, SbRegs& sb) {
+    const int G = p.K / 64, cpr = G / 8;              // 16-byte chunks per row
+    const int a = tid / (16 * cpr), r = (tid / cpr) % 16, col = tid % cpr;
+    int proj, n;
+    tile_row(p, tile, r, proj, n);
+    const bool valid = tid < 32 * cpr && tile < p.ntiles && n < p.N;
+    const uintptr_t u0 = reinterpret_cast<uintptr_t>(a ? p.bi[0] : p.sc[0]);
+    const uintptr_t u1 = reinterpret_cast<uintptr_t>(a ? p.bi[1] : p.sc[1]);
+    const gptr<const char> row = reinterpret_cast<gptr<const char>>(u0 + (uintptr_t)proj * (u1 - u0)) + (long)n * G * 2;
+    const gptr<const char> zero = pick(reinterpret_cast<const char*>(g_zero16), reinterpret_cast<const char*>(g_zero16), 0);
+    sb.v = *reinterpret_cast<gptr<const u4_t>>(valid ? row + 16 * col : zero);
+  }
+  __device__ __forceinline__ static void sb_commit(const LinParams& p, int tid, const SbRegs& sb, unsigned char* slot) {
+    const int G = p.K / 64, cpr = G / 8;
+    asm volatile("" ::"v"(sb.v));   // read on every path (see compute_core)
+    if (tid < 32 * cpr) {
+      const int a = tid / (16 * cpr), r = (tid / cpr) % 16, col = tid % cpr;
+      uint32_t* d = reinterpret_cast<uint32_t*>(slot + (a * 16 + r) * sb_pitch(G) + 16 * col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = sb.v[j];
+    }
+  }
+
+  // One tile through the fragments: codes dw, per-step scale words sc (the step's NG fp16
+  // scales, group g in bits 16g) and the bias operand bfr (slot j of lane group c holds the
+  // bias of this wave's group 8*(c&1) + j, 0 past the slice).
+  __device__ __forceinline__ void compute_core(int nsw, const u4_t dw[MAXS], const uint32_t sc[MAXS], const u4_t& bfr,
+                                               f4_t acc[MT]) {
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
       if (s < nsw) {
-        u4_t d = r.dw[s];
+        u4_t d = dw[s];
         if constexpr (BITS == 4) {
           const auto r01 = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
           const auto r23 = __builtin_amdgcn_permlane32_swap(d[2], d[3], false, false);
@@ -559,7 +684,7 @@ struct Fused {
             }
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
-            const float sf = half_bits_to_float((r.sc[s] >> (16 * g)) & 0xFFFFu);
+            const float sf = half_bits_to_float((sc[s] >> (16 * g)) & 0xFFFFu);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -572,12 +697,24 @@ struct Fused {
       } else {
         // unused step: still read its (zero) registers, so that no path leaves a load unread
         // (the compiler would drain every outstanding load, the prefetch too, before reusing them)
-        asm volatile("" ::"v"(r.dw[s]), "v"(r.sc[s]), "v"(r.bi[s]));
+        asm volatile("" ::"v"(dw[s]), "v"(sc[s]));
       }
     }
     if constexpr (QUANT) {
       // sum_g b[n, g] * (sum of group g's operands): one MFMA per row tile
-      // slot j of lane group c is the bias of this wave's group 8*(c&1) + j
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f4_t cb = mfma<false>(gfrag[mt], bfr, (f4_t){0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(cb[v], (float)(1 << kGsumShift) * kCodeScale, acc[mt][v]);
+      }
+    }
+  }
+
+  // A tile whose scales and biases came with its codes (chunked variant).
+  __device__ __forceinline__ void compute_tile(int nsw, int c, const TileRegs& r, f4_t acc[MT]) {
+    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
+    if constexpr (QUANT) {
       uint32_t el[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -587,56 +724,103 @@ struct Fused {
                                 ? (r.bi[(8 + j) / NG] >> (16 * ((8 + j) % NG))) & 0xFFFFu : 0u;
         el[j] = (c & 1) ? hi : lo;
       }
-      u4_t bfr;
 #pragma unroll
       for (int w = 0; w < 4; ++w) bfr[w] = el[2 * w] | (el[2 * w + 1] << 16);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f4_t cb = mfma<false>(gfrag[mt], bfr, (f4_t){0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(cb[v], (float)(1 << kGsumShift), acc[mt][v]);
-      }
     }
+    compute_core(nsw, r.dw, r.sc, bfr, acc);
+  }
+
+  // A tile whose scales and biases sit in ring slot `slot` (streaming variant).
+  __device__ __forceinline__ void compute_ring(const LinParams& p, int nsw, int s_lo, int c, int li, const u4_t dw[MAXS],
+                                               const unsigned char* slot, f4_t acc[MT]) {
+    uint32_t sc[MAXS];
+    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
+    if constexpr (QUANT) {
+      const int G = p.K / 64, pitch = sb_pitch(G);
+      const unsigned char* srow = slot + li * pitch;
+      const unsigned char* brow = slot + (16 + li) * pitch;
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) {
+        if constexpr (NG == 2) sc[s] = s < nsw ? *reinterpret_cast<const uint32_t*>(srow + 4 * (s_lo + s)) : 0u;
+        else sc[s] = s < nsw ? *reinterpret_cast<const uint16_t*>(srow + 2 * (s_lo + s)) : 0u;
+      }
+      if constexpr (NG == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {   // dword w: both groups of step 4*(c&1) + w
+          const int j = 4 * (c & 1) + w;
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(brow + 4 * min(s_lo + j, G / 2 - 1));
+          bfr[w] = j < nsw ? v : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {   // halves of steps 8*(c&1) + 2w and + 2w + 1
+          const int j0 = 8 * (c & 1) + 2 * w, j1 = j0 + 1;
+          const uint32_t v0 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j0, G - 1));
+          const uint32_t v1 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j1, G - 1));
+          bfr[w] = (j0 < nsw ? v0 : 0u) | ((j1 < nsw ? v1 : 0u) << 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) sc[s] = 0u;
+    }
+    compute_core(nsw, dw, sc, bfr, acc);
   }
 };
 
-// Sum over the workgroup's waves of C row r, column col, from the LDS partials.
+// Sum over the workgroup's waves of C row r, column col, from the LDS partials: all reads
+// are issued before the first add (one LDS round trip), the adds run in wave order.
 template <int MT>
 __device__ __forceinline__ float merged(const float* red, int buf, int r, int col) {
   const int lane = 16 * ((r & 15) >> 2) + col;
+  float v[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) v[w] = red[((buf * kWaves + w) * MT + (r >> 4)) * 256 + lane * 4 + (r & 3)];
   float s = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[((buf * kWaves + w) * MT + (r >> 4)) * 256 + lane * 4 + (r & 3)];
+  for (int w = 0; w < kWaves; ++w) s += v[w];
   return s;
 }
 
 // Output value before the epilogue: no LN, the sum of the row's terms; with LN the fold
-// rstd * (P - m G) + B, m = S1 / K and var = S2 / K - m^2 (biased, clamped at 0).
-template <int MT>
-__device__ __forceinline__ float folded(const LinParams& p, const float* red, const float* stat, int buf, int t, int col) {
+// rstd * (P - m G) + B with the row's m and rstd from row_moments.
+template <int MT, int NT>
+__device__ __forceinline__ float folded(const LinParams& p, const float* red, const float* mr, int buf, int t, int col) {
   const int terms = p.terms;
+  float part[NT];
+#pragma unroll
+  for (int term = 0; term < NT; ++term)   // rows past the operand's terms read row 0, unused
+    part[term] = merged<MT>(red, buf, term < terms ? terms * t + term : 0, col);
   float P = 0.0f;
-  for (int term = 0; term < terms; ++term) P += merged<MT>(red, buf, terms * t + term, col);
+#pragma unroll
+  for (int term = 0; term < NT; ++term)
+    if (term < terms) P += part[term];
   if (!p.ln) return P;
   const float Gw = merged<MT>(red, buf, terms * p.T, col);
   const float Bw = merged<MT>(red, buf, terms * p.T + 1, col);
+  return mr[2 * t + 1] * (P - mr[2 * t] * Gw) + Bw;
+}
+
+// Per-row LN moments from the shifted sums S1, S2 of row t: m = S1 / K (the mean of the
+// shifted row), var = S2 / K - m^2 (biased, clamped at 0), rstd = 1 / sqrt(var + eps).
+__device__ __forceinline__ void row_moments(const LinParams& p, const float* stat, float* mr, int t) {
   const float m = stat[2 * t] / (float)p.K;
   const float var = fmaxf(stat[2 * t + 1] / (float)p.K - m * m, 0.0f);
-  const float rstd = 1.0f / sqrtf(var + p.eps);
-  return rstd * (P - m * Gw) + Bw;
+  mr[2 * t] = m;
+  mr[2 * t + 1] = 1.0f / sqrtf(var + p.eps);
 }
 
 // Epilogue and store of one tile ([p1] `_linear_kernel`: GELU, then residual, then constant).
 // Thread tid finishes output slot out_slot(tid, tile).
-template <int MT>
-__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* stat, int buf, int tile, int tid,
+template <int MT, int NT>
+__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* mr, int buf, int tile, int tid,
                                          uint32_t res_bits, uint32_t add_bits) {
   tid = out_slot(tid, tile);
   if (!p.gateup) {
     if (tid < p.T * 16) {
       const int t = tid >> 4, col = tid & 15, n = tile * 16 + col;
       if (n < p.N) {
-        float v = folded<MT>(p, red, stat, buf, t, col);
+        float v = folded<MT, NT>(p, red, mr, buf, t, col);
         if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
         if (p.res) v += elem_to_float(res_bits, p.x_dtype);
         if (p.add) v += elem_to_float(add_bits, p.x_dtype);
@@ -647,8 +831,8 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
     if (tid < p.T * 8) {
       const int t = tid >> 3, j = tid & 7, n = tile * 8 + j;
       if (n < p.N) {
-        const float g = folded<MT>(p, red, stat, buf, t, j);
-        const float u = folded<MT>(p, red, stat, buf, t, j + 8);
+        const float g = folded<MT, NT>(p, red, mr, buf, t, j);
+        const float u = folded<MT, NT>(p, red, mr, buf, t, j + 8);
         store_out(p.y, p.y_dtype, (long)t * p.N + n, g / (1.0f + expf(-g)) * u);
       }
     }
@@ -663,13 +847,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   float* stat = reinterpret_cast<float*>(lds_raw);
   int* ex = reinterpret_cast<int*>(lds_raw + kStatFloats * 4);
   unsigned* rowmax = reinterpret_cast<unsigned*>(lds_raw + (kStatFloats + kExpInts) * 4);
+  float* x0s = reinterpret_cast<float*>(lds_raw + (kStatFloats + kExpInts + kRowMax) * 4);
+  float* mr = reinterpret_cast<float*>(lds_raw + (kStatFloats + kExpInts + 2 * kRowMax) * 4);
   unsigned char* region = lds_raw + kHeaderBytes;
   float* red = reinterpret_cast<float*>(region);
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane >> 4, li = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  auto slice = [&](int ch, int& cs0, int& s_lo, int& nsw) {
+  auto slice = [&](int ch, int& cs0, int& s_lo, int& nsw) __attribute__((always_inline)) {
     cs0 = ch * p.chunk_steps;
     const int sc = min(p.chunk_steps, p.steps - cs0);
     s_lo = cs0 + (wv * sc) / kWaves;
@@ -677,7 +863,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   };
   // Stage chunk ch into LDS and load this wave's fragments from it.
   S st;
-  auto prepare = [&](int ch, bool stats, int& cs0, int& s_lo, int& nsw) {
+  // Stage chunk ch (its pieces already in sr), run after_stage, load this wave's fragments.
+  auto prepare = [&](int ch, bool stats, int& cs0, int& s_lo, int& nsw, const typename S::StageRegs& sr,
+                     auto&& after_stage) __attribute__((always_inline)) {
     slice(ch, cs0, s_lo, nsw);
     const int kc0 = cs0 * STEPK;
     const int kc = min(p.chunk_steps * STEPK, p.K - kc0);
@@ -686,13 +874,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     float* spart = gsum + (long)p.rows * (kc / 64);
     if (tid < kRowMax) rowmax[tid] = 0u;
     lds_barrier();
-    S::stage(p, stat, ex, rowmax, spart, op, gsum, kc0, kc, stats, tid);
+    S::stage_compute(p, stat, ex, rowmax, x0s, spart, op, gsum, kc0, kc, stats, tid, sr);
+    after_stage();
     lds_barrier();
+    if (stats && p.ln && tid < p.T) row_moments(p, stat, mr, tid);   // read after a later barrier
     st.load_frags(p, ex, op, gsum, kc0, kc, cs0, s_lo, nsw, c, li);
     lds_barrier();
   };
-  // Merge the waves' partials of a tile in LDS (double-buffered by tile parity), finish it.
-  auto merge_finish = [&](const f4_t acc[MT], int tile, int buf, const typename S::EpiRegs& e) {
+  // This wave's partials of a tile into LDS (double-buffered by tile parity).
+  auto write_partials = [&](const f4_t acc[MT], int buf) __attribute__((always_inline)) {
     float* rb = red + (buf * kWaves + wv) * MT * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -701,59 +891,78 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       for (int j = 0; j < 4; ++j) v[j] = acc[mt][j] * st.unscale[mt][j];
       *reinterpret_cast<f4_t*>(rb + mt * 256 + lane * 4) = v;
     }
+  };
+  // Merge the waves' partials of a tile and finish it.
+  auto finish = [&](int tile, int buf, const typename S::EpiRegs& e) __attribute__((always_inline)) {
     // Every lane reads its residual and constant here, used or not: a loaded register left
     // unread on some path makes the compiler drain all loads (the prefetch too) before the
     // register is reused.
     const uint32_t res_bits = e.res, add_bits = e.add;
     asm volatile("" ::"v"(res_bits), "v"(add_bits));
     lds_barrier();
-    finalize<MT>(p, red, stat, buf, tile, tid, res_bits, add_bits);
+    finalize<MT, BF16OP ? 3 : 2>(p, red, mr, buf, tile, tid, res_bits, add_bits);
   };
 
   if (tid < kStatFloats) stat[tid] = 0.0f;
-  lds_barrier();
-
   int cs0, s_lo, nsw;
   if constexpr (!CHUNKED) {
-    // All of K fits: build the fragments once, then stream tiles with the next tile's loads
-    // always in flight.  Two register sets alternate (no copy at the end of an iteration,
-    // which would make the compiler wait for the prefetch).
+    // All of K fits: build the fragments once, then stream tiles with the next tile's codes,
+    // scales and biases always in flight.  Two code register sets alternate (no copy at the
+    // end of an iteration, which would make the compiler wait for the prefetch); scales and
+    // biases alternate between two ring slots.
     slice(0, cs0, s_lo, nsw);
-    typename S::TileRegs ra, rb;
     int tile = blockIdx.x;
-    S::load_tile(p, tile, s_lo, nsw, c, li, ra);   // the weight stream starts before staging
-    prepare(0, true, cs0, s_lo, nsw);
-    int buf = 0;
-    for (;;) {
-      // epilogue inputs are loaded and used within one half: a load still in flight across
-      // the loop edge would make the compiler drain the prefetch at the top of the loop
+    unsigned char* ring = region + (staging_bytes(p.rows, p.K) > merge_bytes(MT) ? staging_bytes(p.rows, p.K)
+                                                                                   : merge_bytes(MT));
+    const int slot_bytes = S::sb_slot_bytes(p.K / 64);
+    // Issue order: the first tile's scales, the staged rows, then the first tile's codes, so
+    // that staging waits for its own rows only and the code stream runs under it.
+    typename S::SbRegs sb0;
+    if constexpr (S::QUANT) S::sb_issue(p, tile, tid, sb0);
+    typename S::StageRegs sr;
+    S::stage_load(p, 0, p.K, tid, sr);
+    typename S::TileRegs ra, rb;
+    S::template load_tile<false, false>(p, tile, s_lo, nsw, c, li, ra);
+    prepare(0, true, cs0, s_lo, nsw, sr, [&] {
+      if constexpr (S::QUANT) S::sb_commit(p, tid, sb0, ring);
+    });
+    // One half: the next tile's scales and codes and this tile's epilogue inputs are issued,
+    // then `tile` is computed from `cur` (loaded one half earlier) and finished.  Epilogue
+    // inputs are loaded and read within one half: a load in flight across the loop edge
+    // would make the compiler drain the prefetch at the top of the loop.
+    auto half = [&](const typename S::TileRegs& cur, typename S::TileRegs& nxt, int tile, int next,
+                    int buf) __attribute__((always_inline)) {
+      typename S::SbRegs sb;
+      if constexpr (S::QUANT) S::sb_issue(p, next, tid, sb);   // past the last tile: zeros
       typename S::EpiRegs e;
       S::load_epi(p, tile, e);
-      const int t1 = tile + gridDim.x;
-      S::load_tile(p, t1, s_lo, nsw, c, li, rb);   // past the last tile this loads zeros
-      {
-        f4_t acc[MT];
+      S::template load_tile<false, false>(p, next, s_lo, nsw, c, li, nxt);
+      f4_t acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-        st.compute_tile(nsw, c, ra, acc);
-        merge_finish(acc, tile, buf, e);
-      }
-      tile = t1;
-      buf ^= 1;
-      if (tile >= p.ntiles) break;
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      st.compute_ring(p, nsw, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
+      write_partials(acc, buf);
+      if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);   // slot read last half
+      finish(tile, buf, e);
+    };
+    // Tiles come in pairs so that the loop is entered again only after the second half: an
+    // exit test after the first half that shares a block with the loop test would leave the
+    // second set's loads looking unread at the top of the loop.
+    const int G = gridDim.x;
+    const int n = (p.ntiles - tile + G - 1) / G;   // this block's tiles (>= 1: grid <= ntiles)
+    for (int i = 0; i + 1 < n; i += 2, tile += 2 * G) {
+      half(ra, rb, tile, tile + G, 0);
+      half(rb, ra, tile + G, tile + 2 * G, 1);
+    }
+    if (n & 1) {
+      typename S::EpiRegs e;
       S::load_epi(p, tile, e);
-      const int t2 = tile + gridDim.x;
-      S::load_tile(p, t2, s_lo, nsw, c, li, ra);
-      {
-        f4_t acc[MT];
+      f4_t acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-        st.compute_tile(nsw, c, rb, acc);
-        merge_finish(acc, tile, buf, e);
-      }
-      tile = t2;
-      buf ^= 1;
-      if (tile >= p.ntiles) break;
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      st.compute_ring(p, nsw, s_lo, c, li, ra.dw, ring, acc);
+      write_partials(acc, 0);
+      finish(tile, 0, e);
     }
   } else {
     // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
@@ -773,7 +982,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) prev[mt][j] = st.unscale[mt][j];
         if (!first || ch > 0) lds_barrier();   // earlier readers of the LDS region are done
-        prepare(ch, first, cs0, s_lo, nsw);
+        typename S::StageRegs sr;
+        slice(ch, cs0, s_lo, nsw);
+        S::stage_load(p, cs0 * STEPK, min(p.chunk_steps * STEPK, p.K - cs0 * STEPK), tid, sr);
+        prepare(ch, first, cs0, s_lo, nsw, sr, [] {});
         S::template load_tile<true>(p, tile, s_lo, nsw, c, li, r);
         if (ch > 0) {
 #pragma unroll
@@ -786,14 +998,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       first = false;
       typename S::EpiRegs e;
       S::load_epi(p, tile, e);
-      merge_finish(acc, tile, buf, e);
+      write_partials(acc, buf);
+      finish(tile, buf, e);
     }
   }
 }
 
-// Dynamic LDS a launch needs: header + max(staging, merge).
+// Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
 __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
-  return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt));
+  return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt)) +
+         2L * 32 * (2 * (kc / 64) + 4);   // two scale/bias ring slots
 }
 
 template <int BITS, bool BF16OP, int MT, bool CHUNKED>
@@ -813,8 +1027,11 @@ hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t 
 template <int BITS, bool BF16OP, int MT>
 hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // The streaming variant needs all of K staged at once and rows of whole 64-byte steps.
+  // Quantized weights also need rows of whole 16-byte scale chunks, at most 128 groups.
   const bool whole_steps = ((long)p.K * BITS / 8) % 64 == 0;
-  return (p.chunk_steps >= p.steps && whole_steps) ? launch_variant<BITS, BF16OP, MT, false>(p, grid, lds, s)
+  const int G = p.K / 64;
+  const bool ring_ok = BITS == 16 || (G % 8 == 0 && G <= 128);
+  return (p.chunk_steps >= p.steps && whole_steps && ring_ok) ? launch_variant<BITS, BF16OP, MT, false>(p, grid, lds, s)
                                                    : launch_variant<BITS, BF16OP, MT, true>(p, grid, lds, s);
 }
 

@@ -113,7 +113,8 @@ qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, 
   p.gamma = ln ? ln->gamma : nullptr; p.beta = ln ? ln->beta : nullptr; p.eps = ln ? ln->eps : 0.0f;
   const bool bf16op = w->bits == 16 && w->dtype == QLIN_BF16;
   if (bf16op) {            // dense bf16 weights: bf16 operands, exact 1- or 3-term activations
-    p.terms = p.ln ? 3 : 1; p.scale_act = 0; p.scale_gb = 0;
+    // (bf16 x is one bf16 term; fp16 x and LN outputs need three)
+    p.terms = (p.ln || x_dtype == QLIN_F16) ? 3 : 1; p.scale_act = 0; p.scale_gb = 0;
   } else {                 // fp16 operands: 1 term when x is fp16 and there is no LN, else 2 scaled terms
     p.terms = p.ln ? 2 : 1;
     p.scale_act = (p.ln || x_dtype == QLIN_BF16) ? 1 : 0;
