@@ -242,6 +242,22 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
+def measured_traffic():
+    """HBM bytes per call of the headline kernel from the committed counter record
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings),
+    or None once the kernel sources differ from those the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -285,7 +301,7 @@ def main():
         "us_per_call": round(us, 3),
         "pct_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic()},
     }
     if extra:
         line["workloads"] = extra
