@@ -181,6 +181,8 @@ constexpr int kHeaderBytes = (2 * kStatFloats + kExpInts + 2 * kRowMax) * 4;   /
 // Largest dynamic LDS a launch may ask for (gfx950 has 160 KiB per CU).
 // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Elements of an epilogue-input slot: residual rows of up to 32 outputs rows and the constant row, 16 columns.
+constexpr int kEpiSlot = 33 * 16;
 constexpr int kLdsMax = 160 * 1024;
 
 __host__ __device__ constexpr int op_pitch(int kc) { return kc + kRowPad; }
@@ -199,12 +201,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Output slot of thread tid for a tile: outputs 0..63 go to wave (tile mod 8), so the
-// epilogue work rotates over the waves instead of always landing on wave 0.
-__device__ __forceinline__ int out_slot(int tid, int tile) {
-  return (tid + kThreads - 64 * (tile % kWaves)) % kThreads;
 }
 
 // Reductions over aligned groups of 8 lanes with DPP moves (lane i sees lane i^1, then i^2
@@ -290,12 +286,13 @@ struct Fused {
     const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.gamma);
     const uint16_t* b16 = reinterpret_cast<const uint16_t*>(p.beta);
     const uint32_t one = p.x_dtype == 1 ? 0x3C003C00u : 0x3F803F80u;
+    const uint32_t magic = 0xFFFFFFFFu / (uint32_t)ppr + 1u;   // idx / ppr as a multiply-high
 #pragma unroll
     for (int u = 0; u < kPieceMax; ++u) {
       const int idx = tid + kThreads * u;
       sr.graw[u] = (u4_t){one, one, one, one};
       if (idx < total) {
-        const int row = idx / ppr, pc = idx - (idx / ppr) * ppr;
+        const int row = (int)__umulhi((uint32_t)idx, magic), pc = idx - row * ppr;
         const bool act = row < T;
         const gptr<const uint16_t> src = pick(act ? x16 : g16, b16, (!act && row != T) ? 1 : 0) +
                                          (act ? (long)row * p.K : 0) + kc0 + 8 * pc;
@@ -361,6 +358,12 @@ struct Fused {
     }
     // pass 1: row maxima (only rows that are scaled) and LN sums
     if (p.ln || p.scale_act) {
+      float x0r1[kPieceMax];
+#pragma unroll
+      for (int u = 0; u < kPieceMax; ++u) {   // shifts read up front (one LDS round trip)
+        const int row = (int)__umulhi((uint32_t)min(tid + kThreads * u, total - 1), magic);
+        x0r1[u] = p.ln && row < T ? x0s[row] : 0.0f;
+      }
 #pragma unroll
       for (int u = 0; u < kPieceMax; ++u) {
         if (kThreads * u < total) {                    // uniform: some lane of the block is live
@@ -372,7 +375,7 @@ struct Fused {
           float amax = 0.0f;
           if (p.ln) {
             const bool lnr = row < T;
-            const float x0 = lnr ? x0s[row] : 0.0f;
+            const float x0 = x0r1[u];
             float g[8];
             unpack_t<XDT>(sr.graw[u], g);
             float s1 = 0.0f, s2 = 0.0f;
@@ -401,7 +404,12 @@ struct Fused {
       }
       lds_barrier();
     }
-    // pass 2
+    // pass 2.  The row maxima (and shifts) of every piece are read up front, from in-range
+    // rows also for pieces past the chunk, so that the reads share one LDS round trip.
+    uint32_t rmax[kPieceMax];
+#pragma unroll
+    for (int u = 0; u < kPieceMax; ++u)
+      rmax[u] = rowmax[(int)__umulhi((uint32_t)min(tid + kThreads * u, total - 1), magic)];
 #pragma unroll
     for (int u = 0; u < kPieceMax; ++u) {
       if (kThreads * u < total) {
@@ -410,7 +418,7 @@ struct Fused {
         const int row = live ? (int)__umulhi((uint32_t)idx, magic) : 0, pc = idx - row * ppr;
         const bool act = row < T;
         const bool need = act ? p.scale_act : p.scale_gb;
-        const int e = need ? row_exponent(__builtin_bit_cast(float, rowmax[row])) : 0;
+        const int e = need ? row_exponent(__builtin_bit_cast(float, rmax[u])) : 0;
         const float scl = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
         const int r0 = act ? NT * row : NT * T + (row - T);
         const int nterm = act ? NT : 1;
@@ -488,28 +496,30 @@ struct Fused {
       for (int q = 0; q < NM; ++q)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int r = 16 * mt + li;
-          const int kk = (s_lo + s) * STEPK + frag_base<BITS>(q, c) - kc0;
-          u4_t a = (u4_t){0u, 0u, 0u, 0u};
-          if (s < nsw && r < R && kk < kc) a = *reinterpret_cast<const u4_t*>(op + (long)r * pitch + kk);
-          afrag[s][q][mt] = a;
+          // Rows past R and steps past the slice read in-range data that is never used: an
+          // A row only feeds its own C row, and steps >= nsw are skipped.  No branches, so
+          // all reads share one LDS round trip.
+          const int r = min(16 * mt + li, R - 1);
+          const int kk = min((s_lo + s) * STEPK + frag_base<BITS>(q, c) - kc0, kc - 8);
+          afrag[s][q][mt] = *reinterpret_cast<const u4_t*>(op + (long)r * pitch + max(kk, 0));
         }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 16 * mt + 4 * c + v;
-        unscale[mt][v] = r < R ? ldexpf(1.0f, (QUANT ? 24 : 0) - ex[r]) : 1.0f;   // QUANT: undo kCodeScale
+      for (int v = 0; v < 4; ++v) {   // 2^-e; rows past R: any finite factor (never read back)
+        const int r = min(16 * mt + 4 * c + v, R - 1);
+        unscale[mt][v] = __builtin_bit_cast(float, (uint32_t)(127 - ex[r]) << 23);
       }
       if constexpr (QUANT) {
         const int r = 16 * mt + li;
         uint32_t el[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+          // slots past the slice meet a zero bias (compute_ring / compute_tile), so any finite
+          // in-range group sum does
           const int gi = 8 * (c & 1) + j;
-          const int gl = (s_lo - cs0) * NG + gi;
-          float v = 0.0f;
-          if (r < R && gi < nsw * NG && gl < gpr) v = gsum[r * gpr + gl] * (1.0f / (float)(1 << kGsumShift));
+          const int gl = min((s_lo - cs0) * NG + gi, gpr - 1);
+          const float v = gsum[min(r, R - 1) * gpr + gl] * (1.0f / (float)(1 << kGsumShift));
           const uint32_t hi = to_op_bits<false>(v);
           const uint32_t lo = to_op_bits<false>(v - op_bits_to_float<false>(hi));
           el[j] = (c >> 1) ? lo : hi;
@@ -534,23 +544,37 @@ struct Fused {
     uint32_t bi[MAXS];      // fp16 bias bits, packed the same way
   };
 
-  // Epilogue inputs of the output this thread finishes, out_slot(tid, tile) = (t, col):
-  // residual[t, n] and constant[n] of a linear tile (zeros when absent or out of range).
-  struct EpiRegs {
-    uint16_t res, add;
+  // Epilogue inputs of a linear tile: residual[t, n0 .. n0+15] for t < T and constant[n0 ..
+  // n0+15] (n0 = 16 tile), fetched by the workgroup a tile ahead, one element per thread and
+  // round (consecutive lanes, consecutive columns), into an LDS slot [T + 1][16] of the
+  // input type.  Nothing is loaded when the call has neither.
+  struct EpRegs {
+    uint32_t v[2];   // (T + 1) * 16 <= 528 elements: at most two per thread
   };
-  __device__ __forceinline__ static void load_epi(const LinParams& p, int tile, EpiRegs& e) {
+  __device__ __forceinline__ static void ep_issue(const LinParams& p, int tile, int tid, EpRegs& e) {
+    e.v[0] = e.v[1] = 0u;
+    if (p.gateup || !(p.res || p.add)) return;   // uniform
     const gptr<const uint16_t> z16 = pick(reinterpret_cast<const uint16_t*>(g_zero16),
                                           reinterpret_cast<const uint16_t*>(g_zero16), 0);
-    const int q = out_slot(threadIdx.x, tile);
-    const int t = q >> 4, on = tile * 16 + (q & 15);
-    const bool mine = !p.gateup && tile < p.ntiles && t < p.T && on < p.N;
     const gptr<const uint16_t> rp = pick(reinterpret_cast<const uint16_t*>(p.res), reinterpret_cast<const uint16_t*>(p.res), 0);
     const gptr<const uint16_t> ap = pick(reinterpret_cast<const uint16_t*>(p.add), reinterpret_cast<const uint16_t*>(p.add), 0);
-    e.res = 0;
-    e.add = 0;
-    if (p.res) e.res = *(mine ? rp + (long)t * p.N + on : z16);   // uniform: no loads without inputs
-    if (p.add) e.add = *(mine ? ap + on : z16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int el = tid + kThreads * i, row = el >> 4, n = tile * 16 + (el & 15);
+      const bool ok = tile < p.ntiles && n < p.N && row <= p.T;
+      const bool isres = row < p.T;
+      const bool have = ok && (isres ? p.res != nullptr : p.add != nullptr);
+      e.v[i] = *(have ? (isres ? rp + (long)row * p.N + n : ap + n) : z16);
+    }
+  }
+  __device__ __forceinline__ static void ep_commit(const LinParams& p, int tid, const EpRegs& e, uint16_t* slot) {
+    asm volatile("" ::"v"(e.v[0]), "v"(e.v[1]));   // read on every path (see compute_core)
+    if (p.gateup || !(p.res || p.add)) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int el = tid + kThreads * i;
+      if (el < (p.T + 1) * 16) slot[el] = (uint16_t)e.v[i];
+    }
   }
 
   // Issue the loads of a tile's codes, scales and biases for steps [s_lo, s_lo + nsw).
@@ -631,7 +655,8 @@ struct Fused {
   };
   __device__ __forceinline__ static void sb_issue(const LinParams& p, int tile, int tid, SbRegs& sb) {
     const int G = p.K / 64, cpr = G / 8;              // 16-byte chunks per row
-    const int a = tid / (16 * cpr), r = (tid / cpr) % 16, col = tid % cpr;
+    const int rr = (tid * ((65535 + cpr) / cpr)) >> 16;   // tid / cpr: exact while tid * cpr < 2^16
+    const int a = rr >> 4, r = rr & 15, col = tid - rr * cpr;
     int proj, n;
     tile_row(p, tile, r, proj, n);
     const bool valid = tid < 32 * cpr && tile < p.ntiles && n < p.N;
@@ -645,7 +670,8 @@ struct Fused {
     const int G = p.K / 64, cpr = G / 8;
     asm volatile("" ::"v"(sb.v));   // read on every path (see compute_core)
     if (tid < 32 * cpr) {
-      const int a = tid / (16 * cpr), r = (tid / cpr) % 16, col = tid % cpr;
+      const int rr = (tid * ((65535 + cpr) / cpr)) >> 16;   // tid / cpr (as in sb_issue)
+      const int a = rr >> 4, r = rr & 15, col = tid - rr * cpr;
       uint32_t* d = reinterpret_cast<uint32_t*>(slot + (a * 16 + r) * sb_pitch(G) + 16 * col);
 #pragma unroll
       for (int j = 0; j < 4; ++j) d[j] = sb.v[j];
@@ -768,39 +794,6 @@ struct Fused {
   }
 };
 
-// Sum over the workgroup's waves of C row r, column col, from the LDS partials: all reads
-// are issued before the first add (one LDS round trip), the adds run in wave order.
-template <int MT>
-__device__ __forceinline__ float merged(const float* red, int buf, int r, int col) {
-  const int lane = 16 * ((r & 15) >> 2) + col;
-  float v[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) v[w] = red[((buf * kWaves + w) * MT + (r >> 4)) * 256 + lane * 4 + (r & 3)];
-  float s = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += v[w];
-  return s;
-}
-
-// Output value before the epilogue: no LN, the sum of the row's terms; with LN the fold
-// rstd * (P - m G) + B with the row's m and rstd from row_moments.
-template <int MT, int NT>
-__device__ __forceinline__ float folded(const LinParams& p, const float* red, const float* mr, int buf, int t, int col) {
-  const int terms = p.terms;
-  float part[NT];
-#pragma unroll
-  for (int term = 0; term < NT; ++term)   // rows past the operand's terms read row 0, unused
-    part[term] = merged<MT>(red, buf, term < terms ? terms * t + term : 0, col);
-  float P = 0.0f;
-#pragma unroll
-  for (int term = 0; term < NT; ++term)
-    if (term < terms) P += part[term];
-  if (!p.ln) return P;
-  const float Gw = merged<MT>(red, buf, terms * p.T, col);
-  const float Bw = merged<MT>(red, buf, terms * p.T + 1, col);
-  return mr[2 * t + 1] * (P - mr[2 * t] * Gw) + Bw;
-}
-
 // Per-row LN moments from the shifted sums S1, S2 of row t: m = S1 / K (the mean of the
 // shifted row), var = S2 / K - m^2 (biased, clamped at 0), rstd = 1 / sqrt(var + eps).
 __device__ __forceinline__ void row_moments(const LinParams& p, const float* stat, float* mr, int t) {
@@ -810,32 +803,59 @@ __device__ __forceinline__ void row_moments(const LinParams& p, const float* sta
   mr[2 * t + 1] = 1.0f / sqrtf(var + p.eps);
 }
 
-// Epilogue and store of one tile ([p1] `_linear_kernel`: GELU, then residual, then constant).
-// Thread tid finishes output slot out_slot(tid, tile).
+// Partial of C row r, column col written by wave w for a tile (double buffer buf).
+template <int MT>
+__device__ __forceinline__ float partial_at(const float* red, int buf, int w, int r, int col) {
+  return red[((buf * kWaves + w) * MT + (r >> 4)) * 256 + (16 * ((r & 15) >> 2) + col) * 4 + (r & 3)];
+}
+
+// Merge, LN fold, epilogue and store of one tile, spread over all lanes of the workgroup:
+// each output takes 8 consecutive lanes, lane w reading wave w's partials (all reads are
+// issued before any arithmetic, at in-range rows), and the 8 are summed with a fixed DPP
+// tree.  A gate/up output pairs the 8 lanes of g with the next 8 lanes holding u.  The
+// storing lane is the group's first.  Epilogue order as [p1] `_linear_kernel`: GELU, then
+// residual, then constant; one rounding to the output type.
 template <int MT, int NT>
-__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* mr, int buf, int tile, int tid,
-                                         uint32_t res_bits, uint32_t add_bits) {
-  tid = out_slot(tid, tile);
-  if (!p.gateup) {
-    if (tid < p.T * 16) {
-      const int t = tid >> 4, col = tid & 15, n = tile * 16 + col;
-      if (n < p.N) {
-        float v = folded<MT, NT>(p, red, mr, buf, t, col);
-        if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
-        if (p.res) v += elem_to_float(res_bits, p.x_dtype);
-        if (p.add) v += elem_to_float(add_bits, p.x_dtype);
-        store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
-      }
+__device__ __forceinline__ void finalize(const LinParams& p, const float* red, const float* mr, const uint16_t* epi,
+                                         int buf, int tile, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, w = lane & 7;
+  const int terms = p.terms, T = p.T;
+  const int rounds = (T + 3) >> 2;   // 64 linear (32 gate/up) outputs per round
+  for (int rd = 0; rd < rounds; ++rd) {
+    int t, col, n, half;
+    if (p.gateup) {
+      const int o = rd * 32 + wv * 4 + (lane >> 4);
+      t = o >> 3; half = (lane >> 3) & 1; col = (o & 7) + 8 * half; n = tile * 8 + (o & 7);
+    } else {
+      const int o = rd * 64 + wv * 8 + (lane >> 3);
+      t = o >> 4; half = 0; col = o & 15; n = tile * 16 + col;
     }
-  } else {
-    if (tid < p.T * 8) {
-      const int t = tid >> 3, j = tid & 7, n = tile * 8 + j;
-      if (n < p.N) {
-        const float g = folded<MT, NT>(p, red, mr, buf, t, j);
-        const float u = folded<MT, NT>(p, red, mr, buf, t, j + 8);
-        store_out(p.y, p.y_dtype, (long)t * p.N + n, g / (1.0f + expf(-g)) * u);
-      }
+    const bool valid = t < T && n < p.N;
+    const int tc = min(t, T - 1);
+    float part[NT];
+#pragma unroll
+    for (int term = 0; term < NT; ++term) part[term] = partial_at<MT>(red, buf, w, term < terms ? terms * tc + term : 0, col);
+    const float gv = partial_at<MT>(red, buf, w, p.ln ? terms * T : 0, col);
+    const float bv = partial_at<MT>(red, buf, w, p.ln ? terms * T + 1 : 0, col);
+    const float m = mr[2 * tc], rstd = mr[2 * tc + 1];
+    const uint32_t rb = epi[tc * 16 + (col & 15)], ab = epi[T * 16 + (col & 15)];
+    float P = 0.0f;
+#pragma unroll
+    for (int term = 0; term < NT; ++term) P += term < terms ? part[term] : 0.0f;
+    P = sum8(P);
+    float v = P;
+    if (p.ln) v = rstd * (P - m * sum8(gv)) + sum8(bv);   // uniform
+    if (p.gateup) {
+      // u from the next 8 lanes (rotate by 8 within the 16-lane row); silu(g) * u with the
+      // hardware exp2 and reciprocal (a few ulp; far inside the tolerance)
+      const float u = dpp_f<0x128>(v);   // row_ror:8
+      v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
+    } else {
+      if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
+      if (p.res) v += elem_to_float(rb, p.x_dtype);
+      if (p.add) v += elem_to_float(ab, p.x_dtype);
     }
+    if (valid && w == 0 && half == 0) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
   }
 }
 
@@ -888,19 +908,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     for (int mt = 0; mt < MT; ++mt) {
       f4_t v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[mt][j] * st.unscale[mt][j];
+      for (int j = 0; j < 4; ++j)   // quantized partials carry the codes' 2^-24 (kCodeScale)
+        v[j] = (S::QUANT ? acc[mt][j] * 0x1p24f : acc[mt][j]) * st.unscale[mt][j];
       *reinterpret_cast<f4_t*>(rb + mt * 256 + lane * 4) = v;
     }
   };
-  // Merge the waves' partials of a tile and finish it.
-  auto finish = [&](int tile, int buf, const typename S::EpiRegs& e) __attribute__((always_inline)) {
-    // Every lane reads its residual and constant here, used or not: a loaded register left
-    // unread on some path makes the compiler drain all loads (the prefetch too) before the
-    // register is reused.
-    const uint32_t res_bits = e.res, add_bits = e.add;
-    asm volatile("" ::"v"(res_bits), "v"(add_bits));
+  // Merge the waves' partials of a tile and finish it (epilogue inputs from slot `epi`).
+  auto finish = [&](int tile, int buf, const uint16_t* epi) __attribute__((always_inline)) {
     lds_barrier();
-    finalize<MT, BF16OP ? 3 : 2>(p, red, mr, buf, tile, tid, res_bits, add_bits);
+    finalize<MT, BF16OP ? 3 : 2>(p, red, mr, epi, buf, tile, tid);
   };
 
   if (tid < kStatFloats) stat[tid] = 0.0f;
@@ -915,16 +931,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     unsigned char* ring = region + (staging_bytes(p.rows, p.K) > merge_bytes(MT) ? staging_bytes(p.rows, p.K)
                                                                                    : merge_bytes(MT));
     const int slot_bytes = S::sb_slot_bytes(p.K / 64);
+    uint16_t* epi = reinterpret_cast<uint16_t*>(ring + 2 * slot_bytes);   // two slots of kEpiSlot
     // Issue order: the first tile's scales, the staged rows, then the first tile's codes, so
     // that staging waits for its own rows only and the code stream runs under it.
     typename S::SbRegs sb0;
     if constexpr (S::QUANT) S::sb_issue(p, tile, tid, sb0);
+    typename S::EpRegs ep0;
+    S::ep_issue(p, tile, tid, ep0);
     typename S::StageRegs sr;
     S::stage_load(p, 0, p.K, tid, sr);
     typename S::TileRegs ra, rb;
     S::template load_tile<false, false>(p, tile, s_lo, nsw, c, li, ra);
     prepare(0, true, cs0, s_lo, nsw, sr, [&] {
       if constexpr (S::QUANT) S::sb_commit(p, tid, sb0, ring);
+      S::ep_commit(p, tid, ep0, epi);
     });
     // One half: the next tile's scales and codes and this tile's epilogue inputs are issued,
     // then `tile` is computed from `cur` (loaded one half earlier) and finished.  Epilogue
@@ -934,16 +954,18 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
                     int buf) __attribute__((always_inline)) {
       typename S::SbRegs sb;
       if constexpr (S::QUANT) S::sb_issue(p, next, tid, sb);   // past the last tile: zeros
-      typename S::EpiRegs e;
-      S::load_epi(p, tile, e);
+      typename S::EpRegs ep;
+      S::ep_issue(p, next, tid, ep);
       S::template load_tile<false, false>(p, next, s_lo, nsw, c, li, nxt);
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_ring(p, nsw, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
       write_partials(acc, buf);
-      if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);   // slot read last half
-      finish(tile, buf, e);
+      // the next tile's slots were last read during the previous half
+      if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);
+      S::ep_commit(p, tid, ep, epi + (buf ^ 1) * kEpiSlot);
+      finish(tile, buf, epi + buf * kEpiSlot);
     };
     // Tiles come in pairs so that the loop is entered again only after the second half: an
     // exit test after the first half that shares a block with the loop test would leave the
@@ -955,14 +977,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       half(rb, ra, tile + G, tile + 2 * G, 1);
     }
     if (n & 1) {
-      typename S::EpiRegs e;
-      S::load_epi(p, tile, e);
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_ring(p, nsw, s_lo, c, li, ra.dw, ring, acc);
       write_partials(acc, 0);
-      finish(tile, 0, e);
+      finish(tile, 0, epi);
     }
   } else {
     // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
@@ -996,10 +1016,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
         st.compute_tile(nsw, c, r, acc);
       }
       first = false;
-      typename S::EpiRegs e;
-      S::load_epi(p, tile, e);
+      // epilogue inputs: slot buf was last read two tiles ago, before the previous barrier
+      uint16_t* epi = reinterpret_cast<uint16_t*>(region + (staging_bytes(p.rows, min(p.chunk_steps * STEPK, p.K)) >
+                                                                   merge_bytes(MT) ? staging_bytes(p.rows, min(p.chunk_steps * STEPK, p.K))
+                                                                                   : merge_bytes(MT)) +
+                                                   2 * S::sb_slot_bytes(min(p.chunk_steps * STEPK, p.K) / 64));
+      typename S::EpRegs ep;
+      S::ep_issue(p, tile, tid, ep);
       write_partials(acc, buf);
-      finish(tile, buf, e);
+      S::ep_commit(p, tid, ep, epi + buf * kEpiSlot);
+      finish(tile, buf, epi + buf * kEpiSlot);
     }
   }
 }
@@ -1007,7 +1033,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
 // Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
 __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
   return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt)) +
-         2L * 32 * (2 * (kc / 64) + 4);   // two scale/bias ring slots
+         2L * 32 * (2 * (kc / 64) + 4) +   // two scale/bias ring slots
+         2L * kEpiSlot * 2;                // two epilogue-input slots
 }
 
 template <int BITS, bool BF16OP, int MT, bool CHUNKED>
