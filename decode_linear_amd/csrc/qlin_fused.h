@@ -177,7 +177,9 @@ constexpr int kRowPad = 8;
 constexpr int kStatFloats = 64;
 constexpr int kExpInts = 128;
 constexpr int kRowMax = 64;
-constexpr int kHeaderBytes = (2 * kStatFloats + kExpInts + 2 * kRowMax) * 4;   // sums, moments, exps, max, x[t, 0]
+// Streaming variant: per-wave LN sums S1, S2 of up to 32 rows (each wave sums its window).
+constexpr int kWaveStatFloats = kWaves * 64;
+constexpr int kHeaderBytes = (2 * kStatFloats + kExpInts + 2 * kRowMax + kWaveStatFloats) * 4;
 // Largest dynamic LDS a launch may ask for (gfx950 has 160 KiB per CU).
 // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -249,13 +251,16 @@ __device__ __forceinline__ void unpack8(const u4_t raw, int dtype, float v[8]) {
   for (int j = 0; j < 8; ++j) v[j] = elem_to_float((raw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu, dtype);
 }
 
-template <int BITS, bool BF16OP, int MT>
+// NS > 0: the streaming variant, where every wave runs exactly NS steps (a window of the row
+// that may overlap the previous wave's; the overlapped steps are masked).  NS == 0: the
+// chunked variant, up to MAXS steps per wave and chunk.
+template <int BITS, bool BF16OP, int MT, int NS = 0>
 struct Fused {
   static constexpr int NM = Fmt<BITS>::kMfma;
   static constexpr int NG = Fmt<BITS>::kGroups > 0 ? Fmt<BITS>::kGroups : 1;
   static constexpr bool QUANT = BITS != 16;
   static constexpr int STEPK = Fmt<BITS>::kStepK;
-  static constexpr int MAXS = max_steps_for(NM, MT);
+  static constexpr int MAXS = NS > 0 ? NS : max_steps_for(NM, MT);
 
   u4_t afrag[MAXS][NM][MT];   // operand fragments of this wave's K slice
   u4_t gfrag[MT];             // quantized: group sums of this wave's slice as an A operand
@@ -486,9 +491,255 @@ struct Fused {
     }
   }
 
+  // ---- per-wave staging (streaming variant) ------------------------------------------
+  // Each wave stages only its own window of K, k0 = s_lo * STEPK .. k0 + WK: the source rows
+  // (x rows, then gamma and beta with LN) go through the same transform as above into a
+  // block of LDS that only this wave reads.  The power-of-two row scale is per wave (each
+  // wave unscales its own partials before the merge), so no value crosses waves before the
+  // merge: no atomics and no barrier.  Piece pc = lane + 64 u is source row pc / W8,
+  // elements 8 (pc % W8) .. + 7 of the window; W8 <= 64, so the lanes of one row form an
+  // aligned group of W8 lanes within one u, and the row reductions are lane butterflies.
+  static constexpr int WK = (NS > 0 ? NS : 1) * STEPK;   // window width (elements)
+  static constexpr int W8 = WK / 8;                        // pieces per source row
+  static constexpr int WG = WK >= 64 ? WK / 64 : 1;        // quantization groups per window
+  static constexpr int kWavePieces = 12;                   // pieces per lane, at most
+  static_assert(W8 <= 64, "a source row's pieces fit one u");
+  __host__ __device__ static constexpr int wave_pitch() { return WK + kRowPad; }
+  // Bytes of one wave's block: operand rows, group sums, row exponents.
+  __host__ __device__ static constexpr long wave_block_bytes(int rows) {
+    return ((long)rows * wave_pitch() * 2 + (long)rows * WG * 4 + (long)rows * 4 + 15) / 16 * 16;
+  }
+  struct WaveRegs {
+    u4_t raw[kWavePieces];    // the piece
+    u4_t graw[kWavePieces];   // LN: gamma at the piece's columns
+    uint32_t x0[kWavePieces]; // LN: x[row, 0], the shift of the row's sums
+  };
+  __device__ __forceinline__ static void wave_stage_load(const LinParams& p, int k0, int lane, WaveRegs& wr) {
+    const int T = p.T, total = (T + (p.ln ? 2 : 0)) * W8;
+    const uint16_t* x16 = reinterpret_cast<const uint16_t*>(p.x);
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.gamma);
+    const uint16_t* b16 = reinterpret_cast<const uint16_t*>(p.beta);
+#pragma unroll
+    for (int u = 0; u < kWavePieces; ++u) {
+      if (64 * u < total) {   // uniform
+        // lanes past the last piece load the last piece again (never written back)
+        const int pc = min(lane + 64 * u, total - 1);
+        const int row = pc / W8, kp = pc % W8;
+        const bool act = row < T;
+        const gptr<const uint16_t> src = pick(act ? x16 : g16, b16, (!act && row != T) ? 1 : 0) +
+                                         (act ? (long)row * p.K : 0) + k0 + 8 * kp;
+        wr.raw[u] = *reinterpret_cast<gptr<const u4_t>>(src);
+        if (p.ln) {   // uniform; gamma and x[row, 0] of the piece's (clamped) activation row
+          wr.graw[u] = *reinterpret_cast<gptr<const u4_t>>(pick(g16, g16, 0) + k0 + 8 * kp);
+          wr.x0[u] = *(pick(x16, x16, 0) + (long)min(row, T - 1) * p.K);
+        }
+      }
+    }
+  }
+  // Reductions over aligned groups of N lanes (N a power of two <= 64); every lane of a
+  // group ends with the group's value.  Within 16-lane rows: DPP moves (xor 1, xor 2, then
+  // the mirrored half row and row, which pair every lane with one holding the other half's
+  // total); across rows: the gfx950 row swaps, v_permlane16_swap (rows 0<->1, 2<->3) and
+  // v_permlane32_swap (lanes l <-> l + 32), which with both operands equal leave one lane of
+  // each pair in each result.
+  template <int CTRL> __device__ __forceinline__ static uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  }
+  template <int N> __device__ __forceinline__ static uint32_t group_max_u(uint32_t v) {
+    if constexpr (N >= 2) v = max(v, dpp_u<0xB1>(v));
+    if constexpr (N >= 4) v = max(v, dpp_u<0x4E>(v));
+    if constexpr (N >= 8) v = max(v, dpp_u<0x141>(v));
+    if constexpr (N >= 16) v = max(v, dpp_u<0x140>(v));
+    if constexpr (N >= 32) {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      v = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    if constexpr (N >= 64) {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      v = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    return v;
+  }
+  template <int N> __device__ __forceinline__ static float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_f<0xB1>(v);
+    if constexpr (N >= 4) v += dpp_f<0x4E>(v);
+    if constexpr (N >= 8) v += dpp_f<0x141>(v);
+    if constexpr (N >= 16) v += dpp_f<0x140>(v);
+    if constexpr (N >= 32) {   // both lanes of a pair add the same two values: equal sums
+      const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                      false, false);
+      v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+    if constexpr (N >= 64) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                      false, false);
+      v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+    return v;
+  }
+  // s_from: the window's steps before s_from are another wave's (they are staged, but do not
+  // count towards this wave's LN sums).
+  __device__ __forceinline__ static void wave_stage(const LinParams& p, float* wstat, unsigned char* blk, int lane,
+                                                    int s_from, const WaveRegs& wr) {
+    asm volatile("" : "+v"(lane));
+    if (p.x_dtype == 1) {
+      if (p.terms == 1) wave_stage_body<1, true>(p, wstat, blk, lane, s_from, wr);
+      else wave_stage_body<1, false>(p, wstat, blk, lane, s_from, wr);
+    } else {
+      if (p.terms == 1) wave_stage_body<2, true>(p, wstat, blk, lane, s_from, wr);
+      else wave_stage_body<2, false>(p, wstat, blk, lane, s_from, wr);
+    }
+  }
+  template <int XDT, bool ONE>
+  __device__ __forceinline__ static void wave_stage_body(const LinParams& p, float* wstat, unsigned char* blk,
+                                                         int lane, int s_from, const WaveRegs& wr) {
+    constexpr int NT = ONE ? 1 : (BF16OP ? 3 : 2);   // terms of an activation row
+    const int T = p.T, R = p.rows;
+    const int total = (T + (p.ln ? 2 : 0)) * W8;
+    uint16_t* op = reinterpret_cast<uint16_t*>(blk);
+    float* gsum = reinterpret_cast<float*>(blk + (long)R * wave_pitch() * 2);
+    int* ex = reinterpret_cast<int*>(blk + (long)R * wave_pitch() * 2 + (long)R * WG * 4);
+#pragma unroll
+    for (int u = 0; u < kWavePieces; ++u) {
+      if (64 * u < total) {   // uniform: some lane of the wave holds a piece
+        const int pc = lane + 64 * u;
+        const bool live = pc < total;
+        const int row = min(pc, total - 1) / W8, kp = pc % W8;
+        const bool act = row < T;
+        float v[8];
+        unpack_t<XDT>(wr.raw[u], v);
+        // LN: activation rows become (x - x[row, 0]) * gamma; gamma and beta rows stay
+        if (p.ln) {   // uniform
+          const float x0 = act ? (XDT == 1 ? half_bits_to_float(wr.x0[u] & 0xFFFFu)
+                                           : __builtin_bit_cast(float, wr.x0[u] << 16)) : 0.0f;
+          float g[8];
+          unpack_t<XDT>(wr.graw[u], g);
+          float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float d = v[jj] - x0;
+            s1 += d;
+            s2 += d * d;
+            v[jj] = act ? d * g[jj] : v[jj];
+          }
+          if (8 * kp < s_from * STEPK) s1 = s2 = 0.0f;   // another wave's step
+          s1 = group_sum<W8>(s1);
+          s2 = group_sum<W8>(s2);
+          if (live && act && kp == 0) {
+            wstat[2 * row] = s1;
+            wstat[2 * row + 1] = s2;
+          }
+        }
+        const bool need = act ? p.scale_act : p.scale_gb;
+        int e = 0;
+        if (p.ln || p.scale_act) {   // uniform; |v| compared as bit patterns (same order)
+          uint32_t amax = 0u;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) amax = max(amax, __builtin_bit_cast(uint32_t, v[jj]) & 0x7FFFFFFFu);
+          amax = group_max_u<W8>(amax);
+          e = need ? row_exponent(__builtin_bit_cast(float, amax)) : 0;
+        }
+        const float scl = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+        const int r0 = act ? NT * row : NT * T + (row - T);
+        const int nterm = act ? NT : 1;
+        if (live && kp == 0) {
+#pragma unroll
+          for (int term = 0; term < NT; ++term)
+            if (term < nterm) ex[r0 + term] = e;
+        }
+        // Terms: hi = the scaled value rounded to the operand type, then the rounded
+        // remainders; each remainder is exact before its rounding (one fma).
+        uint32_t el[NT][8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float x = v[slot_k<BITS>(jj)];
+          const float sj = slot_hi_nibble<BITS>(jj) ? scl * 0.0625f : scl;
+          const uint32_t hi = to_op_bits<BF16OP>(x * sj);
+          el[0][jj] = hi;
+          if constexpr (NT >= 2) {
+            const float r1 = fmaf(x, sj, -op_bits_to_float<BF16OP>(hi));
+            const uint32_t mid = to_op_bits<BF16OP>(r1);
+            el[1][jj] = mid;
+            if constexpr (NT == 3) el[2][jj] = to_op_bits<BF16OP>(r1 - op_bits_to_float<BF16OP>(mid));
+          }
+        }
+#pragma unroll
+        for (int term = 0; term < NT; ++term) {
+          if (term < nterm && live) {
+            u4_t w;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = el[term][2 * r] | (el[term][2 * r + 1] << 16);
+            *reinterpret_cast<u4_t*>(op + (long)(r0 + term) * wave_pitch() + 8 * kp) = w;
+          }
+        }
+        if constexpr (QUANT) {
+          // Group sum of the row's operand values: scl * sum(v) (a value's terms add up to
+          // it within 2^-22 relative; a high-nibble slot's 1/16 operand counts 16 times).
+          // It rides on the first term's row; the other terms' rows carry 0.
+          float t = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) t += v[jj];
+          t = sum8(t) * scl;
+          if (live && (kp & 7) == 0) {
+#pragma unroll
+            for (int term = 0; term < NT; ++term)
+              if (term < nterm) gsum[(r0 + term) * WG + kp / 8] = term == 0 ? t : 0.0f;
+          }
+        }
+      } else {
+        // pieces past the window were loaded on no path; reading them keeps the compiler's
+        // view of every path alike (see compute_core)
+        asm volatile("" ::"v"(wr.raw[u]), "v"(wr.graw[u]), "v"(wr.x0[u]));
+      }
+    }
+  }
+  // This wave's fragments from its own block (window-relative columns).
+  __device__ __forceinline__ void load_frags_wave(const LinParams& p, const unsigned char* blk, int s_from, int c,
+                                                  int li) {
+    const int R = p.rows;
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(blk);
+    const float* gsum = reinterpret_cast<const float*>(blk + (long)R * wave_pitch() * 2);
+    const int* ex = reinterpret_cast<const int*>(blk + (long)R * wave_pitch() * 2 + (long)R * WG * 4);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+      for (int q = 0; q < NM; ++q)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          // rows past R read an in-range row (an A row only feeds its own C row)
+          const int r = min(16 * mt + li, R - 1);
+          const u4_t v = *reinterpret_cast<const u4_t*>(op + (long)r * wave_pitch() + s * STEPK + frag_base<BITS>(q, c));
+          // steps before s_from belong to the previous wave: zero operands, no contribution
+          afrag[s][q][mt] = s < s_from ? (u4_t){0u, 0u, 0u, 0u} : v;
+        }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = min(16 * mt + 4 * c + v, R - 1);
+        unscale[mt][v] = __builtin_bit_cast(float, (uint32_t)(127 - ex[r]) << 23);
+      }
+      if constexpr (QUANT) {
+        const int r = min(16 * mt + li, R - 1);
+        uint32_t el[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // groups past the window meet a zero bias, so any finite in-range sum does
+          const int gi = min(8 * (c & 1) + j, WG - 1);
+          const float v = gsum[r * WG + gi] * (1.0f / (float)(1 << kGsumShift));
+          const uint32_t hi = to_op_bits<false>(v);
+          const uint32_t lo = to_op_bits<false>(v - op_bits_to_float<false>(hi));
+          el[j] = (c >> 1) ? lo : hi;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) gfrag[mt][w] = el[2 * w] | (el[2 * w + 1] << 16);
+      }
+    }
+  }
+
   // ---- per-wave fragment load from the staged rows ----------------------------------
   __device__ __forceinline__ void load_frags(const LinParams& p, const int* ex, const uint16_t* op, const float* gsum,
-                                             int kc0, int kc, int cs0, int s_lo, int nsw, int c, int li) {
+                                             int kc0, int kc, int cs0, int s_lo, int s_from, int c, int li) {
     const int R = p.rows, pitch = op_pitch(kc), gpr = kc / 64;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
@@ -503,6 +754,16 @@ struct Fused {
           const int kk = min((s_lo + s) * STEPK + frag_base<BITS>(q, c) - kc0, kc - 8);
           afrag[s][q][mt] = *reinterpret_cast<const u4_t*>(op + (long)r * pitch + max(kk, 0));
         }
+    if constexpr (NS > 0) {
+      // steps before s_from belong to the previous wave: zero operands, no contribution
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+        for (int q = 0; q < NM; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (s < s_from) afrag[s][q][mt] = (u4_t){0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -598,7 +859,7 @@ struct Fused {
     for (int s = 0; s < MAXS; ++s) {
       // steps >= nsw (uniform) read the zero buffer: no branch, so the whole batch issues
       // back to back and the wait counts stay exact
-      const gptr<const char> a = s < nsw ? cb + s * 64 : zero + 16 * c;
+      const gptr<const char> a = (NS > 0 || s < nsw) ? cb + s * 64 : zero + 16 * c;
       if constexpr (CHECKED) {   // a row may end half-way through its last step
         const bool in = (long)(s_lo + s) * 64 + 16 * c < row_bytes;
         r.dw[s] = *reinterpret_cast<gptr<const u4_t>>(in ? a : zero + 16 * c);
@@ -685,7 +946,7 @@ struct Fused {
                                                f4_t acc[MT]) {
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
-      if (s < nsw) {
+      if (NS > 0 || s < nsw) {   // streaming: every step runs (masked steps have zero operands)
         u4_t d = dw[s];
         if constexpr (BITS == 4) {
           const auto r01 = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
@@ -757,8 +1018,9 @@ struct Fused {
   }
 
   // A tile whose scales and biases sit in ring slot `slot` (streaming variant).
-  __device__ __forceinline__ void compute_ring(const LinParams& p, int nsw, int s_lo, int c, int li, const u4_t dw[MAXS],
+  __device__ __forceinline__ void compute_ring(const LinParams& p, int s_from, int s_lo, int c, int li, const u4_t dw[MAXS],
                                                const unsigned char* slot, f4_t acc[MT]) {
+    static_assert(NS > 0, "the ring feeds the streaming variant");
     uint32_t sc[MAXS];
     u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
     if constexpr (QUANT) {
@@ -767,15 +1029,18 @@ struct Fused {
       const unsigned char* brow = slot + (16 + li) * pitch;
 #pragma unroll
       for (int s = 0; s < MAXS; ++s) {
-        if constexpr (NG == 2) sc[s] = s < nsw ? *reinterpret_cast<const uint32_t*>(srow + 4 * (s_lo + s)) : 0u;
-        else sc[s] = s < nsw ? *reinterpret_cast<const uint16_t*>(srow + 2 * (s_lo + s)) : 0u;
+        // the window lies inside the row; steps before s_from get a zero scale
+        uint32_t v;
+        if constexpr (NG == 2) v = *reinterpret_cast<const uint32_t*>(srow + 4 * (s_lo + s));
+        else v = *reinterpret_cast<const uint16_t*>(srow + 2 * (s_lo + s));
+        sc[s] = s >= s_from ? v : 0u;
       }
       if constexpr (NG == 2) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {   // dword w: both groups of step 4*(c&1) + w
           const int j = 4 * (c & 1) + w;
           const uint32_t v = *reinterpret_cast<const uint32_t*>(brow + 4 * min(s_lo + j, G / 2 - 1));
-          bfr[w] = j < nsw ? v : 0u;
+          bfr[w] = (j >= s_from && j < NS) ? v : 0u;
         }
       } else {
 #pragma unroll
@@ -783,14 +1048,14 @@ struct Fused {
           const int j0 = 8 * (c & 1) + 2 * w, j1 = j0 + 1;
           const uint32_t v0 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j0, G - 1));
           const uint32_t v1 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j1, G - 1));
-          bfr[w] = (j0 < nsw ? v0 : 0u) | ((j1 < nsw ? v1 : 0u) << 16);
+          bfr[w] = ((j0 >= s_from && j0 < NS) ? v0 : 0u) | (((j1 >= s_from && j1 < NS) ? v1 : 0u) << 16);
         }
       }
     } else {
 #pragma unroll
       for (int s = 0; s < MAXS; ++s) sc[s] = 0u;
     }
-    compute_core(nsw, dw, sc, bfr, acc);
+    compute_core(NS, dw, sc, bfr, acc);
   }
 };
 
@@ -859,9 +1124,10 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
   }
 }
 
-template <int BITS, bool BF16OP, int MT, bool CHUNKED>
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
-  using S = Fused<BITS, BF16OP, MT>;
+  static_assert(CHUNKED == (NS == 0), "the streaming variant has a fixed step count");
+  using S = Fused<BITS, BF16OP, MT, NS>;
   constexpr int STEPK = S::STEPK;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   float* stat = reinterpret_cast<float*>(lds_raw);
@@ -869,24 +1135,37 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   unsigned* rowmax = reinterpret_cast<unsigned*>(lds_raw + (kStatFloats + kExpInts) * 4);
   float* x0s = reinterpret_cast<float*>(lds_raw + (kStatFloats + kExpInts + kRowMax) * 4);
   float* mr = reinterpret_cast<float*>(lds_raw + (kStatFloats + kExpInts + 2 * kRowMax) * 4);
+  float* wstat = reinterpret_cast<float*>(lds_raw + (2 * kStatFloats + kExpInts + 2 * kRowMax) * 4);
   unsigned char* region = lds_raw + kHeaderBytes;
   float* red = reinterpret_cast<float*>(region);
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane >> 4, li = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  auto slice = [&](int ch, int& cs0, int& s_lo, int& nsw) __attribute__((always_inline)) {
-    cs0 = ch * p.chunk_steps;
-    const int sc = min(p.chunk_steps, p.steps - cs0);
-    s_lo = cs0 + (wv * sc) / kWaves;
-    nsw = cs0 + ((wv + 1) * sc) / kWaves - s_lo;
+  // This wave's steps of chunk ch: [s_lo, s_lo + nsw), of which those before s_from are
+  // another wave's.  Chunked: an even split of the chunk (s_from = 0).  Streaming: a window
+  // of NS steps that starts at wv * NS, moved back to end at the row's last step when it
+  // would run past it (NS <= steps), so that every load stays inside the row.
+  auto slice = [&](int ch, int& cs0, int& s_lo, int& nsw, int& s_from) __attribute__((always_inline)) {
+    if constexpr (NS > 0) {
+      cs0 = 0;
+      s_lo = min(wv * NS, p.steps - NS);
+      s_from = wv * NS - s_lo;
+      nsw = NS;
+    } else {
+      cs0 = ch * p.chunk_steps;
+      const int sc = min(p.chunk_steps, p.steps - cs0);
+      s_lo = cs0 + (wv * sc) / kWaves;
+      nsw = cs0 + ((wv + 1) * sc) / kWaves - s_lo;
+      s_from = 0;
+    }
   };
   // Stage chunk ch into LDS and load this wave's fragments from it.
   S st;
   // Stage chunk ch (its pieces already in sr), run after_stage, load this wave's fragments.
-  auto prepare = [&](int ch, bool stats, int& cs0, int& s_lo, int& nsw, const typename S::StageRegs& sr,
+  auto prepare = [&](int ch, bool stats, int& cs0, int& s_lo, int& nsw, int& s_from, const typename S::StageRegs& sr,
                      auto&& after_stage) __attribute__((always_inline)) {
-    slice(ch, cs0, s_lo, nsw);
+    slice(ch, cs0, s_lo, nsw, s_from);
     const int kc0 = cs0 * STEPK;
     const int kc = min(p.chunk_steps * STEPK, p.K - kc0);
     uint16_t* op = reinterpret_cast<uint16_t*>(region);
@@ -898,7 +1177,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     after_stage();
     lds_barrier();
     if (stats && p.ln && tid < p.T) row_moments(p, stat, mr, tid);   // read after a later barrier
-    st.load_frags(p, ex, op, gsum, kc0, kc, cs0, s_lo, nsw, c, li);
+    st.load_frags(p, ex, op, gsum, kc0, kc, cs0, s_lo, s_from, c, li);
     lds_barrier();
   };
   // This wave's partials of a tile into LDS (double-buffered by tile parity).
@@ -920,32 +1199,49 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   };
 
   if (tid < kStatFloats) stat[tid] = 0.0f;
-  int cs0, s_lo, nsw;
+  int cs0, s_lo, nsw, s_from;
   if constexpr (!CHUNKED) {
     // All of K fits: build the fragments once, then stream tiles with the next tile's codes,
     // scales and biases always in flight.  Two code register sets alternate (no copy at the
     // end of an iteration, which would make the compiler wait for the prefetch); scales and
     // biases alternate between two ring slots.
-    slice(0, cs0, s_lo, nsw);
+    slice(0, cs0, s_lo, nsw, s_from);
     int tile = blockIdx.x;
-    unsigned char* ring = region + (staging_bytes(p.rows, p.K) > merge_bytes(MT) ? staging_bytes(p.rows, p.K)
-                                                                                   : merge_bytes(MT));
+    const long stage_bytes = kWaves * S::wave_block_bytes(p.rows);
+    unsigned char* ring = region + (stage_bytes > merge_bytes(MT) ? stage_bytes : merge_bytes(MT));
     const int slot_bytes = S::sb_slot_bytes(p.K / 64);
     uint16_t* epi = reinterpret_cast<uint16_t*>(ring + 2 * slot_bytes);   // two slots of kEpiSlot
-    // Issue order: the first tile's scales, the staged rows, then the first tile's codes, so
-    // that staging waits for its own rows only and the code stream runs under it.
+    unsigned char* blk = region + wv * S::wave_block_bytes(p.rows);
+    // Issue order: the first tile's scales, this wave's window of the activation rows, then
+    // the first tile's codes, so that staging waits for its own rows only and the code
+    // stream runs under it.
     typename S::SbRegs sb0;
     if constexpr (S::QUANT) S::sb_issue(p, tile, tid, sb0);
     typename S::EpRegs ep0;
     S::ep_issue(p, tile, tid, ep0);
-    typename S::StageRegs sr;
-    S::stage_load(p, 0, p.K, tid, sr);
+    typename S::WaveRegs wr;
+    S::wave_stage_load(p, s_lo * STEPK, lane, wr);
     typename S::TileRegs ra, rb;
     S::template load_tile<false, false>(p, tile, s_lo, nsw, c, li, ra);
-    prepare(0, true, cs0, s_lo, nsw, sr, [&] {
-      if constexpr (S::QUANT) S::sb_commit(p, tid, sb0, ring);
-      S::ep_commit(p, tid, ep0, epi);
-    });
+    S::wave_stage(p, wstat + wv * 64, blk, lane, s_from, wr);
+    if constexpr (S::QUANT) S::sb_commit(p, tid, sb0, ring);
+    S::ep_commit(p, tid, ep0, epi);
+    // the block is this wave's own: its writes only need to have completed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    st.load_frags_wave(p, blk, s_from, c, li);
+    // every wave is done with its block before the merge partials reuse the region; the
+    // ring, epilogue slot and LN sums are visible to all
+    lds_barrier();
+    if (p.ln && tid < p.T) {   // LN moments from the waves' sums (read after a later barrier)
+      float s1 = 0.0f, s2 = 0.0f;
+      for (int w = 0; w < kWaves; ++w) { s1 += wstat[w * 64 + 2 * tid]; s2 += wstat[w * 64 + 2 * tid + 1]; }
+      const float m = s1 / (float)p.K;
+      const float var = fmaxf(s2 / (float)p.K - m * m, 0.0f);
+      mr[2 * tid] = m;
+      mr[2 * tid + 1] = 1.0f / sqrtf(var + p.eps);
+    }
     // One half: the next tile's scales and codes and this tile's epilogue inputs are issued,
     // then `tile` is computed from `cur` (loaded one half earlier) and finished.  Epilogue
     // inputs are loaded and read within one half: a load in flight across the loop edge
@@ -960,7 +1256,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      st.compute_ring(p, nsw, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
+      st.compute_ring(p, s_from, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
       write_partials(acc, buf);
       // the next tile's slots were last read during the previous half
       if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);
@@ -980,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      st.compute_ring(p, nsw, s_lo, c, li, ra.dw, ring, acc);
+      st.compute_ring(p, s_from, s_lo, c, li, ra.dw, ring, acc);
       write_partials(acc, 0);
       finish(tile, 0, epi);
     }
@@ -1003,9 +1299,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
           for (int j = 0; j < 4; ++j) prev[mt][j] = st.unscale[mt][j];
         if (!first || ch > 0) lds_barrier();   // earlier readers of the LDS region are done
         typename S::StageRegs sr;
-        slice(ch, cs0, s_lo, nsw);
+        slice(ch, cs0, s_lo, nsw, s_from);
         S::stage_load(p, cs0 * STEPK, min(p.chunk_steps * STEPK, p.K - cs0 * STEPK), tid, sr);
-        prepare(ch, first, cs0, s_lo, nsw, sr, [] {});
+        prepare(ch, first, cs0, s_lo, nsw, s_from, sr, [] {});
         S::template load_tile<true>(p, tile, s_lo, nsw, c, li, r);
         if (ch > 0) {
 #pragma unroll
@@ -1030,6 +1326,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   }
 }
 
+// Dynamic LDS of a streaming launch: header + max(per-wave staging blocks, merge) + the
+// scale/bias ring + the epilogue slots (the same layout the kernel carves).
+template <int BITS, bool BF16OP, int MT, int NS>
+__host__ __device__ constexpr long stream_lds_bytes(int rows, int K) {
+  using S = Fused<BITS, BF16OP, MT, NS>;
+  const long st = kWaves * S::wave_block_bytes(rows), mg = merge_bytes(MT);
+  return kHeaderBytes + (st > mg ? st : mg) + 2L * S::sb_slot_bytes(K / 64) + 2L * kEpiSlot * 2;
+}
+
 // Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
 __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
   return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt)) +
@@ -1037,29 +1342,50 @@ __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
          2L * kEpiSlot * 2;                // two epilogue-input slots
 }
 
-template <int BITS, bool BF16OP, int MT, bool CHUNKED>
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS>
 hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // Above 64 KiB of dynamic LDS the kernel must opt in once (a host-side attribute).
   static bool opted_in = false;
   if (!opted_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED, NS>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
     opted_in = true;
   }
-  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED>), dim3(grid), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED, NS>), dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
+}
+
+// The streaming variant with NS steps per wave, if its staging fits (pieces per lane and
+// LDS); hipErrorNotSupported otherwise.
+template <int BITS, bool BF16OP, int MT, int NS>
+hipError_t try_streaming(const LinParams& p, int grid, hipStream_t s) {
+  using S = Fused<BITS, BF16OP, MT, NS>;
+  const long pieces = (long)(p.T + (p.ln ? 2 : 0)) * S::W8;
+  const long lds = stream_lds_bytes<BITS, BF16OP, MT, NS>(p.rows, p.K);
+  if (NS > p.steps || pieces > 64L * S::kWavePieces || lds > kLdsMax) return hipErrorNotSupported;
+  return launch_variant<BITS, BF16OP, MT, false, NS>(p, grid, (size_t)lds, s);
 }
 
 template <int BITS, bool BF16OP, int MT>
 hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
-  // The streaming variant needs all of K staged at once and rows of whole 64-byte steps.
-  // Quantized weights also need rows of whole 16-byte scale chunks, at most 128 groups.
+  // The streaming variant: every wave a window of NS steps (NS a power of two, at most the
+  // fragment budget), the smallest that covers ceil(steps / waves).  It needs rows of whole
+  // 64-byte steps and, quantized, rows of whole 16-byte scale chunks, at most 128 groups.
+  constexpr int M = max_steps_for(Fmt<BITS>::kMfma, MT);
   const bool whole_steps = ((long)p.K * BITS / 8) % 64 == 0;
   const int G = p.K / 64;
   const bool ring_ok = BITS == 16 || (G % 8 == 0 && G <= 128);
-  return (p.chunk_steps >= p.steps && whole_steps && ring_ok) ? launch_variant<BITS, BF16OP, MT, false>(p, grid, lds, s)
-                                                   : launch_variant<BITS, BF16OP, MT, true>(p, grid, lds, s);
+  const int need = (p.steps + kWaves - 1) / kWaves;
+  if (whole_steps && ring_ok) {
+    hipError_t e = hipErrorNotSupported;
+    if (need <= 1) e = try_streaming<BITS, BF16OP, MT, 1>(p, grid, s);
+    else if (need <= 2) { if constexpr (M >= 2) e = try_streaming<BITS, BF16OP, MT, 2>(p, grid, s); }
+    else if (need <= 4) { if constexpr (M >= 4) e = try_streaming<BITS, BF16OP, MT, 4>(p, grid, s); }
+    else if (need <= 8) { if constexpr (M >= 8) e = try_streaming<BITS, BF16OP, MT, 8>(p, grid, s); }
+    if (e != hipErrorNotSupported) return e;
+  }
+  return launch_variant<BITS, BF16OP, MT, true, 0>(p, grid, lds, s);
 }
 
 }  // namespace qlin
