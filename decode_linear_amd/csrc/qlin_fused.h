@@ -1124,6 +1124,67 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
   }
 }
 
+// Merge, LN fold, epilogue and store of one tile, by the waves that own its 16-row blocks:
+// wave w takes block b = (w - rot) mod 8 (when b < MT), rot counting the workgroup's tiles,
+// so that the work rotates over the waves from tile to tile.  Each lane sums the eight waves' partials of its own C position
+// (16-byte LDS reads at the position the partials were written from: no bank conflicts),
+// in wave order, then finishes the outputs of its rows in registers: rows NT t .. NT t +
+// NT - 1 of an activation row t lie in one lane (NT = 1 or 2).  With LN, G_n and B_n (the
+// gamma and beta rows) are merged from the partials by every lane that needs them.  A
+// gate/up tile pairs column n (gate) with column n + 8 (up) of the same 16-lane row.
+// Epilogue order as [p1] `_linear_kernel`: GELU, then residual, then constant; one rounding
+// to the output type.
+template <int MT, int NT>
+__device__ __forceinline__ void finalize_rows(const LinParams& p, const float* red, const float* mr, const uint16_t* epi,
+                                              int buf, int tile, int rot, int wv, int lane) {
+  const int c = lane >> 4, li = lane & 15;
+  const int T = p.T;
+  for (int b = (wv - rot) & 7; b < MT; b += kWaves) {   // uniform per wave
+    f4_t m = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const f4_t v = *reinterpret_cast<const f4_t*>(red + ((buf * kWaves + w) * MT + b) * 256 + lane * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] += v[j];
+    }
+    float G = 0.0f, B = 0.0f;
+    if (p.ln) {   // uniform: G_n, B_n from rows NT T and NT T + 1, column li
+      const int rg = NT * T, rb = rg + 1;
+      const float* pg = red + (buf * kWaves * MT + (rg >> 4)) * 256 + ((((rg & 15) >> 2) << 4) | li) * 4 + (rg & 3);
+      const float* pb = red + (buf * kWaves * MT + (rb >> 4)) * 256 + ((((rb & 15) >> 2) << 4) | li) * 4 + (rb & 3);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        G += pg[w * MT * 256];
+        B += pb[w * MT * 256];
+      }
+    }
+    constexpr int NO = 4 / NT;   // activation rows per lane
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      const int t = (16 * b + 4 * c) / NT + o;
+      const int tc = min(t, T - 1);
+      float v = 0.0f;
+#pragma unroll
+      for (int term = 0; term < NT; ++term) v += m[o * NT + term];
+      if (p.ln) v = mr[2 * tc + 1] * (v - mr[2 * tc] * G) + B;
+      if (p.gateup) {
+        // u from the lane 8 to the right in the 16-lane row; silu(g) * u with the hardware
+        // exp2 and reciprocal (a few ulp; far inside the tolerance)
+        const float u = dpp_f<0x128>(v);   // row_ror:8
+        v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
+        const int n = tile * 8 + li;
+        if (t < T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      } else {
+        if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
+        if (p.res) v += elem_to_float(epi[tc * 16 + li], p.x_dtype);
+        if (p.add) v += elem_to_float(epi[T * 16 + li], p.x_dtype);
+        const int n = tile * 16 + li;
+        if (t < T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      }
+    }
+  }
+}
+
 template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   static_assert(CHUNKED == (NS == 0), "the streaming variant has a fixed step count");
@@ -1193,9 +1254,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     }
   };
   // Merge the waves' partials of a tile and finish it (epilogue inputs from slot `epi`).
-  auto finish = [&](int tile, int buf, const uint16_t* epi) __attribute__((always_inline)) {
+  // Finish a tile whose partials sit in buffer buf (rot: the tile's index among this
+  // workgroup's tiles; a barrier must separate the partial writes from this).
+  auto fin = [&](int tile, int rot, int buf, const uint16_t* epi) __attribute__((always_inline)) {
+    if (BF16OP && p.terms == 3) finalize<MT, 3>(p, red, mr, epi, buf, tile, tid);   // rows straddle lanes
+    else if (p.terms == 1) finalize_rows<MT, 1>(p, red, mr, epi, buf, tile, rot, wv, lane);
+    else finalize_rows<MT, 2>(p, red, mr, epi, buf, tile, rot, wv, lane);
+  };
+  auto finish = [&](int tile, int rot, int buf, const uint16_t* epi) __attribute__((always_inline)) {
     lds_barrier();
-    finalize<MT, BF16OP ? 3 : 2>(p, red, mr, epi, buf, tile, tid);
+    fin(tile, rot, buf, epi);
   };
 
   if (tid < kStatFloats) stat[tid] = 0.0f;
@@ -1210,7 +1278,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     const long stage_bytes = kWaves * S::wave_block_bytes(p.rows);
     unsigned char* ring = region + (stage_bytes > merge_bytes(MT) ? stage_bytes : merge_bytes(MT));
     const int slot_bytes = S::sb_slot_bytes(p.K / 64);
-    uint16_t* epi = reinterpret_cast<uint16_t*>(ring + 2 * slot_bytes);   // two slots of kEpiSlot
+    uint16_t* epi = reinterpret_cast<uint16_t*>(ring + 2 * slot_bytes);   // three slots of kEpiSlot
     unsigned char* blk = region + wv * S::wave_block_bytes(p.rows);
     // Issue order: the first tile's scales, this wave's window of the activation rows, then
     // the first tile's codes, so that staging waits for its own rows only and the code
@@ -1242,51 +1310,61 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       mr[2 * tid] = m;
       mr[2 * tid + 1] = 1.0f / sqrtf(var + p.eps);
     }
-    // One half: the next tile's scales and codes and this tile's epilogue inputs are issued,
-    // then `tile` is computed from `cur` (loaded one half earlier) and finished.  Epilogue
-    // inputs are loaded and read within one half: a load in flight across the loop edge
-    // would make the compiler drain the prefetch at the top of the loop.
+    // One half: the next tile's scales, codes and epilogue inputs are issued; the previous
+    // tile is finished (its partials were ordered by the last barrier, and the wave's wait for
+    // this tile's codes absorbs the work); this tile is computed from `cur` (loaded one half
+    // earlier), its partials written, the next tile's slots filled, and the workgroup synced.
+    // Epilogue inputs rotate over three slots: tile r's slot is read in half r + 1, while
+    // half r + 1 fills tile r + 2's.  Epilogue inputs are loaded and stored within one half:
+    // a load in flight across the loop edge would make the compiler drain the prefetch at the
+    // top of the loop.
+    const int G = gridDim.x;
+    auto epi_slot = [&](int rot) __attribute__((always_inline)) { return epi + (rot % 3) * kEpiSlot; };
     auto half = [&](const typename S::TileRegs& cur, typename S::TileRegs& nxt, int tile, int next,
-                    int buf) __attribute__((always_inline)) {
+                    int buf, int rot) __attribute__((always_inline)) {
       typename S::SbRegs sb;
       if constexpr (S::QUANT) S::sb_issue(p, next, tid, sb);   // past the last tile: zeros
       typename S::EpRegs ep;
       S::ep_issue(p, next, tid, ep);
       S::template load_tile<false, false>(p, next, s_lo, nsw, c, li, nxt);
+      if (rot > 0) fin(tile - G, rot - 1, buf ^ 1, epi_slot(rot - 1));
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_ring(p, s_from, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
       write_partials(acc, buf);
-      // the next tile's slots were last read during the previous half
+      // the next tile's ring slot was last read during the previous half
       if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);
-      S::ep_commit(p, tid, ep, epi + (buf ^ 1) * kEpiSlot);
-      finish(tile, buf, epi + buf * kEpiSlot);
+      S::ep_commit(p, tid, ep, epi_slot(rot + 1));
+      lds_barrier();
     };
     // Tiles come in pairs so that the loop is entered again only after the second half: an
     // exit test after the first half that shares a block with the loop test would leave the
     // second set's loads looking unread at the top of the loop.
-    const int G = gridDim.x;
     const int n = (p.ntiles - tile + G - 1) / G;   // this block's tiles (>= 1: grid <= ntiles)
     for (int i = 0; i + 1 < n; i += 2, tile += 2 * G) {
-      half(ra, rb, tile, tile + G, 0);
-      half(rb, ra, tile + G, tile + 2 * G, 1);
+      half(ra, rb, tile, tile + G, 0, i);
+      half(rb, ra, tile + G, tile + 2 * G, 1, i + 1);
     }
-    if (n & 1) {
+    if (n & 1) {   // the last tile (index n - 1, buffer 0) is `tile`
+      if (n > 1) fin(tile - G, n - 2, 1, epi_slot(n - 2));
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_ring(p, s_from, s_lo, c, li, ra.dw, ring, acc);
       write_partials(acc, 0);
-      finish(tile, 0, epi);
+      lds_barrier();
+      fin(tile, n - 1, 0, epi_slot(n - 1));
+    } else {       // the last tile (index n - 1, buffer 1) is tile - G
+      fin(tile - G, n - 1, 1, epi_slot(n - 1));
     }
   } else {
     // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
     // units; switching chunks multiplies by a ratio of powers of two (exact).
     const int nchunks = (p.steps + p.chunk_steps - 1) / p.chunk_steps;
     bool first = true;
-    int buf = 0;
-    for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x, buf ^= 1) {
+    int buf = 0, rot = 0;
+    for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x, buf ^= 1, ++rot) {
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
@@ -1321,18 +1399,18 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       S::ep_issue(p, tile, tid, ep);
       write_partials(acc, buf);
       S::ep_commit(p, tid, ep, epi + buf * kEpiSlot);
-      finish(tile, buf, epi + buf * kEpiSlot);
+      finish(tile, rot, buf, epi + buf * kEpiSlot);
     }
   }
 }
 
 // Dynamic LDS of a streaming launch: header + max(per-wave staging blocks, merge) + the
-// scale/bias ring + the epilogue slots (the same layout the kernel carves).
+// scale/bias ring (two slots) + the epilogue slots (three), the layout the kernel carves.
 template <int BITS, bool BF16OP, int MT, int NS>
 __host__ __device__ constexpr long stream_lds_bytes(int rows, int K) {
   using S = Fused<BITS, BF16OP, MT, NS>;
   const long st = kWaves * S::wave_block_bytes(rows), mg = merge_bytes(MT);
-  return kHeaderBytes + (st > mg ? st : mg) + 2L * S::sb_slot_bytes(K / 64) + 2L * kEpiSlot * 2;
+  return kHeaderBytes + (st > mg ? st : mg) + 2L * S::sb_slot_bytes(K / 64) + 3L * kEpiSlot * 2;
 }
 
 // Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
