@@ -177,9 +177,15 @@ constexpr int kRowPad = 8;
 constexpr int kStatFloats = 64;
 constexpr int kExpInts = 128;
 constexpr int kRowMax = 64;
-// Streaming variant: per-wave LN sums S1, S2 of up to 32 rows (each wave sums its window).
+// Streaming variant: per-wave LN sums S1, S2 of up to 32 rows (each wave sums its window),
+// and the merge-buffer handshake words (count, generation, finished, per buffer).
 constexpr int kWaveStatFloats = kWaves * 64;
-constexpr int kHeaderBytes = (2 * kStatFloats + kExpInts + 2 * kRowMax + kWaveStatFloats) * 4;
+constexpr int kSyncInts = 16;
+constexpr int kSyncOffset = (2 * kStatFloats + kExpInts + 2 * kRowMax + kWaveStatFloats) * 4;
+constexpr int kHeaderBytes = kSyncOffset + kSyncInts * 4;
+// Iterations of a bounded LDS wait (each sleeps ~64 clocks): far longer than any real wait,
+// so that a broken handshake ends the kernel instead of hanging the device.
+constexpr int kSpinMax = 1 << 22;
 // Largest dynamic LDS a launch may ask for (gfx950 has 160 KiB per CU).
 // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -1057,6 +1063,103 @@ struct Fused {
     }
     compute_core(NS, dw, sc, bfr, acc);
   }
+
+  // ---- per-wave scales and biases (streaming variant) --------------------------------
+  // Each wave loads the scales and biases of its own window for a tile's 16 rows with one
+  // load per lane: lanes of even lane groups c take row li's biases, odd ones its scales
+  // (WGR fp16 values, one aligned load: K is a multiple of 512 and the window starts at a
+  // multiple of NS steps), and v_permlane16_swap hands each lane its partner group's half.
+  static constexpr int WGR = NS * NG;                    // groups of a window
+  static constexpr int WD = WGR >= 2 ? WGR / 2 : 1;      // dwords they take
+  struct SbW {
+    u4_t v;
+  };
+  __device__ __forceinline__ static void sbw_issue(const LinParams& p, int tile, int s_lo, int c, int li, SbW& r) {
+    r.v = (u4_t){0u, 0u, 0u, 0u};
+    if constexpr (QUANT) {
+      int proj, n;
+      tile_row(p, tile, li, proj, n);
+      const bool valid = tile < p.ntiles && n < p.N;
+      const int G = p.K / 64;
+      const gptr<const uint16_t> base = pick((c & 1) ? p.sc[0] : p.bi[0], (c & 1) ? p.sc[1] : p.bi[1], proj);
+      const gptr<const uint16_t> zh = pick(reinterpret_cast<const uint16_t*>(g_zero16),
+                                           reinterpret_cast<const uint16_t*>(g_zero16), 0);
+      const gptr<const uint16_t> src = valid ? base + (long)n * G + (long)s_lo * NG : zh;
+      if constexpr (WGR == 1) {
+        r.v[0] = *src;
+      } else if constexpr (WGR == 2) {
+        r.v[0] = *reinterpret_cast<gptr<const uint32_t>>(src);
+      } else if constexpr (WGR == 4) {
+        typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+        const u2_t d = *reinterpret_cast<gptr<const u2_t>>(src);
+        r.v[0] = d[0];
+        r.v[1] = d[1];
+      } else {
+        static_assert(WGR == 8, "windows of 1, 2, 4 or 8 groups");
+        r.v = *reinterpret_cast<gptr<const u4_t>>(src);
+      }
+    }
+  }
+  // A tile from the code registers and this wave's scale/bias registers.
+  __device__ __forceinline__ void compute_regs(int s_from, int c, const SbW& sb, const u4_t dw[MAXS], f4_t acc[MT]) {
+    static_assert(NS > 0, "the streaming variant");
+    uint32_t sc[MAXS];
+    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
+    if constexpr (QUANT) {
+      uint32_t scl[WD], bia[WD];
+#pragma unroll
+      for (int j = 0; j < WD; ++j) {
+        // with both operands equal, result 0 holds rows 0, 0, 2, 2 and result 1 rows 1, 1, 3, 3
+        const auto r = __builtin_amdgcn_permlane16_swap(sb.v[j], sb.v[j], false, false);
+        const uint32_t own = (c & 1) ? (uint32_t)r[1] : (uint32_t)r[0];
+        const uint32_t partner = (c & 1) ? (uint32_t)r[0] : (uint32_t)r[1];
+        scl[j] = (c & 1) ? own : partner;
+        bia[j] = (c & 1) ? 0u : own;   // odd lane groups feed the bias MFMA groups 8..15: none
+      }
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) {
+        const uint32_t v = NG == 2 ? scl[s] : (scl[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+        sc[s] = s >= s_from ? v : 0u;   // steps before s_from are another wave's
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int g0 = 2 * w, g1 = 2 * w + 1;
+        const uint32_t v = w < WD ? bia[w < WD ? w : 0] : 0u;
+        const bool ok0 = g0 < WGR && g0 >= s_from * NG, ok1 = g1 < WGR && g1 >= s_from * NG;
+        bfr[w] = (ok0 ? (v & 0xFFFFu) : 0u) | (ok1 ? (v & 0xFFFF0000u) : 0u);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) sc[s] = 0u;
+    }
+    compute_core(NS, dw, sc, bfr, acc);
+  }
+
+  // Epilogue inputs of the outputs a finishing lane owns (linear with residual or constant):
+  // residual[t, n] for its NO rows and constant[n], loaded a tile ahead.  Every wave issues
+  // the loads, from the zero buffer where it does not finish the tile's block b (< MT):
+  // a load on one path only would make the compiler copy, and so wait for, its value.
+  struct EpW {
+    uint32_t v[5];
+  };
+  // nt: operand terms per activation row (1 or 2): the lane owns 4 / nt output rows.
+  __device__ __forceinline__ static void epw_issue(const LinParams& p, int tile, int b, int nt, int c, int li, EpW& e) {
+    const gptr<const uint16_t> z16 = pick(reinterpret_cast<const uint16_t*>(g_zero16),
+                                          reinterpret_cast<const uint16_t*>(g_zero16), 0);
+    const gptr<const uint16_t> rp = pick(reinterpret_cast<const uint16_t*>(p.res), reinterpret_cast<const uint16_t*>(p.res), 0);
+    const gptr<const uint16_t> ap = pick(reinterpret_cast<const uint16_t*>(p.add), reinterpret_cast<const uint16_t*>(p.add), 0);
+    const int n = tile * 16 + li;
+    const bool nok = b < MT && tile < p.ntiles && n < p.N;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      const int t = ((16 * b + 4 * c) >> (nt - 1)) + o;
+      // 32 x 32 -> 64-bit offset in one multiply-add (a 64-bit product would read an
+      // undefined high half, which may be a register still waiting for a load)
+      const uint64_t off = (uint64_t)(uint32_t)t * (uint32_t)p.N + (uint32_t)n;
+      e.v[o] = *((p.res && nok && o < (4 >> (nt - 1)) && t < p.T) ? rp + off : z16);
+    }
+    e.v[4] = *((p.add && nok) ? ap + n : z16);
+  }
 };
 
 // Per-row LN moments from the shifted sums S1, S2 of row t: m = S1 / K (the mean of the
@@ -1124,70 +1227,146 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
   }
 }
 
-// Merge, LN fold, epilogue and store of one tile, by the waves that own its 16-row blocks:
-// wave w takes block b = (w - rot) mod 8 (when b < MT), rot counting the workgroup's tiles,
-// so that the work rotates over the waves from tile to tile.  Each lane sums the eight waves' partials of its own C position
-// (16-byte LDS reads at the position the partials were written from: no bank conflicts),
-// in wave order, then finishes the outputs of its rows in registers: rows NT t .. NT t +
-// NT - 1 of an activation row t lie in one lane (NT = 1 or 2).  With LN, G_n and B_n (the
-// gamma and beta rows) are merged from the partials by every lane that needs them.  A
-// gate/up tile pairs column n (gate) with column n + 8 (up) of the same 16-lane row.
-// Epilogue order as [p1] `_linear_kernel`: GELU, then residual, then constant; one rounding
-// to the output type.
+// Merge, LN fold, epilogue and store of 16-row block b of a tile, by one wave.  Each lane
+// sums the eight waves' partials of its own C position (16-byte LDS reads where the
+// partials were written: no bank conflicts) in wave order, then finishes the outputs of its
+// rows in registers: rows NT t .. NT t + NT - 1 of an activation row t lie in one lane
+// (NT = 1 or 2).  With LN, G_n and B_n (the gamma and beta rows) are merged from the
+// partials as well.  A gate/up tile pairs column n (gate) with column n + 8 (up) of the same
+// 16-lane row.  part: the tile's partials, [wave][MT][256].  res / add: the lane's residual
+// values (one per output row) and constant.  Epilogue order as [p1] `_linear_kernel`: GELU,
+// then residual, then constant; one rounding to the output type.
 template <int MT, int NT>
-__device__ __forceinline__ void finalize_rows(const LinParams& p, const float* red, const float* mr, const uint16_t* epi,
-                                              int buf, int tile, int rot, int wv, int lane) {
+__device__ __forceinline__ void finalize_block(const LinParams& p, const float* part, const float* mr, int b, int tile,
+                                               int lane, const float res[4 / NT], float add) {
   const int c = lane >> 4, li = lane & 15;
   const int T = p.T;
-  for (int b = (wv - rot) & 7; b < MT; b += kWaves) {   // uniform per wave
-    f4_t m = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  f4_t m = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const f4_t v = *reinterpret_cast<const f4_t*>(part + (w * MT + b) * 256 + lane * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] += v[j];
+  }
+  float G = 0.0f, B = 0.0f;
+  if (p.ln) {   // uniform: G_n, B_n from rows NT T and NT T + 1, column li
+    const int rg = NT * T, rb = rg + 1;
+    const float* pg = part + (rg >> 4) * 256 + ((((rg & 15) >> 2) << 4) | li) * 4 + (rg & 3);
+    const float* pb = part + (rb >> 4) * 256 + ((((rb & 15) >> 2) << 4) | li) * 4 + (rb & 3);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const f4_t v = *reinterpret_cast<const f4_t*>(red + ((buf * kWaves + w) * MT + b) * 256 + lane * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m[j] += v[j];
+      G += pg[w * MT * 256];
+      B += pb[w * MT * 256];
     }
-    float G = 0.0f, B = 0.0f;
-    if (p.ln) {   // uniform: G_n, B_n from rows NT T and NT T + 1, column li
-      const int rg = NT * T, rb = rg + 1;
-      const float* pg = red + (buf * kWaves * MT + (rg >> 4)) * 256 + ((((rg & 15) >> 2) << 4) | li) * 4 + (rg & 3);
-      const float* pb = red + (buf * kWaves * MT + (rb >> 4)) * 256 + ((((rb & 15) >> 2) << 4) | li) * 4 + (rb & 3);
+  }
+  constexpr int NO = 4 / NT;   // activation rows per lane
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        G += pg[w * MT * 256];
-        B += pb[w * MT * 256];
-      }
-    }
-    constexpr int NO = 4 / NT;   // activation rows per lane
+  for (int o = 0; o < NO; ++o) {
+    const int t = (16 * b + 4 * c) / NT + o;
+    const int tc = min(t, T - 1);
+    float v = 0.0f;
 #pragma unroll
-    for (int o = 0; o < NO; ++o) {
-      const int t = (16 * b + 4 * c) / NT + o;
-      const int tc = min(t, T - 1);
-      float v = 0.0f;
-#pragma unroll
-      for (int term = 0; term < NT; ++term) v += m[o * NT + term];
-      if (p.ln) v = mr[2 * tc + 1] * (v - mr[2 * tc] * G) + B;
-      if (p.gateup) {
-        // u from the lane 8 to the right in the 16-lane row; silu(g) * u with the hardware
-        // exp2 and reciprocal (a few ulp; far inside the tolerance)
-        const float u = dpp_f<0x128>(v);   // row_ror:8
-        v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
-        const int n = tile * 8 + li;
-        if (t < T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
-      } else {
-        if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
-        if (p.res) v += elem_to_float(epi[tc * 16 + li], p.x_dtype);
-        if (p.add) v += elem_to_float(epi[T * 16 + li], p.x_dtype);
-        const int n = tile * 16 + li;
-        if (t < T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
-      }
+    for (int term = 0; term < NT; ++term) v += m[o * NT + term];
+    if (p.ln) v = mr[2 * tc + 1] * (v - mr[2 * tc] * G) + B;
+    if (p.gateup) {
+      // u from the lane 8 to the right in the 16-lane row; silu(g) * u with the hardware
+      // exp2 and reciprocal (a few ulp; far inside the tolerance)
+      const float u = dpp_f<0x128>(v);   // row_ror:8
+      v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
+      const int n = tile * 8 + li;
+      if (t < T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+    } else {
+      if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
+      if (p.res) v += res[o];
+      if (p.add) v += add;
+      const int n = tile * 16 + li;
+      if (t < T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
     }
   }
 }
 
-template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS>
+// A tile whose partials sit in double-buffer half buf, finished by the waves that own its
+// blocks: wave w takes block b = (w - rot) mod 8 (when b < MT), rot counting the
+// workgroup's tiles, so that the work rotates over the waves.  Epilogue inputs come from
+// the LDS slot epi ([T + 1][16] of the input type).
+template <int MT, int NT>
+__device__ __forceinline__ void finalize_rows(const LinParams& p, const float* red, const float* mr, const uint16_t* epi,
+                                              int buf, int tile, int rot, int wv, int lane) {
+  const int c = lane >> 4, li = lane & 15;
+  for (int b = (wv - rot) & 7; b < MT; b += kWaves) {   // uniform per wave
+    float res[4 / NT];
+#pragma unroll
+    for (int o = 0; o < 4 / NT; ++o) {
+      const int t = min((16 * b + 4 * c) / NT + o, p.T - 1);
+      res[o] = p.res ? elem_to_float(epi[t * 16 + li], p.x_dtype) : 0.0f;
+    }
+    const float add = p.add ? elem_to_float(epi[p.T * 16 + li], p.x_dtype) : 0.0f;
+    finalize_block<MT, NT>(p, red + buf * kWaves * MT * 256, mr, b, tile, lane, res, add);
+  }
+}
+
+// The whole tile by one wave, for rows of three terms (they straddle lanes and blocks):
+// the lanes merge every block into wave 0's partials (in place, each lane its own
+// positions), then lane (q, n) finishes outputs (4 i + q, n) from the merged rows.  The
+// residual and constant are read from global memory here (a rare path).
+template <int MT>
+__device__ __forceinline__ void finalize_tile3(const LinParams& p, float* part, const float* mr, int tile, int lane) {
+  constexpr int NT = 3;
+  const int T = p.T;
+#pragma unroll
+  for (int b = 0; b < MT; ++b) {
+    f4_t m = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const f4_t v = *reinterpret_cast<const f4_t*>(part + (w * MT + b) * 256 + lane * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] += v[j];
+    }
+    *reinterpret_cast<f4_t*>(part + b * 256 + lane * 4) = m;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  auto row = [&](int r, int n) __attribute__((always_inline)) {
+    return part[(r >> 4) * 256 + ((((r & 15) >> 2) << 4) | n) * 4 + (r & 3)];
+  };
+  const int q = lane >> 4, col = lane & 15;
+  const float G = p.ln ? row(NT * T, col) : 0.0f, B = p.ln ? row(NT * T + 1, col) : 0.0f;
+  for (int t0 = 0; t0 < T; t0 += 4) {
+    const int t = t0 + q, tc = min(t, T - 1);
+    float v = row(NT * tc, col) + row(NT * tc + 1, col) + row(NT * tc + 2, col);
+    if (p.ln) v = mr[2 * tc + 1] * (v - mr[2 * tc] * G) + B;
+    if (p.gateup) {
+      const float u = dpp_f<0x128>(v);   // row_ror:8
+      v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
+      const int n = tile * 8 + col;
+      if (t < T && col < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+    } else {
+      const int n = tile * 16 + col;
+      const bool ok = t < T && n < p.N;
+      if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
+      if (p.res && ok) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.res)[(long)t * p.N + n], p.x_dtype);
+      if (p.add && ok) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.add)[n], p.x_dtype);
+      if (ok) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+    }
+  }
+}
+
+// Bounded wait until an LDS word equals v (all lanes read the same word).
+__device__ __forceinline__ void lds_wait_eq(const int* a, int v) {
+#pragma nounroll
+  for (int it = 0; it < kSpinMax; ++it) {
+    const int cur = __builtin_amdgcn_readfirstlane(__hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (cur == v) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// EPI (streaming variant): the call is a linear with residual or constant inputs.
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   static_assert(CHUNKED == (NS == 0), "the streaming variant has a fixed step count");
+  static_assert(!(CHUNKED && EPI), "the chunked variant stages epilogue inputs in LDS");
   using S = Fused<BITS, BF16OP, MT, NS>;
   constexpr int STEPK = S::STEPK;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -1242,8 +1421,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     lds_barrier();
   };
   // This wave's partials of a tile into LDS (double-buffered by tile parity).
-  auto write_partials = [&](const f4_t acc[MT], int buf) __attribute__((always_inline)) {
-    float* rb = red + (buf * kWaves + wv) * MT * 256;
+  auto write_partials = [&](const f4_t acc[MT], int buf, float* base) __attribute__((always_inline)) {
+    float* rb = base + (buf * kWaves + wv) * MT * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f4_t v;
@@ -1270,93 +1449,141 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   int cs0, s_lo, nsw, s_from;
   if constexpr (!CHUNKED) {
     // All of K fits: build the fragments once, then stream tiles with the next tile's codes,
-    // scales and biases always in flight.  Two code register sets alternate (no copy at the
-    // end of an iteration, which would make the compiler wait for the prefetch); scales and
-    // biases alternate between two ring slots.
+    // scales and biases always in flight (two register sets alternate: a copy at the end of
+    // an iteration would make the compiler wait for the prefetch).  The waves do not meet at
+    // a barrier per tile: each streams its own window, and the partials of a tile meet in
+    // one of NB LDS buffers through a handshake of three words per buffer:
+    //   gen  the tile the buffer is open for; a wave writes its partials only once it is;
+    //   cnt  waves whose partials are in; the finishing waves wait for all eight;
+    //   fin  finishing waves done; the last one empties the buffer and opens it for tile + NB.
+    // Every wait is for earlier work of tiles in order, so no wait can close a cycle, and
+    // each is bounded besides.
+    constexpr int NB = MT <= 2 ? 4 : 2;   // merge buffers in flight
     slice(0, cs0, s_lo, nsw, s_from);
     int tile = blockIdx.x;
-    const long stage_bytes = kWaves * S::wave_block_bytes(p.rows);
-    unsigned char* ring = region + (stage_bytes > merge_bytes(MT) ? stage_bytes : merge_bytes(MT));
-    const int slot_bytes = S::sb_slot_bytes(p.K / 64);
-    uint16_t* epi = reinterpret_cast<uint16_t*>(ring + 2 * slot_bytes);   // three slots of kEpiSlot
     unsigned char* blk = region + wv * S::wave_block_bytes(p.rows);
+    int* pcnt = reinterpret_cast<int*>(lds_raw + kSyncOffset);
+    int* pgen = pcnt + NB;
+    int* pfin = pgen + NB;
+    const bool three = BF16OP && p.terms == 3;   // rows straddle lanes: one wave finishes a tile
+    const int nfin = three ? 1 : MT;               // finishing waves per tile
     // Issue order: the first tile's scales, this wave's window of the activation rows, then
     // the first tile's codes, so that staging waits for its own rows only and the code
     // stream runs under it.
-    typename S::SbRegs sb0;
-    if constexpr (S::QUANT) S::sb_issue(p, tile, tid, sb0);
-    typename S::EpRegs ep0;
-    S::ep_issue(p, tile, tid, ep0);
+    typename S::SbW sa, sb;
+    S::sbw_issue(p, tile, s_lo, c, li, sa);
     typename S::WaveRegs wr;
     S::wave_stage_load(p, s_lo * STEPK, lane, wr);
     typename S::TileRegs ra, rb;
     S::template load_tile<false, false>(p, tile, s_lo, nsw, c, li, ra);
     S::wave_stage(p, wstat + wv * 64, blk, lane, s_from, wr);
-    if constexpr (S::QUANT) S::sb_commit(p, tid, sb0, ring);
-    S::ep_commit(p, tid, ep0, epi);
     // the block is this wave's own: its writes only need to have completed
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     st.load_frags_wave(p, blk, s_from, c, li);
-    // every wave is done with its block before the merge partials reuse the region; the
-    // ring, epilogue slot and LN sums are visible to all
-    lds_barrier();
-    if (p.ln && tid < p.T) {   // LN moments from the waves' sums (read after a later barrier)
-      float s1 = 0.0f, s2 = 0.0f;
-      for (int w = 0; w < kWaves; ++w) { s1 += wstat[w * 64 + 2 * tid]; s2 += wstat[w * 64 + 2 * tid + 1]; }
-      const float m = s1 / (float)p.K;
-      const float var = fmaxf(s2 / (float)p.K - m * m, 0.0f);
-      mr[2 * tid] = m;
-      mr[2 * tid + 1] = 1.0f / sqrtf(var + p.eps);
+    if (tid < NB) {
+      pcnt[tid] = 0;
+      pfin[tid] = 0;
+      pgen[tid] = tid;
     }
-    // One half: the next tile's scales, codes and epilogue inputs are issued; the previous
-    // tile is finished (its partials were ordered by the last barrier, and the wave's wait for
-    // this tile's codes absorbs the work); this tile is computed from `cur` (loaded one half
-    // earlier), its partials written, the next tile's slots filled, and the workgroup synced.
-    // Epilogue inputs rotate over three slots: tile r's slot is read in half r + 1, while
-    // half r + 1 fills tile r + 2's.  Epilogue inputs are loaded and stored within one half:
-    // a load in flight across the loop edge would make the compiler drain the prefetch at the
-    // top of the loop.
+    // every wave is done with its block before the merge partials reuse the region; the LN
+    // sums and the handshake words are visible to all
+    lds_barrier();
+    if (p.ln) {   // uniform: LN moments from the waves' sums, for every finishing wave
+      if (tid < p.T) {
+        float s1 = 0.0f, s2 = 0.0f;
+        for (int w = 0; w < kWaves; ++w) { s1 += wstat[w * 64 + 2 * tid]; s2 += wstat[w * 64 + 2 * tid + 1]; }
+        const float m = s1 / (float)p.K;
+        const float var = fmaxf(s2 / (float)p.K - m * m, 0.0f);
+        mr[2 * tid] = m;
+        mr[2 * tid + 1] = 1.0f / sqrtf(var + p.eps);
+      }
+      lds_barrier();
+    }
     const int G = gridDim.x;
-    auto epi_slot = [&](int rot) __attribute__((always_inline)) { return epi + (rot % 3) * kEpiSlot; };
-    auto half = [&](const typename S::TileRegs& cur, typename S::TileRegs& nxt, int tile, int next,
-                    int buf, int rot) __attribute__((always_inline)) {
-      typename S::SbRegs sb;
-      if constexpr (S::QUANT) S::sb_issue(p, next, tid, sb);   // past the last tile: zeros
-      typename S::EpRegs ep;
-      S::ep_issue(p, next, tid, ep);
+    // block of tile rot this wave finishes (none when >= nfin)
+    auto my_block = [&](int rot) __attribute__((always_inline)) { return (wv - rot) & 7; };
+    // Put this wave's partials of tile rot into its buffer once the buffer is open for it.
+    auto put = [&](const f4_t acc[MT], int rot) __attribute__((always_inline)) {
+      const int q = rot & (NB - 1);
+      lds_wait_eq(pgen + q, rot);
+      write_partials(acc, 0, red + q * kWaves * MT * 256);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the writes are done
+      if (lane == 0) __hip_atomic_fetch_add(pcnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // Finish tile `tl` (index rot) if this wave owns one of its blocks.
+    auto finish_tile = [&](int tl, int rot, const typename S::EpW& e) __attribute__((always_inline)) {
+      const int b = my_block(rot);
+      if (b < nfin) {   // uniform
+        const int q = rot & (NB - 1);
+        lds_wait_eq(pcnt + q, kWaves);
+        float* part = red + q * kWaves * MT * 256;
+        if (three) {
+          finalize_tile3<MT>(p, part, mr, tl, lane);
+        } else {
+          float res[4], add = __builtin_bit_cast(float, 0u);
+#pragma unroll
+          for (int o = 0; o < 4; ++o) res[o] = elem_to_float(e.v[o], p.x_dtype);
+          add = elem_to_float(e.v[4], p.x_dtype);
+          if (p.terms == 1) finalize_block<MT, 1>(p, part, mr, b, tl, lane, res, add);
+          else finalize_block<MT, 2>(p, part, mr, b, tl, lane, res, add);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the reads are done
+        if (lane == 0) {
+          if (__hip_atomic_fetch_add(pfin + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == nfin - 1) {
+            __hip_atomic_store(pfin + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(pcnt + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(pgen + q, rot + NB, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+      } else {
+        asm volatile("" ::"v"(e.v[0]), "v"(e.v[1]), "v"(e.v[2]), "v"(e.v[3]), "v"(e.v[4]));
+      }
+    };
+    auto ep_load = [&](int tl, int rot, typename S::EpW& e) __attribute__((always_inline)) {
+      if constexpr (EPI) S::epw_issue(p, tl, three ? MT : my_block(rot), three ? 1 : p.terms, c, li, e);
+    };
+    // One half: the next tile's codes and scales and this tile's epilogue inputs are issued;
+    // the previous tile is finished (the wave's wait for this tile's codes absorbs the work);
+    // this tile is computed from `cur` and `scur` (loaded one half earlier) and its partials
+    // are put.  Epilogue inputs are loaded in the half before their use.
+    auto half = [&](const typename S::TileRegs& cur, typename S::TileRegs& nxt, const typename S::SbW& scur,
+                    typename S::SbW& snxt, const typename S::EpW& eprev, typename S::EpW& ecur, int tl, int next,
+                    int rot) __attribute__((always_inline)) {
+      S::sbw_issue(p, next, s_lo, c, li, snxt);   // past the last tile: zeros
       S::template load_tile<false, false>(p, next, s_lo, nsw, c, li, nxt);
-      if (rot > 0) fin(tile - G, rot - 1, buf ^ 1, epi_slot(rot - 1));
+      ep_load(tl, rot, ecur);
+      if (rot > 0) finish_tile(tl - G, rot - 1, eprev);
+      else asm volatile("" ::"v"(eprev.v[0]), "v"(eprev.v[1]), "v"(eprev.v[2]), "v"(eprev.v[3]), "v"(eprev.v[4]));
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      st.compute_ring(p, s_from, s_lo, c, li, cur.dw, ring + buf * slot_bytes, acc);
-      write_partials(acc, buf);
-      // the next tile's ring slot was last read during the previous half
-      if constexpr (S::QUANT) S::sb_commit(p, tid, sb, ring + (buf ^ 1) * slot_bytes);
-      S::ep_commit(p, tid, ep, epi_slot(rot + 1));
-      lds_barrier();
+      st.compute_regs(s_from, c, scur, cur.dw, acc);
+      put(acc, rot);
     };
     // Tiles come in pairs so that the loop is entered again only after the second half: an
     // exit test after the first half that shares a block with the loop test would leave the
     // second set's loads looking unread at the top of the loop.
     const int n = (p.ntiles - tile + G - 1) / G;   // this block's tiles (>= 1: grid <= ntiles)
+    typename S::EpW ea, eb;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ea.v[i] = eb.v[i] = 0u;
     for (int i = 0; i + 1 < n; i += 2, tile += 2 * G) {
-      half(ra, rb, tile, tile + G, 0, i);
-      half(rb, ra, tile + G, tile + 2 * G, 1, i + 1);
+      half(ra, rb, sa, sb, ea, eb, tile, tile + G, i);
+      half(rb, ra, sb, sa, eb, ea, tile + G, tile + 2 * G, i + 1);
     }
-    if (n & 1) {   // the last tile (index n - 1, buffer 0) is `tile`
-      if (n > 1) fin(tile - G, n - 2, 1, epi_slot(n - 2));
+    if (n & 1) {   // the last tile (index n - 1) is `tile`, in ra / sa
+      ep_load(tile, n - 1, eb);
+      if (n > 1) finish_tile(tile - G, n - 2, ea);
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      st.compute_ring(p, s_from, s_lo, c, li, ra.dw, ring, acc);
-      write_partials(acc, 0);
-      lds_barrier();
-      fin(tile, n - 1, 0, epi_slot(n - 1));
-    } else {       // the last tile (index n - 1, buffer 1) is tile - G
-      fin(tile - G, n - 1, 1, epi_slot(n - 1));
+      st.compute_regs(s_from, c, sa, ra.dw, acc);
+      put(acc, n - 1);
+      finish_tile(tile, n - 1, eb);
+    } else {       // the last tile (index n - 1) is tile - G
+      finish_tile(tile - G, n - 1, ea);
     }
   } else {
     // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
@@ -1397,20 +1624,21 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
                                                    2 * S::sb_slot_bytes(min(p.chunk_steps * STEPK, p.K) / 64));
       typename S::EpRegs ep;
       S::ep_issue(p, tile, tid, ep);
-      write_partials(acc, buf);
+      write_partials(acc, buf, red);
       S::ep_commit(p, tid, ep, epi + buf * kEpiSlot);
       finish(tile, rot, buf, epi + buf * kEpiSlot);
     }
   }
 }
 
-// Dynamic LDS of a streaming launch: header + max(per-wave staging blocks, merge) + the
-// scale/bias ring (two slots) + the epilogue slots (three), the layout the kernel carves.
+// Dynamic LDS of a streaming launch: header + max(per-wave staging blocks, merge buffers),
+// the layout the kernel carves.
 template <int BITS, bool BF16OP, int MT, int NS>
 __host__ __device__ constexpr long stream_lds_bytes(int rows, int K) {
   using S = Fused<BITS, BF16OP, MT, NS>;
-  const long st = kWaves * S::wave_block_bytes(rows), mg = merge_bytes(MT);
-  return kHeaderBytes + (st > mg ? st : mg) + 2L * S::sb_slot_bytes(K / 64) + 3L * kEpiSlot * 2;
+  const long st = kWaves * S::wave_block_bytes(rows);
+  const long mg = (MT <= 2 ? 4L : 2L) * kWaves * MT * 256 * 4;   // the merge buffers
+  return kHeaderBytes + (st > mg ? st : mg);
 }
 
 // Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
@@ -1420,17 +1648,17 @@ __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
          2L * kEpiSlot * 2;                // two epilogue-input slots
 }
 
-template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS>
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI = false>
 hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // Above 64 KiB of dynamic LDS the kernel must opt in once (a host-side attribute).
   static bool opted_in = false;
   if (!opted_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED, NS>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
     opted_in = true;
   }
-  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED, NS>), dim3(grid), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI>), dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
@@ -1442,18 +1670,21 @@ hipError_t try_streaming(const LinParams& p, int grid, hipStream_t s) {
   const long pieces = (long)(p.T + (p.ln ? 2 : 0)) * S::W8;
   const long lds = stream_lds_bytes<BITS, BF16OP, MT, NS>(p.rows, p.K);
   if (NS > p.steps || pieces > 64L * S::kWavePieces || lds > kLdsMax) return hipErrorNotSupported;
-  return launch_variant<BITS, BF16OP, MT, false, NS>(p, grid, (size_t)lds, s);
+  if (!p.gateup && (p.res || p.add)) return launch_variant<BITS, BF16OP, MT, false, NS, true>(p, grid, (size_t)lds, s);
+  return launch_variant<BITS, BF16OP, MT, false, NS, false>(p, grid, (size_t)lds, s);
 }
 
 template <int BITS, bool BF16OP, int MT>
 hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // The streaming variant: every wave a window of NS steps (NS a power of two, at most the
   // fragment budget), the smallest that covers ceil(steps / waves).  It needs rows of whole
-  // 64-byte steps and, quantized, rows of whole 16-byte scale chunks, at most 128 groups.
+  // 64-byte steps and, quantized, K a multiple of 512 and 16-byte aligned scales and biases
+  // (each wave's window of a scale row is then one load aligned to its size).
   constexpr int M = max_steps_for(Fmt<BITS>::kMfma, MT);
   const bool whole_steps = ((long)p.K * BITS / 8) % 64 == 0;
   const int G = p.K / 64;
-  const bool ring_ok = BITS == 16 || (G % 8 == 0 && G <= 128);
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool ring_ok = BITS == 16 || (G % 8 == 0 && a16(p.sc[0]) && a16(p.sc[1]) && a16(p.bi[0]) && a16(p.bi[1]));
   const int need = (p.steps + kWaves - 1) / kWaves;
   if (whole_steps && ring_ok) {
     hipError_t e = hipErrorNotSupported;
