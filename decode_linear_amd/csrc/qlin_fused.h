@@ -782,7 +782,7 @@ struct Fused {
         uint32_t el[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          // slots past the slice meet a zero bias (compute_ring / compute_tile), so any finite
+          // slots past the slice meet a zero bias (compute_tile), so any finite
           // in-range group sum does
           const int gi = 8 * (c & 1) + j;
           const int gl = min((s_lo - cs0) * NG + gi, gpr - 1);
@@ -909,42 +909,6 @@ struct Fused {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- scales and biases of a tile through an LDS ring (streaming variant) ----------
-  // The workgroup fetches a tile's scales and biases with one coalesced 16-byte load per
-  // thread, a tile ahead, and parks them in a ring slot: [scales, biases][16 rows][pitch].
-  // Per-lane loads of a few bytes from 16 rows each would cost as much memory-pipeline time
-  // as the codes themselves.  Needs G = K / 64 a multiple of 8 (rows of whole 16-byte
-  // chunks) and G <= 128 (one chunk per thread).
-  __host__ __device__ static constexpr int sb_pitch(int G) { return 2 * G + 4; }   // bytes; +4 spreads rows over banks
-  __host__ __device__ static constexpr int sb_slot_bytes(int G) { return 32 * sb_pitch(G); }
-  struct SbRegs {
-    u4_t v;
-  };
-  __device__ __forceinline__ static void sb_issue(const LinParams& p, int tile, int tid, SbRegs& sb) {
-    const int G = p.K / 64, cpr = G / 8;              // 16-byte chunks per row
-    const int rr = (tid * ((65535 + cpr) / cpr)) >> 16;   // tid / cpr: exact while tid * cpr < 2^16
-    const int a = rr >> 4, r = rr & 15, col = tid - rr * cpr;
-    int proj, n;
-    tile_row(p, tile, r, proj, n);
-    const bool valid = tid < 32 * cpr && tile < p.ntiles && n < p.N;
-    const uintptr_t u0 = reinterpret_cast<uintptr_t>(a ? p.bi[0] : p.sc[0]);
-    const uintptr_t u1 = reinterpret_cast<uintptr_t>(a ? p.bi[1] : p.sc[1]);
-    const gptr<const char> row = reinterpret_cast<gptr<const char>>(u0 + (uintptr_t)proj * (u1 - u0)) + (long)n * G * 2;
-    const gptr<const char> zero = pick(reinterpret_cast<const char*>(g_zero16), reinterpret_cast<const char*>(g_zero16), 0);
-    sb.v = *reinterpret_cast<gptr<const u4_t>>(valid ? row + 16 * col : zero);
-  }
-  __device__ __forceinline__ static void sb_commit(const LinParams& p, int tid, const SbRegs& sb, unsigned char* slot) {
-    const int G = p.K / 64, cpr = G / 8;
-    asm volatile("" ::"v"(sb.v));   // read on every path (see compute_core)
-    if (tid < 32 * cpr) {
-      const int rr = (tid * ((65535 + cpr) / cpr)) >> 16;   // tid / cpr (as in sb_issue)
-      const int a = rr >> 4, r = rr & 15, col = tid - rr * cpr;
-      uint32_t* d = reinterpret_cast<uint32_t*>(slot + (a * 16 + r) * sb_pitch(G) + 16 * col);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[j] = sb.v[j];
-    }
-  }
-
   // One tile through the fragments: codes dw, per-step scale words sc (the step's NG fp16
   // scales, group g in bits 16g) and the bias operand bfr (slot j of lane group c holds the
   // bias of this wave's group 8*(c&1) + j, 0 past the slice).
@@ -1021,47 +985,6 @@ struct Fused {
       for (int w = 0; w < 4; ++w) bfr[w] = el[2 * w] | (el[2 * w + 1] << 16);
     }
     compute_core(nsw, r.dw, r.sc, bfr, acc);
-  }
-
-  // A tile whose scales and biases sit in ring slot `slot` (streaming variant).
-  __device__ __forceinline__ void compute_ring(const LinParams& p, int s_from, int s_lo, int c, int li, const u4_t dw[MAXS],
-                                               const unsigned char* slot, f4_t acc[MT]) {
-    static_assert(NS > 0, "the ring feeds the streaming variant");
-    uint32_t sc[MAXS];
-    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
-    if constexpr (QUANT) {
-      const int G = p.K / 64, pitch = sb_pitch(G);
-      const unsigned char* srow = slot + li * pitch;
-      const unsigned char* brow = slot + (16 + li) * pitch;
-#pragma unroll
-      for (int s = 0; s < MAXS; ++s) {
-        // the window lies inside the row; steps before s_from get a zero scale
-        uint32_t v;
-        if constexpr (NG == 2) v = *reinterpret_cast<const uint32_t*>(srow + 4 * (s_lo + s));
-        else v = *reinterpret_cast<const uint16_t*>(srow + 2 * (s_lo + s));
-        sc[s] = s >= s_from ? v : 0u;
-      }
-      if constexpr (NG == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {   // dword w: both groups of step 4*(c&1) + w
-          const int j = 4 * (c & 1) + w;
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(brow + 4 * min(s_lo + j, G / 2 - 1));
-          bfr[w] = (j >= s_from && j < NS) ? v : 0u;
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {   // halves of steps 8*(c&1) + 2w and + 2w + 1
-          const int j0 = 8 * (c & 1) + 2 * w, j1 = j0 + 1;
-          const uint32_t v0 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j0, G - 1));
-          const uint32_t v1 = *reinterpret_cast<const uint16_t*>(brow + 2 * min(s_lo + j1, G - 1));
-          bfr[w] = ((j0 >= s_from && j0 < NS) ? v0 : 0u) | (((j1 >= s_from && j1 < NS) ? v1 : 0u) << 16);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < MAXS; ++s) sc[s] = 0u;
-    }
-    compute_core(NS, dw, sc, bfr, acc);
   }
 
   // ---- per-wave scales and biases (streaming variant) --------------------------------
@@ -1545,22 +1468,24 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       if constexpr (EPI) S::epw_issue(p, tl, three ? MT : my_block(rot), three ? 1 : p.terms, c, li, e);
     };
     // One half: the next tile's codes and scales and this tile's epilogue inputs are issued;
-    // the previous tile is finished (the wave's wait for this tile's codes absorbs the work);
     // this tile is computed from `cur` and `scur` (loaded one half earlier) and its partials
-    // are put.  Epilogue inputs are loaded in the half before their use.
+    // are put; then the previous tile is finished, while the next tile's loads are in flight.
+    // Putting before finishing keeps a finishing wave from delaying its own partials, which
+    // the next tile's finishing wave waits for (a chain that would add one finish per tile).
+    // Epilogue inputs are loaded in the half before their use.
     auto half = [&](const typename S::TileRegs& cur, typename S::TileRegs& nxt, const typename S::SbW& scur,
                     typename S::SbW& snxt, const typename S::EpW& eprev, typename S::EpW& ecur, int tl, int next,
                     int rot) __attribute__((always_inline)) {
       S::sbw_issue(p, next, s_lo, c, li, snxt);   // past the last tile: zeros
       S::template load_tile<false, false>(p, next, s_lo, nsw, c, li, nxt);
       ep_load(tl, rot, ecur);
-      if (rot > 0) finish_tile(tl - G, rot - 1, eprev);
-      else asm volatile("" ::"v"(eprev.v[0]), "v"(eprev.v[1]), "v"(eprev.v[2]), "v"(eprev.v[3]), "v"(eprev.v[4]));
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_regs(s_from, c, scur, cur.dw, acc);
       put(acc, rot);
+      if (rot > 0) finish_tile(tl - G, rot - 1, eprev);
+      else asm volatile("" ::"v"(eprev.v[0]), "v"(eprev.v[1]), "v"(eprev.v[2]), "v"(eprev.v[3]), "v"(eprev.v[4]));
     };
     // Tiles come in pairs so that the loop is entered again only after the second half: an
     // exit test after the first half that shares a block with the loop test would leave the
@@ -1575,12 +1500,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     }
     if (n & 1) {   // the last tile (index n - 1) is `tile`, in ra / sa
       ep_load(tile, n - 1, eb);
-      if (n > 1) finish_tile(tile - G, n - 2, ea);
       f4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
       st.compute_regs(s_from, c, sa, ra.dw, acc);
       put(acc, n - 1);
+      if (n > 1) finish_tile(tile - G, n - 2, ea);
       finish_tile(tile, n - 1, eb);
     } else {       // the last tile (index n - 1) is tile - G
       finish_tile(tile - G, n - 1, ea);
@@ -1618,10 +1543,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       }
       first = false;
       // epilogue inputs: slot buf was last read two tiles ago, before the previous barrier
-      uint16_t* epi = reinterpret_cast<uint16_t*>(region + (staging_bytes(p.rows, min(p.chunk_steps * STEPK, p.K)) >
-                                                                   merge_bytes(MT) ? staging_bytes(p.rows, min(p.chunk_steps * STEPK, p.K))
-                                                                                   : merge_bytes(MT)) +
-                                                   2 * S::sb_slot_bytes(min(p.chunk_steps * STEPK, p.K) / 64));
+      const long stage_bytes = staging_bytes(p.rows, min(p.chunk_steps * STEPK, p.K));
+      uint16_t* epi = reinterpret_cast<uint16_t*>(region + (stage_bytes > merge_bytes(MT) ? stage_bytes : merge_bytes(MT)));
       typename S::EpRegs ep;
       S::ep_issue(p, tile, tid, ep);
       write_partials(acc, buf, red);
@@ -1641,11 +1564,10 @@ __host__ __device__ constexpr long stream_lds_bytes(int rows, int K) {
   return kHeaderBytes + (st > mg ? st : mg);
 }
 
-// Dynamic LDS a launch needs: header + max(staging, merge) + the scale/bias ring.
+// Dynamic LDS of a chunked launch: header + max(staging, merge) + two epilogue-input slots.
 __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
   return kHeaderBytes + (staging_bytes(rows, kc) > merge_bytes(mt) ? staging_bytes(rows, kc) : merge_bytes(mt)) +
-         2L * 32 * (2 * (kc / 64) + 4) +   // two scale/bias ring slots
-         2L * kEpiSlot * 2;                // two epilogue-input slots
+         2L * kEpiSlot * 2;
 }
 
 template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI = false>
@@ -1684,9 +1606,9 @@ hipError_t launch_one(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   const bool whole_steps = ((long)p.K * BITS / 8) % 64 == 0;
   const int G = p.K / 64;
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  const bool ring_ok = BITS == 16 || (G % 8 == 0 && a16(p.sc[0]) && a16(p.sc[1]) && a16(p.bi[0]) && a16(p.bi[1]));
+  const bool scales_ok = BITS == 16 || (G % 8 == 0 && a16(p.sc[0]) && a16(p.sc[1]) && a16(p.bi[0]) && a16(p.bi[1]));
   const int need = (p.steps + kWaves - 1) / kWaves;
-  if (whole_steps && ring_ok) {
+  if (whole_steps && scales_ok) {
     hipError_t e = hipErrorNotSupported;
     if (need <= 1) e = try_streaming<BITS, BF16OP, MT, 1>(p, grid, s);
     else if (need <= 2) { if constexpr (M >= 2) e = try_streaming<BITS, BF16OP, MT, 2>(p, grid, s); }
