@@ -1164,13 +1164,16 @@ __device__ __forceinline__ void finalize_block(const LinParams& p, const float* 
                                                int lane, const float res[4 / NT], float add) {
   const int c = lane >> 4, li = lane & 15;
   const int T = p.T;
+  // all eight reads in flight before the first add (one LDS round trip)
+  f4_t pv[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) pv[w] = *reinterpret_cast<const f4_t*>(part + (w * MT + b) * 256 + lane * 4);
+  __builtin_amdgcn_sched_barrier(0);
   f4_t m = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const f4_t v = *reinterpret_cast<const f4_t*>(part + (w * MT + b) * 256 + lane * 4);
+  for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] += v[j];
-  }
+    for (int j = 0; j < 4; ++j) m[j] += pv[w][j];
   float G = 0.0f, B = 0.0f;
   if (p.ln) {   // uniform: G_n, B_n from rows NT T and NT T + 1, column li
     const int rg = NT * T, rb = rg + 1;
