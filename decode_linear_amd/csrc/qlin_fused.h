@@ -1393,13 +1393,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     int* pfin = pgen + NB;
     const bool three = BF16OP && p.terms == 3;   // rows straddle lanes: one wave finishes a tile
     const int nfin = three ? 1 : MT;               // finishing waves per tile
-    // Issue order: the first tile's scales, this wave's window of the activation rows, then
-    // the first tile's codes, so that staging waits for its own rows only and the code
-    // stream runs under it.
-    typename S::SbW sa, sb;
-    S::sbw_issue(p, tile, s_lo, c, li, sa);
+    // Issue order: this wave's window of the activation rows, then the first tile's scales
+    // and codes, so that staging waits for its own rows only (loads complete in order) and
+    // the weight stream runs under it.
     typename S::WaveRegs wr;
     S::wave_stage_load(p, s_lo * STEPK, lane, wr);
+    typename S::SbW sa, sb;
+    S::sbw_issue(p, tile, s_lo, c, li, sa);
     typename S::TileRegs ra, rb;
     S::template load_tile<false, false>(p, tile, s_lo, nsw, c, li, ra);
     S::wave_stage(p, wstat + wv * 64, blk, lane, s_from, wr);
