@@ -11,31 +11,33 @@
 //
 // How it maps onto CDNA4:
 //   * One workgroup = 8 waves, about one workgroup per CU; workgroup b visits output tiles
-//     b, b + grid, ...  Wave w owns a fixed slice of K for the whole launch.
-//   * Staging (once per launch, or once per K chunk when K is long): the workgroup reads
-//     the activation rows (x, gamma, beta) with coalesced 16-byte loads, one source row per
-//     wave, and writes the MFMA operand rows into LDS: per-row power-of-two scale into the
-//     fp16 range, split into 1-3 16-bit terms so the operand carries >= 22 significant bits,
-//     plus per-group sums for the bias product and the shifted LayerNorm sums (all row
-//     reductions are fixed-order wave butterflies).  Each wave then loads its slice's
-//     fragments into VGPRs; the LDS is reused for the cross-wave merge.
+//     b, b + grid, ...  Wave w owns a fixed window of K for the whole launch.
+//   * Staging: the activation rows (x, and gamma, beta with LN) become MFMA operand rows in
+//     LDS: a per-row power-of-two scale into the fp16 range, a split into 1-3 16-bit terms
+//     so that the operand carries >= 22 significant bits, per-group sums for the bias
+//     product, and the shifted LayerNorm sums.  When all of K fits (the streaming variant)
+//     each wave stages only its own window with its own loads (group reductions by DPP and
+//     the gfx950 row swaps) and needs no workgroup barrier for it; long K is staged per
+//     chunk by the whole workgroup.  Each wave then keeps its fragments in VGPRs.
 //   * Weight stream: lane (c, i) of a wave (c = lane/16, i = lane%16) reads 16 bytes of
 //     weight row i per 64-byte step (a dwordx4); 64 lanes cover 16 rows x 64 contiguous
-//     bytes per instruction.  The next tile's loads are issued before the current tile is
-//     computed.
-//   * Contraction: v_mfma_f32_16x16x32_{f16,bf16}.  B = 16 weight rows x 32 k of exactly
-//     converted codes (integers 0..255 are exact in fp16): 8-bit codes become fp16 with a
-//     byte permute under the exponent of 1024 and a packed subtract; 4-bit nibbles the same
-//     way with masks (odd nibbles sit 4 bits higher and are rescaled by an exact packed FMA).
-//     A = up to 16 operand rows x 32 k.  LayerNorm adds the rows gamma and beta, whose
-//     products give sum g w and sum b w for the fold.
+//     bytes per instruction.  Scales and biases of the wave's groups come with one aligned
+//     load per lane (even lane groups take biases, odd ones scales; a lane swap pairs them).
+//     The next tile's loads are issued before the current tile is computed.
+//   * Contraction: v_mfma_f32_16x16x32_{f16,bf16}.  B = 16 weight rows x 32 k of codes fed
+//     to the matrix cores as 16-bit subnormals: the bit pattern q is the value q * 2^-24,
+//     so a mask (4-bit) or a byte permute (8-bit) is the whole conversion.  A = up to 16
+//     operand rows x 32 k.  LayerNorm adds the rows gamma and beta, whose products give
+//     sum g w and sum b w for the fold.
 //   * Per group of 64 codes the MFMA output is a fresh partial P and acc += s * P; the bias
 //     term sum_g b * (sum of the group's operands) is one more MFMA per tile (group sums as
-//     an fp16 hi/lo operand against the exact fp16 biases).
+//     an operand row against the exact fp16 biases).
 //   * 4-bit rows hold two groups per 64-byte step; after the load, v_permlane32_swap
 //     exchanges half-registers between the lane halves so that every MFMA sees one group.
-//   * No atomics: partial sums merge in a fixed order (waves, then terms), so results are
-//     bitwise reproducible.
+//   * Split-K merge: each wave puts its partial tile into an LDS buffer; the wave that
+//     finishes the tile sums the eight partials in wave order.  The streaming variant has no
+//     barrier per tile: buffers are handed over with LDS counters (atomics on counters
+//     only), so results are bitwise reproducible.
 #pragma once
 
 #include "qlin_internal.h"
