@@ -70,6 +70,8 @@ def load():
     lib.orc_linear.restype = i32
     lib.orc_gateup.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, d, vp]
     lib.orc_gateup.restype = i32
+    lib.orc_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp]
+    lib.orc_attend.restype = i32
     _lib = lib
     return lib
 
@@ -218,3 +220,22 @@ def gateup(x, x_dtype: int, bits: int, gate, up, w_dtype: int = F16,
     if rc != 0:
         raise ValueError("oracle.gateup: unsupported arguments")
     return y
+
+
+def attend(qkv, kv, dtype: int, heads: int, head_dim: int, last: bool = False):
+    """[p1] `attend`: qkv (T, 3D) and kv (2, H, P, HD) or None as fp16/bf16 bit patterns ->
+    (out (T, D) fp64, or (1, D) with last; kv_out (2, H, P + T, HD) bit patterns)."""
+    qkv = _c(qkv, np.uint16)
+    T = qkv.shape[0]
+    D = heads * head_dim
+    if qkv.shape[1] != 3 * D:
+        raise ValueError("oracle.attend: qkv must be (T, 3 * heads * head_dim)")
+    P = 0 if kv is None else kv.shape[2]
+    if kv is not None:
+        kv = _c(kv, np.uint16)
+    out = np.empty((1 if last else T, D), np.float64)
+    kv_out = np.empty((2, heads, P + T, head_dim), np.uint16)
+    rc = load().orc_attend(_p(qkv), _p(kv), dtype, P, T, heads, head_dim, int(last), _p(out), _p(kv_out))
+    if rc != 0:
+        raise ValueError("oracle.attend: unsupported arguments")
+    return out, kv_out

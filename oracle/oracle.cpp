@@ -20,6 +20,8 @@
 //   z[t,n]   = sum_k xhat[t,k] * W[n,k]                     (fp64, k ascending)
 //   y        = [add +] [res +] act(z)      act = exact-erf GELU or none
 //   gate/up  = silu(z_gate) * z_up
+//   attend   = the band's cache with this pass's keys and values appended, and causal
+//              softmax attention of the new positions over it (at most 32 positions)
 // Everything is computed in double precision from the exact bit patterns the GPU
 // receives.  Build: g++ -O2 -std=c++17 -fPIC -shared -ffp-contract=off (no fast-math).
 //
@@ -331,6 +333,64 @@ int orc_gateup(const void* x, int x_dtype, int64_t T, int64_t K, int64_t N, int 
   weight_f64(bits, udata, w_dtype, uscales, ubiases, N, K, Wu);
   contract(a, Wu, T, K, N, zu.data());
   for (int64_t i = 0; i < T * N; ++i) y[i] = orc_silu(zg[(size_t)i]) * zu[(size_t)i];
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// attend — [p1] `_ATTEND` and `attend()`: one pass of a decoder layer's attention over a
+// short band of positions.  It appends this pass's keys and values to the band's cache
+// and runs causal softmax attention over at most 32 positions.
+//   qkv (T, 3D), D = H * HD: per new position t, the query in columns [0, D), the key in
+//       [D, 2D) and the value in [2D, 3D); head h owns columns h*HD .. h*HD + HD - 1 of each.
+//   kv (2, H, P, HD): cached keys (index 0) and values (index 1) of P earlier positions.
+//   kv_out (2, H, P + T, HD): the cache, then this pass's T rows (bit patterns copied).
+//   For new position t (absolute position P + t) and head h, over keys j = 0 .. P + t
+//   (the later positions are not visible: causal):
+//       s_j = (q . k_j) / sqrt(HD)
+//       p_j = exp(s_j - max_i s_i) / sum_i exp(s_i - max_i s_i)
+//       out[t, h*HD + d] = sum_j p_j * v_j[d]
+//   last = 1 asks for the last new position's row only (out has one row).
+// Everything in fp64 from the exact input values; out is fp64, kv_out the copied bits.
+// Returns 0, or -1 on an argument the oracle does not handle.
+// ---------------------------------------------------------------------------
+int orc_attend(const uint16_t* qkv, const uint16_t* kv, int dtype, int64_t P, int64_t T, int64_t H,
+               int64_t HD, int last, double* out, uint16_t* kv_out) {
+  if (P < 0 || T < 1 || H < 1 || HD < 1 || P + T > 32) return -1;
+  if (P > 0 && !kv) return -1;
+  const int64_t D = H * HD, L = P + T;
+  // the cache, then the new rows
+  for (int64_t i = 0; i < 2; ++i)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t j = 0; j < L; ++j)
+        for (int64_t d = 0; d < HD; ++d) {
+          const uint16_t v = j < P ? kv[((i * H + h) * P + j) * HD + d]
+                                   : qkv[(j - P) * 3 * D + (1 + i) * D + h * HD + d];
+          kv_out[((i * H + h) * L + j) * HD + d] = v;
+        }
+  auto val = [&](uint16_t b) { return dtype == 1 ? f16_to_f64(b) : bf16_to_f64(b); };
+  // key or value row of absolute position j, head h, dimension d (i = 0 key, 1 value)
+  auto kvv = [&](int64_t i, int64_t h, int64_t j, int64_t d) { return val(kv_out[((i * H + h) * L + j) * HD + d]); };
+  const double scale = 1.0 / std::sqrt((double)HD);
+  std::vector<double> s((size_t)L), pr((size_t)L);
+  for (int64_t t = last ? T - 1 : 0; t < T; ++t) {
+    const int64_t row = last ? 0 : t, pos = P + t;
+    for (int64_t h = 0; h < H; ++h) {
+      double m = -std::numeric_limits<double>::infinity();
+      for (int64_t j = 0; j <= pos; ++j) {
+        double a = 0.0;
+        for (int64_t d = 0; d < HD; ++d) a += val(qkv[t * 3 * D + h * HD + d]) * kvv(0, h, j, d);
+        s[(size_t)j] = a * scale;
+        if (s[(size_t)j] > m) m = s[(size_t)j];
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j <= pos; ++j) { pr[(size_t)j] = std::exp(s[(size_t)j] - m); z += pr[(size_t)j]; }
+      for (int64_t d = 0; d < HD; ++d) {
+        double o = 0.0;
+        for (int64_t j = 0; j <= pos; ++j) o += pr[(size_t)j] / z * kvv(1, h, j, d);
+        out[row * D + h * HD + d] = o;
+      }
+    }
+  }
   return 0;
 }
 
