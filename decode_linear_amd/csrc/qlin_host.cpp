@@ -12,11 +12,14 @@
 
 namespace {
 
-std::atomic<int64_t> g_dispatch[4];
+std::atomic<int64_t> g_dispatch[5];
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
 constexpr int64_t kMaxN = int64_t(1) << 28;
 constexpr int kMaxT = 32;
+constexpr int kMaxPositions = 32;    // attend: cached + new positions (one key per lane of a half wave)
+constexpr int kMaxHeads = 1 << 16;
+constexpr int kMaxHeadDim = 512;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -229,6 +232,42 @@ qlin_status qlin_unpack_affine(const qlin_weight* w, float* out, void* stream) {
   return QLIN_OK;
 }
 
+qlin_status qlin_attend_check(const void* qkv, const void* kv, qlin_dtype dtype, int32_t P, int32_t T,
+                              int32_t heads, int32_t head_dim, int32_t last, const void* out, qlin_dtype out_dtype,
+                              const void* kv_out) {
+  if (dtype != QLIN_F16 && dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (out_dtype != QLIN_F32 && out_dtype != QLIN_F16 && out_dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (T < 1 || P < 0 || P > kMaxPositions - T) return QLIN_ERR_SHAPE;
+  if (heads < 1 || heads > kMaxHeads) return QLIN_ERR_SHAPE;
+  if (head_dim < 16 || head_dim > kMaxHeadDim || head_dim % 16 != 0) return QLIN_ERR_SHAPE;
+  if (last != 0 && last != 1) return QLIN_ERR_ARG;
+  if (!qkv || !out || !kv_out || (P > 0 && !kv)) return QLIN_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(kv_out, 16) || (P > 0 && !aligned(kv, 16))) return QLIN_ERR_ALIGN;
+  if (!aligned(out, dtype_size(out_dtype))) return QLIN_ERR_ALIGN;
+  const size_t D = (size_t)heads * (size_t)head_dim;
+  const size_t qkv_bytes = (size_t)T * 3 * D * 2, kv_bytes = P > 0 ? 2 * (size_t)P * D * 2 : 0;
+  const size_t kv_out_bytes = 2 * (size_t)(P + T) * D * 2, out_bytes = (last ? 1 : (size_t)T) * D * dtype_size(out_dtype);
+  if (overlaps(kv_out, kv_out_bytes, qkv, qkv_bytes) || overlaps(kv_out, kv_out_bytes, kv, kv_bytes)) return QLIN_ERR_ARG;
+  if (overlaps(out, out_bytes, qkv, qkv_bytes) || overlaps(out, out_bytes, kv, kv_bytes) ||
+      overlaps(out, out_bytes, kv_out, kv_out_bytes))
+    return QLIN_ERR_ARG;
+  return QLIN_OK;
+}
+
+qlin_status qlin_attend(const void* qkv, const void* kv, qlin_dtype dtype, int32_t P, int32_t T, int32_t heads,
+                        int32_t head_dim, int32_t last, void* out, qlin_dtype out_dtype, void* kv_out, void* stream) {
+  const qlin_status st = qlin_attend_check(qkv, kv, dtype, P, T, heads, head_dim, last, out, out_dtype, kv_out);
+  if (st != QLIN_OK) return st;
+  qlin::AttendParams a{};
+  a.qkv = qkv; a.kv = P > 0 ? kv : nullptr; a.out = out; a.kv_out = kv_out;
+  a.dtype = dtype; a.out_dtype = out_dtype;
+  a.H = heads; a.HD = head_dim; a.P = P; a.T = T; a.last = last;
+  a.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  if (qlin::launch_attend(a, static_cast<hipStream_t>(stream)) != hipSuccess) return QLIN_ERR_HIP;
+  g_dispatch[4].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
 qlin_status qlin_chain_create(const qlin_pass* passes, int32_t n_passes, qlin_dtype x_dtype, qlin_dtype y_dtype,
                               void* capture_stream, qlin_chain** out) {
   if (!out) return QLIN_ERR_NULL;
@@ -290,7 +329,7 @@ void qlin_chain_destroy(qlin_chain* chain) {
 }
 
 int64_t qlin_dispatch_count(int32_t which) {
-  if (which < 0 || which > 3) return -1;
+  if (which < 0 || which > 4) return -1;
   return g_dispatch[which].load(std::memory_order_relaxed);
 }
 

@@ -52,6 +52,20 @@ hipError_t launch_fused_bf16(const LinParams& p, int mt, int grid, size_t lds, h
 int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K);
 size_t fused_lds_bytes(int bits, int rows, int chunk_steps, long K, int mt);
 
+// Arguments of one attend launch (cache append + causal attention, <= 32 positions).
+struct AttendParams {
+  const void* qkv;        // (T, 3 * H * HD), dtype
+  const void* kv;         // (2, H, P, HD), dtype; null when P == 0
+  void* out;              // (T, H * HD) or (1, H * HD) with last, out_dtype
+  void* kv_out;           // (2, H, P + T, HD), dtype
+  int dtype;              // 1 fp16, 2 bf16
+  int out_dtype;          // 0 fp32, 1 fp16, 2 bf16
+  int H, HD, P, T;
+  int last;               // 1: only the last new position's output row
+  float scale;            // 1 / sqrt(HD), rounded to fp32
+};
+hipError_t launch_attend(const AttendParams& a, hipStream_t s);
+
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bits, uint32_t* codes, uint16_t* scales,
                        uint16_t* biases, int32_t* flag, hipStream_t s);
 hipError_t launch_unpack(const void* data, const uint16_t* scales, const uint16_t* biases, int bits,

@@ -3,7 +3,8 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_check, qlin_status_string, qlin_dispatch_count, and the chain calls
+qlin_attend, qlin_check, qlin_attend_check, qlin_status_string, qlin_dispatch_count,
+and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
 
 There is no fallback: if libqlin.so is missing or a call fails, this raises.
@@ -68,6 +69,8 @@ def lib():
     L.qlin_pack_affine.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp]
     L.qlin_unpack_affine.argtypes = [W, vp, vp]
     L.qlin_check.argtypes = [vp, i32, i32, W, W, Ln, i32, vp, vp, vp, i32]
+    L.qlin_attend.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp]
+    L.qlin_attend_check.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp]
     L.qlin_chain_create.argtypes = [ctypes.POINTER(_Pass), i32, i32, i32, vp, ctypes.POINTER(vp)]
     L.qlin_chain_launch.argtypes = [vp, vp]
     L.qlin_chain_passes.argtypes = [vp]
@@ -78,7 +81,7 @@ def lib():
     L.qlin_status_string.argtypes = [i32]
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
-                 "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes"):
+                 "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -176,6 +179,36 @@ def qlin_gateup_swiglu(x: torch.Tensor, gate: QWeight, up: QWeight, ln=None, out
                                   None if lnc is None else ctypes.byref(lnc), _ptr(out), _dtype(out), _stream(stream))
     _check(st, "qlin_gateup_swiglu")
     return out
+
+
+def qlin_attend(qkv: torch.Tensor, kv: Optional[torch.Tensor], heads: int, head_dim: int, last: bool = False,
+                out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                kv_out: Optional[torch.Tensor] = None, stream=None):
+    """(out, kv_out) of one attention pass: kv_out (2, H, P + T, HD) = the cache with this
+    pass's keys and values appended; out (T, D), or (1, D) with last, = causal softmax
+    attention of the new positions.  qkv (T, 3D); kv (2, H, P, HD) or None."""
+    T = qkv.shape[0]
+    D = heads * head_dim
+    P = 0 if kv is None else kv.shape[2]
+    # shapes are checked here because the C ABI sees only pointers and sizes
+    if qkv.dim() != 2 or qkv.shape[1] != 3 * D or not qkv.is_contiguous():
+        raise ValueError("qlin_attend: qkv must be a contiguous (T, 3 * heads * head_dim) tensor")
+    if kv is not None and (tuple(kv.shape) != (2, heads, P, head_dim) or not kv.is_contiguous()
+                           or kv.dtype != qkv.dtype):
+        raise ValueError("qlin_attend: kv must be a contiguous (2, heads, P, head_dim) tensor of qkv's dtype")
+    rows = 1 if last else T
+    if out is None:
+        out = torch.empty((rows, D), dtype=out_dtype or qkv.dtype, device=qkv.device)
+    elif tuple(out.shape) != (rows, D) or not out.is_contiguous():
+        raise ValueError("qlin_attend: out must be a contiguous (T or 1, heads * head_dim) tensor")
+    if kv_out is None:
+        kv_out = torch.empty((2, heads, P + T, head_dim), dtype=qkv.dtype, device=qkv.device)
+    elif tuple(kv_out.shape) != (2, heads, P + T, head_dim) or not kv_out.is_contiguous() or kv_out.dtype != qkv.dtype:
+        raise ValueError("qlin_attend: kv_out must be a contiguous (2, heads, P + T, head_dim) tensor of qkv's dtype")
+    st = lib().qlin_attend(_ptr(qkv), _ptr(kv), _dtype(qkv), P, T, heads, head_dim, int(bool(last)), _ptr(out),
+                           _dtype(out), _ptr(kv_out), _stream(stream))
+    _check(st, "qlin_attend")
+    return out, kv_out
 
 
 def qlin_pack_affine(w: torch.Tensor, bits: int, flag: Optional[torch.Tensor] = None, stream=None) -> QWeight:

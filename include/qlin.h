@@ -169,8 +169,36 @@ int32_t qlin_chain_passes(const qlin_chain* chain);
 /* Release the graph and its host memory.  NULL is ignored. */
 void qlin_chain_destroy(qlin_chain* chain);
 
+/* Attention of one decoder-layer pass over a short band of positions ([p1] maya-mac
+ * src/maya_mac/mlx_kernels.py, `_ATTEND` and `attend()`): append this pass's keys and
+ * values to the band's cache, then causal softmax attention of the new positions.
+ *   qkv      (T, 3D) of dtype (QLIN_F16 or QLIN_BF16), D = heads * head_dim: per new
+ *            position the query (columns [0, D)), key ([D, 2D)) and value ([2D, 3D)) of
+ *            every head; head h owns head_dim consecutive columns of each.  16-byte aligned.
+ *   kv       (2, heads, P, head_dim) of dtype: the cached keys (index 0) and values (1) of
+ *            the P earlier positions; may be NULL when P == 0.  16-byte aligned.
+ *   P, T     0 <= P, 1 <= T, P + T <= 32.
+ *   heads    1 .. 65536;  head_dim a multiple of 16 in [16, 512].
+ *   last     0: out is (T, D), one row per new position;  1: out is (1, D), the last new
+ *            position's row only.
+ *   out      of out_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16): row t, columns h*head_dim + d
+ *            hold sum_{j <= P + t} p_j v_j[d], p = softmax over j of (q_t . k_j) / sqrt(head_dim)
+ *            (position P + t sees keys 0 .. P + t only), computed in fp32 and rounded once.
+ *   kv_out   (2, heads, P + T, head_dim) of dtype: the cache, then this pass's T rows (bit
+ *            patterns copied).  It must not overlap qkv or kv; out must not overlap any input
+ *            or kv_out.
+ * Returns QLIN_OK once the work is enqueued; argument errors as for qlin_linear. */
+qlin_status qlin_attend(const void* qkv, const void* kv, qlin_dtype dtype, int32_t P, int32_t T, int32_t heads,
+                        int32_t head_dim, int32_t last, void* out, qlin_dtype out_dtype, void* kv_out, void* stream);
+
+/* Validation only: what qlin_attend would return for these arguments, with nothing
+ * enqueued.  Needs no GPU. */
+qlin_status qlin_attend_check(const void* qkv, const void* kv, qlin_dtype dtype, int32_t P, int32_t T,
+                              int32_t heads, int32_t head_dim, int32_t last, const void* out, qlin_dtype out_dtype,
+                              const void* kv_out);
+
 /* Number of kernels this library has enqueued in this process, by entry point:
- * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack (a test can assert a kernel ran). */
+ * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend (a test can assert a kernel ran). */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Static description of a status code. */

@@ -23,6 +23,9 @@ N(0, 1/K) whose 1/K is the variance):
   4  gate+up SwiGLU, M=4, K=4096, N=14336 each; x bf16 N(0,1); gate/up 4-bit from N(0,0.02)
   5  124 dependent LN + linear passes, K=N=1024, T_p = 1 + (p mod 8); buffers B_0..B_124
      (8, 1024) bf16 N(0,1); per pass gamma, beta as in 2, W_p 8-bit from N(0,0.02)
+  6  attend over the depth decoder's band: D = 1024 as 16 heads of 64, P = 24 cached and
+     T = 8 new positions (the 32-position cap); qkv (T, 3D) and the cache (2, 16, 24, 64)
+     bf16 N(0,1), so that scores q.k / sqrt(64) are about N(0,1)
 """
 from __future__ import annotations
 
@@ -34,7 +37,7 @@ import numpy as np
 F32, F16, BF16 = 0, 1, 2
 NP_CODES = {F32: np.float32}
 
-TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7}
+TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9}
 CHAIN_PASSES = 124
 CHAIN_K = CHAIN_N = 1024
 CHAIN_TMAX = 8
@@ -197,3 +200,33 @@ def random_gateup(s: int, T: int, K: int, N: int, bits: int, x_dtype: int = BF16
         u = draw(c, 0, "up", (N, K), 0.0, 0.02, F32)
     return GateUpCase(f"gu{s}-T{T}-K{K}-N{N}-b{bits}", T, K, N, x_dtype, bits, y_dtype,
                       x=draw(c, 0, "x", (T, K), 0.0, 1.0, x_dtype), gate=g, up=u, **kw)
+
+
+@dataclass
+class AttendCase:
+    name: str
+    H: int
+    HD: int
+    P: int
+    T: int
+    dtype: int
+    qkv: np.ndarray                  # (T, 3 H HD) bit patterns
+    kv: Optional[np.ndarray]         # (2, H, P, HD) bit patterns, None when P == 0
+
+
+ATTEND_H, ATTEND_HD, ATTEND_P, ATTEND_T = 16, 64, 24, 8
+
+
+def attend_case(s: int, H: int, HD: int, P: int, T: int, dtype: int = BF16, c: Optional[int] = None) -> AttendCase:
+    """qkv and the cache drawn N(0, 1) in dtype (workload 6 with its own shapes; parity cases
+    use stream ids offset by s)."""
+    c = 100 + s if c is None else c
+    kv = draw(c, 0, "kv", (2, H, P, HD), 0.0, 1.0, dtype) if P > 0 else None
+    return AttendCase(f"att{s}-H{H}-HD{HD}-P{P}-T{T}", H, HD, P, T, dtype,
+                      qkv=draw(c, 0, "qkv", (T, 3 * H * HD), 0.0, 1.0, dtype), kv=kv)
+
+
+def attend_workload() -> AttendCase:
+    case = attend_case(0, ATTEND_H, ATTEND_HD, ATTEND_P, ATTEND_T, BF16, c=6)
+    case.name = f"attend-H{ATTEND_H}-HD{ATTEND_HD}-P{ATTEND_P}-T{ATTEND_T}"
+    return case

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
-                 "qlin_dispatch_count"):
+                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check"):
         assert must in names
 
 
@@ -164,5 +164,57 @@ def test_chain_argument_errors(q):
 
 
 def test_dispatch_counter_range(q):
-    assert q.qlin_dispatch_count(4) == -1
+    assert q.qlin_dispatch_count(5) == -1
+    assert q.qlin_dispatch_count(-1) == -1
     assert q.qlin_dispatch_count(0) >= 0
+    assert q.qlin_dispatch_count(4) >= 0
+
+
+# attend: qkv, kv, out, kv_out at fake, 16-byte aligned addresses far apart
+QKV, KV, AO, KVO = (0x1000000 * i for i in range(1, 5))
+
+
+def _att(q, qkv=QKV, kv=KV, dtype=None, P=24, T=8, H=16, HD=64, last=0, out=AO, out_dtype=None, kv_out=KVO):
+    dtype = q.QLIN_BF16 if dtype is None else dtype
+    out_dtype = q.QLIN_BF16 if out_dtype is None else out_dtype
+    return q.lib().qlin_attend_check(qkv, kv, dtype, P, T, H, HD, last, out, out_dtype, kv_out)
+
+
+def test_attend_valid_calls(q):
+    assert _att(q) == 0
+    assert _att(q, P=0, kv=None, T=32) == 0
+    assert _att(q, P=31, T=1, last=1, out_dtype=q.QLIN_F32) == 0
+    assert _att(q, dtype=q.QLIN_F16, out_dtype=q.QLIN_F16, H=1, HD=512) == 0
+
+
+@pytest.mark.parametrize("P,T", [(0, 0), (-1, 4), (30, 3), (0, 33), (32, 1)])
+def test_attend_bad_positions(q, P, T):
+    assert _att(q, P=P, T=T) == -2
+
+
+@pytest.mark.parametrize("H,HD", [(0, 64), (16, 8), (16, 24), (16, 0), (1, 528), (70000, 16)])
+def test_attend_bad_heads(q, H, HD):
+    assert _att(q, H=H, HD=HD) == -2
+
+
+def test_attend_dtypes_nulls_alignment_overlap(q):
+    assert _att(q, dtype=q.QLIN_F32) == -3
+    assert _att(q, out_dtype=7) == -3
+    assert _att(q, last=2) == -7
+    assert _att(q, qkv=None) == -1
+    assert _att(q, kv=None) == -1              # P > 0 needs the cache
+    assert _att(q, out=None) == -1
+    assert _att(q, kv_out=None) == -1
+    assert _att(q, qkv=QKV + 8) == -5
+    assert _att(q, kv_out=KVO + 8) == -5
+    assert _att(q, out=AO + 1) == -5
+    assert _att(q, out=AO + 2, out_dtype=q.QLIN_F32) == -5
+    assert _att(q, kv_out=QKV + 16) == -7
+    assert _att(q, kv_out=KV + 64) == -7
+    assert _att(q, out=KVO) == -7
+    assert _att(q, out=QKV + 32) == -7
+
+
+def test_invalid_attend_call_returns_before_any_hip_call(q):
+    st = q.lib().qlin_attend(QKV, KV, q.QLIN_BF16, 30, 3, 16, 64, 0, AO, q.QLIN_BF16, KVO, None)
+    assert st == -2
