@@ -8,9 +8,16 @@ The headline workload is the largest single call, the 4-bit SwiGLU gate+up proje
 Weight bytes per call are the algorithmic weight stream: codes + scales + biases of both
 projections, each byte read once (activations and outputs are reported separately).
 Weights rotate over enough copies to total >= 1 GiB, so the 256 MB Infinity Cache cannot
-serve them; everything is resident in HBM before the timed region.  Time comes from HIP
-events recorded on the stream the kernels are launched on, bracketing the timed steps
-(warmup steps first), with device synchronization on both sides.
+serve them; everything is resident in HBM before the timed region.  The timed steps are
+captured into one HIP graph (after eager warmup steps and one untimed replay) and replayed
+once, bracketed by HIP events on the stream the graph runs on, with device synchronization
+on both sides: that is the GPU time of the calls, without the ~10 us of host work a Python
+call costs (which would otherwise bound every call under ~10 us).  The same steps launched
+eagerly from Python are reported too (us_per_call_eager).
+
+read_ceiling: the library's plain streaming read (qlin_stream_read, 16-byte loads and
+nothing else) over the same number of bytes, rotated and timed the same way: the rate a
+pure read reaches on this device, next to which the fused call's rate can be read.
 
 Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
 with 32 rows) and the 124-pass LN+linear chain (hipGraph replay vs eager launches), and a
@@ -71,6 +78,45 @@ def _time_calls(fn, n_copies, steps, warmup):
     return start.elapsed_time(end)
 
 
+def _time_graph(fn, n_copies, steps, warmup):
+    """Warmup calls eagerly, then exactly `steps` calls (cycling over the weight copies)
+    captured into one HIP graph; one untimed replay uploads it, one timed replay runs the
+    steps back to back, bracketed by events on the stream the graph runs on.  Returns ms
+    of the timed replay (GPU time of the calls, without per-call host overhead)."""
+    torch = _torch()
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn((warmup + i) % n_copies)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end)
+
+
+def read_ceiling(nbytes, steps, warmup):
+    """The device's streaming-read rate over nbytes (qlin_stream_read: 16-byte loads, no
+    other work), rotated over >= 1 GiB of buffers and timed like the fused calls."""
+    from decode_linear_amd import qlin_stream_read
+    torch = _torch()
+    nbytes = -(-nbytes // 16) * 16
+    n_copies = max(2, -(-ROTATE_BYTES // nbytes))
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_copies)]
+    part = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    ms = _time_graph(lambda i: qlin_stream_read(bufs[i], part), n_copies, steps, warmup)
+    us = ms * 1e3 / steps
+    del bufs
+    return dict(bytes=nbytes, copies=n_copies, us=us, gbs=nbytes / (us * 1e-6) / 1e9)
+
+
 def _rotated(make, nbytes):
     """Enough independent copies of a weight set to total >= ROTATE_BYTES."""
     n = max(2, -(-ROTATE_BYTES // nbytes))
@@ -120,11 +166,11 @@ def bench_swiglu(steps, warmup):
         g, u = weights[i]
         qlin_gateup_swiglu(x, g, u, out=y)
 
-    ms = _time_calls(step, n_copies, steps, warmup)
-    us = ms * 1e3 / steps
+    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
     other = case.x.size * 2 + y.numel() * 2
     return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=4, weight_bytes=wbytes, other_bytes=other,
-                copies=n_copies, us=us, gbs=wbytes / (us * 1e-6) / 1e9)
+                copies=n_copies, us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
 
 
 def bench_linear(c, steps, warmup):
@@ -148,10 +194,10 @@ def bench_linear(c, steps, warmup):
     def step(i):
         qlin_linear(x, weights[i], ln=ln, act=case.act, residual=res, out=y)
 
-    ms = _time_calls(step, n_copies, steps, warmup)
-    us = ms * 1e3 / steps
+    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
     return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=case.bits, weight_bytes=wbytes, copies=n_copies,
-                us=us, gbs=wbytes / (us * 1e-6) / 1e9)
+                us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
 
 
 def bench_chain(replays, warmup):
@@ -272,6 +318,7 @@ def main():
         copy_probe(a.copy_probe)
         return
     main_r = bench_swiglu(a.steps, a.warmup)
+    ceil_r = read_ceiling(main_r["weight_bytes"], a.steps, a.warmup)
     extra = {}
     if not a.only_main:
         for c in (1, 2, 3):
@@ -299,7 +346,11 @@ def main():
                    "weights": "4-bit affine, group 64, fp16 scale/bias", "activations": "bf16",
                    "weight_bytes_per_call": main_r["weight_bytes"], "rotation_copies": main_r["copies"]},
         "us_per_call": round(us, 3),
+        "us_per_call_eager": round(main_r["us_eager"], 3),
         "pct_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+        "read_ceiling": {"gbs": round(ceil_r["gbs"], 2), "us": round(ceil_r["us"], 3), "bytes": ceil_r["bytes"],
+                         "frac_of_peak": round(ceil_r["gbs"] / PEAK_HBM_GBS, 4),
+                         "fused_frac_of_ceiling": round(achieved / ceil_r["gbs"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic()},
     }

@@ -12,7 +12,7 @@
 
 namespace {
 
-std::atomic<int64_t> g_dispatch[5];
+std::atomic<int64_t> g_dispatch[6];
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
 constexpr int64_t kMaxN = int64_t(1) << 28;
@@ -328,8 +328,21 @@ void qlin_chain_destroy(qlin_chain* chain) {
   delete chain;
 }
 
+qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream) {
+  if (!buf || !partial) return QLIN_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return QLIN_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || (reinterpret_cast<uintptr_t>(partial) & 3u) != 0)
+    return QLIN_ERR_ALIGN;
+  const int cus = cu_count();
+  const int grid = cus < QLIN_STREAM_READ_BLOCKS ? cus : QLIN_STREAM_READ_BLOCKS;
+  if (qlin::launch_stream_read(buf, bytes, partial, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return QLIN_ERR_HIP;
+  g_dispatch[5].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
 int64_t qlin_dispatch_count(int32_t which) {
-  if (which < 0 || which > 4) return -1;
+  if (which < 0 || which > 5) return -1;
   return g_dispatch[which].load(std::memory_order_relaxed);
 }
 

@@ -71,4 +71,8 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bits, uint32_t*
 hipError_t launch_unpack(const void* data, const uint16_t* scales, const uint16_t* biases, int bits,
                          int dtype, int64_t N, int64_t K, float* out, hipStream_t s);
 
+// Plain 16-byte streaming read of `bytes` (a multiple of 16) at buf; block b writes the XOR
+// fold of the words it read to partial[b] (grid blocks of 512 threads).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int grid, hipStream_t s);
+
 }  // namespace qlin

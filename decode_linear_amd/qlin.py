@@ -3,7 +3,8 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_attend, qlin_check, qlin_attend_check, qlin_status_string, qlin_dispatch_count,
+qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
+qlin_dispatch_count,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
 
@@ -76,12 +77,14 @@ def lib():
     L.qlin_chain_passes.argtypes = [vp]
     L.qlin_chain_destroy.argtypes = [vp]
     L.qlin_chain_destroy.restype = None
+    L.qlin_stream_read.argtypes = [vp, i64, vp, vp]
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
-                 "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes"):
+                 "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
+                 "qlin_stream_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -279,3 +282,20 @@ class QlinChain:
             self.close()
         except Exception:
             pass
+
+
+STREAM_READ_BLOCKS = 1024
+
+
+def qlin_stream_read(buf: torch.Tensor, partial: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One plain 16-byte streaming read of buf (the device's read ceiling); returns the
+    (STREAM_READ_BLOCKS,) int32 tensor of per-block XOR folds (entries past the launch's
+    blocks are left as they were)."""
+    if partial is None:
+        partial = torch.zeros(STREAM_READ_BLOCKS, dtype=torch.int32, device=buf.device)
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    st = lib().qlin_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partial), _stream(stream))
+    if st != 0:
+        raise QlinError(st, "qlin_stream_read")
+    return partial

@@ -197,8 +197,25 @@ qlin_status qlin_attend_check(const void* qkv, const void* kv, qlin_dtype dtype,
                               int32_t heads, int32_t head_dim, int32_t last, const void* out, qlin_dtype out_dtype,
                               const void* kv_out);
 
+/* ---- measurement aid ----------------------------------------------------------------
+ * qlin_stream_read: the device's streaming-read ceiling for the weight stream's access (the
+ * "HBM bandwidth" the pages' 8-bit-versus-fp16 timing comparison of the maya-mac depth
+ * decoder kernels turns on, section "Custom Metal kernels for the depth decoder"): one
+ * plain pass of 16-byte loads over a buffer, no other work.  Timing it over the same bytes
+ * as a fused call gives the rate a pure read reaches on this device.
+ *   buf      device pointer, 16-byte aligned; bytes a positive multiple of 16.  Read only.
+ *   partial  device array of QLIN_STREAM_READ_BLOCKS uint32 (4-byte aligned), owned by the
+ *            caller: block b of the launch writes the XOR of the 32-bit words it read to
+ *            partial[b]; blocks past min(compute units, QLIN_STREAM_READ_BLOCKS) write
+ *            nothing.  The XOR of all written entries is the XOR of every word of buf.
+ * Errors: QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN before any HIP call; QLIN_ERR_HIP
+ * on a launch failure. */
+#define QLIN_STREAM_READ_BLOCKS 1024
+qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream);
+
 /* Number of kernels this library has enqueued in this process, by entry point:
- * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend (a test can assert a kernel ran). */
+ * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read (a test can
+ * assert a kernel ran). */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Static description of a status code. */

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
-                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check"):
+                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read"):
         assert must in names
 
 
@@ -164,10 +164,10 @@ def test_chain_argument_errors(q):
 
 
 def test_dispatch_counter_range(q):
-    assert q.qlin_dispatch_count(5) == -1
+    assert q.qlin_dispatch_count(6) == -1
     assert q.qlin_dispatch_count(-1) == -1
     assert q.qlin_dispatch_count(0) >= 0
-    assert q.qlin_dispatch_count(4) >= 0
+    assert q.qlin_dispatch_count(5) >= 0
 
 
 # attend: qkv, kv, out, kv_out at fake, 16-byte aligned addresses far apart
@@ -218,3 +218,13 @@ def test_attend_dtypes_nulls_alignment_overlap(q):
 def test_invalid_attend_call_returns_before_any_hip_call(q):
     st = q.lib().qlin_attend(QKV, KV, q.QLIN_BF16, 30, 3, 16, 64, 0, AO, q.QLIN_BF16, KVO, None)
     assert st == -2
+
+
+def test_stream_read_validation(q):
+    f = q.lib().qlin_stream_read
+    assert f(None, 1024, AO, None) == -1
+    assert f(QKV, 1024, None, None) == -1
+    assert f(QKV, 0, AO, None) == -2
+    assert f(QKV, 1000, AO, None) == -2       # not a multiple of 16
+    assert f(QKV + 8, 1024, AO, None) == -5
+    assert f(QKV, 1024, AO + 2, None) == -5
