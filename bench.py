@@ -20,8 +20,10 @@ nothing else) over the same number of bytes, rotated and timed the same way: the
 pure read reaches on this device, next to which the fused call's rate can be read.
 
 Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
-with 32 rows) and the 124-pass LN+linear chain (hipGraph replay vs eager launches), and a
-CPU baseline: the fp64 oracle timed on the host on a bounded sample of the workload.
+with 32 rows), the 124-pass LN+linear chain (hipGraph replay vs eager launches), the whole
+MLP around the headline projection (qlin_mlp: gate/up then down with the residual), one
+attend pass, and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
+the workload.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--only-main]
 """
@@ -200,6 +202,54 @@ def bench_linear(c, steps, warmup):
                 us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
 
 
+def bench_mlp(steps, warmup):
+    """The MLP around the headline workload (qlin_mlp: gate/up 4-bit K=4096 I=14336, then the
+    4-bit down projection Hout=4096 with the residual), weights rotated like the others."""
+    import synth
+    from decode_linear_amd import qlin_mlp
+    torch = _torch()
+    case = synth.mlp_workload()
+    g0, u0, d0 = _pack(case.gate, 4), _pack(case.up, 4), _pack(case.down, 4)
+    del case.gate, case.up, case.down
+    wbytes = g0.nbytes + u0.nbytes + d0.nbytes
+    n_copies = max(2, -(-ROTATE_BYTES // wbytes))
+    weights = [(g0, u0, d0)] + [tuple(_clone_q(q) for q in (g0, u0, d0)) for _ in range(n_copies - 1)]
+    x = _dev(case.x, case.x_dtype)
+    res = _dev(case.res, case.x_dtype)
+    h = torch.empty((case.T, case.I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((case.T, case.Hout), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        qlin_mlp(x, *weights[i], residual=res, h=h, out=y)
+
+    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
+    return dict(name=case.name, T=case.T, K=case.K, I=case.I, Hout=case.Hout, bits=4, weight_bytes=wbytes,
+                copies=n_copies, dispatches=2, us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
+
+
+def bench_attend(steps, warmup):
+    """One attend pass of the depth decoder's band (16 heads of 64, 24 cached + 8 new
+    positions, bf16): ~300 KB per call, so it is bound by latency and stays cache-resident;
+    bytes are qkv + cache read, extended cache + output written."""
+    import synth
+    from decode_linear_amd import qlin_attend
+    torch = _torch()
+    case = synth.attend_workload()
+    qkv, kv = _dev(case.qkv, case.dtype), _dev(case.kv, case.dtype)
+    D = case.H * case.HD
+    out = torch.empty((case.T, D), dtype=torch.bfloat16, device="cuda")
+    kv_out = torch.empty((2, case.H, case.P + case.T, case.HD), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        qlin_attend(qkv, kv, case.H, case.HD, out=out, kv_out=kv_out)
+
+    us = _time_graph(step, 1, steps, warmup) * 1e3 / steps
+    nbytes = (qkv.numel() + kv.numel() + kv_out.numel() + out.numel()) * 2
+    return dict(name=case.name, H=case.H, HD=case.HD, P=case.P, T=case.T, bytes=nbytes, us=us,
+                gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
+
+
 def bench_chain(replays, warmup):
     """124 dependent LN + linear passes (8-bit, K=N=1024, T = 1 + p mod 8): graph replay
     and eager launches, rotated over >= 1 GiB of chain copies."""
@@ -327,6 +377,9 @@ def main():
             extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
         ch = bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))
         extra[ch["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ch.items() if k != "name"}
+        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup)):
+            extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
+            extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
     us = main_r["us"]
     achieved = main_r["weight_bytes"] / (us * 1e-6) / 1e9
     line = {

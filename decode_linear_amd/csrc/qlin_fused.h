@@ -25,13 +25,15 @@
 //     load per lane (even lane groups take biases, odd ones scales; a lane swap pairs them).
 //     The next tile's loads are issued before the current tile is computed.
 //   * Contraction: v_mfma_f32_16x16x32_{f16,bf16}.  B = 16 weight rows x 32 k of codes fed
-//     to the matrix cores as 16-bit subnormals: the bit pattern q is the value q * 2^-24,
-//     so a mask (4-bit) or a byte permute (8-bit) is the whole conversion.  A = up to 16
-//     operand rows x 32 k.  LayerNorm adds the rows gamma and beta, whose products give
-//     sum g w and sum b w for the fold.
-//   * Per group of 64 codes the MFMA output is a fresh partial P and acc += s * P; the bias
-//     term sum_g b * (sum of the group's operands) is one more MFMA per tile (group sums as
-//     an operand row against the exact fp16 biases).
+//     to the matrix cores as the normal fp16 values 1 + q 2^-bits (the code in the top
+//     mantissa bits of 1.0: one shift and one and-or per register), A = up to 16 operand
+//     rows x 32 k.  LayerNorm adds the rows gamma and beta, whose products give sum g w and
+//     sum b w for the fold.
+//   * Per group of 64 codes the MFMA output is a fresh partial P' = G + 2^-bits P, where
+//     P = sum q a and G = sum a (the group's operands), and acc += s * P'.  Two more MFMAs
+//     per tile take the group sums G as an operand row against the exact fp16 biases and
+//     scales: sum_g b G and sum_g s G.  Then s P + b G = 2^bits (s P' - s G) + b G, and the
+//     cancellation of s G costs about one bit.
 //   * 4-bit rows hold two groups per 64-byte step; after the load, v_permlane32_swap
 //     exchanges half-registers between the lane halves so that every MFMA sees one group.
 //   * Split-K merge: each wave puts its partial tile into an LDS buffer; the wave that
@@ -92,37 +94,63 @@ __device__ __forceinline__ void load8(const void* base, int dtype, long idx, flo
 }
 
 // ---- code conversion to fp16 operand pairs ------------------------------------------
-// Codes enter the MFMA as fp16 subnormals: the bit pattern q (q < 1024) is the value
-// q * 2^-24 exactly, and the matrix cores take fp16 subnormal inputs exactly.  So a mask
-// or a byte permute is the whole conversion; the 2^-24 is undone with the row scale.
-// 4-bit: nibbles 0 and 4 of r (bits 0-3, 16-19) give n * 2^-24; nibbles 1 and 5 (bits 4-7,
-// 20-23) give 16 n * 2^-24, and the activations of those slots are staged divided by 16.
-template <int BITS>
+// A code q of b bits enters the MFMA as the normal fp16 value 1 + q 2^-b: the code in the
+// top b bits of the 10-bit mantissa of 1.0 (0x3C00).  Entered as the subnormal q 2^-24
+// instead (the bare bit pattern), the matrix cores lose precision: against exact fp64 dot
+// products, a 16x16x32 f16 MFMA of subnormal codes and activations spread over 2^-5..2^15
+// was off by up to 2^-14.4 of sum |product|, against 2^-21.9 for the same codes as normal
+// values (and no error at all for activations within one binade).
+// 4-bit: nibble i of r (bits 4i .. 4i+3) moves to bits 6..9 of a half; halves hold nibbles
+// (0, 4), (1, 5), (2, 6), (3, 7).  8-bit: byte i moves to bits 2..9 of a half.
+// The normal form has its own cost: the partial carries the offset G, which is removed
+// again in fp32, so rows whose operands share a large common part (LayerNorm rows, shifted
+// by x[t, 0] and multiplied by gamma ~ 1) lose more than subnormal codes lose.  NC selects
+// the normal form (4-bit calls without LayerNorm); otherwise codes enter as subnormals:
+// the bit pattern q (q < 1024) is the value q * 2^-24, a mask or a byte permute is the
+// whole conversion, and 4-bit high-nibble slots (value 16 q * 2^-24) carry their
+// activation divided by 16.
+template <int BITS, bool NC>
 __device__ __forceinline__ u4_t convert_codes(const u4_t d, int q) {
   u4_t b;
-  if constexpr (BITS == 8) {
+  if constexpr (!NC && BITS == 8) {
     const uint32_t da = d[2 * q], db = d[2 * q + 1];
     b[0] = __builtin_amdgcn_perm(0u, da, 0x0C010C00u);   // bytes 0, 1 -> low byte of each half
     b[1] = __builtin_amdgcn_perm(0u, da, 0x0C030C02u);   // bytes 2, 3
     b[2] = __builtin_amdgcn_perm(0u, db, 0x0C010C00u);
     b[3] = __builtin_amdgcn_perm(0u, db, 0x0C030C02u);
-  } else if constexpr (BITS == 4) {
+  } else if constexpr (!NC && BITS == 4) {
     const uint32_t r = d[(q & 1) * 2 + (q >> 1)];
     b[0] = r & 0x000F000Fu;
     b[1] = r & 0x00F000F0u;
     b[2] = (r >> 8) & 0x000F000Fu;
     b[3] = (r >> 8) & 0x00F000F0u;
+  } else if constexpr (BITS == 8) {
+    const uint32_t da = d[2 * q], db = d[2 * q + 1];
+    // bytes 0, 1 (2, 3) to the low byte of each half, then two places up under 1.0
+    b[0] = (__builtin_amdgcn_perm(0u, da, 0x0C010C00u) << 2) | 0x3C003C00u;
+    b[1] = (__builtin_amdgcn_perm(0u, da, 0x0C030C02u) << 2) | 0x3C003C00u;
+    b[2] = (__builtin_amdgcn_perm(0u, db, 0x0C010C00u) << 2) | 0x3C003C00u;
+    b[3] = (__builtin_amdgcn_perm(0u, db, 0x0C030C02u) << 2) | 0x3C003C00u;
+  } else if constexpr (BITS == 4) {
+    const uint32_t r = d[(q & 1) * 2 + (q >> 1)];
+    b[0] = ((r << 6) & 0x03C003C0u) | 0x3C003C00u;
+    b[1] = ((r << 2) & 0x03C003C0u) | 0x3C003C00u;
+    b[2] = ((r >> 2) & 0x03C003C0u) | 0x3C003C00u;
+    b[3] = ((r >> 6) & 0x03C003C0u) | 0x3C003C00u;
   } else {
     b = d;
   }
   return b;
 }
-// Scale of the quantized MFMA partials: codes enter as q * 2^-24.
-constexpr float kCodeScale = 0x1p-24f;
-// 4-bit operand slots fed by the high nibble of a byte (value 16 q * 2^-24) carry their
-// activation divided by 16.
-template <int BITS> __device__ __forceinline__ constexpr bool slot_hi_nibble(int j) {
-  return BITS == 4 && ((j >> 1) & 1) != 0;
+// The unit of a quantized MFMA partial: 2^-bits for normal codes (the partial of a group is
+// G + 2^-bits P), 2^-24 for subnormal codes.
+template <int BITS, bool NC> __host__ __device__ constexpr float code_mul() {
+  return NC ? (BITS == 4 ? 16.0f : 256.0f) : 0x1p24f;
+}
+// 4-bit subnormal-code operand slots fed by the high nibble of a byte (value 16 q 2^-24)
+// carry their activation divided by 16.
+template <int BITS, bool NC> __device__ __forceinline__ constexpr bool slot_hi_nibble(int j) {
+  return BITS == 4 && !NC && ((j >> 1) & 1) != 0;
 }
 
 template <bool BF16OP>
@@ -262,7 +290,7 @@ __device__ __forceinline__ void unpack8(const u4_t raw, int dtype, float v[8]) {
 // NS > 0: the streaming variant, where every wave runs exactly NS steps (a window of the row
 // that may overlap the previous wave's; the overlapped steps are masked).  NS == 0: the
 // chunked variant, up to MAXS steps per wave and chunk.
-template <int BITS, bool BF16OP, int MT, int NS = 0>
+template <int BITS, bool BF16OP, int MT, int NS = 0, bool NC = false>
 struct Fused {
   static constexpr int NM = Fmt<BITS>::kMfma;
   static constexpr int NG = Fmt<BITS>::kGroups > 0 ? Fmt<BITS>::kGroups : 1;
@@ -455,7 +483,7 @@ struct Fused {
         for (int term = 0; term < NT; ++term) ts[term] = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const float sv = v[slot_k<BITS>(jj)] * (slot_hi_nibble<BITS>(jj) ? scl * 0.0625f : scl);
+          const float sv = v[slot_k<BITS>(jj)] * (slot_hi_nibble<BITS, NC>(jj) ? scl * 0.0625f : scl);
           const uint32_t hi = to_op_bits<BF16OP>(sv);
           el[0][jj] = hi;
           if constexpr (NT >= 2) {
@@ -466,7 +494,7 @@ struct Fused {
           }
 #pragma unroll
           for (int term = 0; term < NT; ++term)   // group sums of the values as represented, unscaled by 1/16
-            ts[term] += op_bits_to_float<BF16OP>(el[term][jj]) * (slot_hi_nibble<BITS>(jj) ? 16.0f : 1.0f);
+            ts[term] += op_bits_to_float<BF16OP>(el[term][jj]) * (slot_hi_nibble<BITS, NC>(jj) ? 16.0f : 1.0f);
         }
 #pragma unroll
         for (int term = 0; term < NT; ++term) {
@@ -661,7 +689,7 @@ struct Fused {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const float x = v[slot_k<BITS>(jj)];
-          const float sj = slot_hi_nibble<BITS>(jj) ? scl * 0.0625f : scl;
+          const float sj = slot_hi_nibble<BITS, NC>(jj) ? scl * 0.0625f : scl;
           const uint32_t hi = to_op_bits<BF16OP>(x * sj);
           el[0][jj] = hi;
           if constexpr (NT >= 2) {
@@ -915,7 +943,7 @@ struct Fused {
   // scales, group g in bits 16g) and the bias operand bfr (slot j of lane group c holds the
   // bias of this wave's group 8*(c&1) + j, 0 past the slice).
   __device__ __forceinline__ void compute_core(int nsw, const u4_t dw[MAXS], const uint32_t sc[MAXS], const u4_t& bfr,
-                                               f4_t acc[MT]) {
+                                               const u4_t& sfr, f4_t acc[MT]) {
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
       if (NS > 0 || s < nsw) {   // streaming: every step runs (masked steps have zero operands)
@@ -937,7 +965,7 @@ struct Fused {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
               const int q = g * (NM / NG) + qq;
-              const u4_t b = convert_codes<BITS>(d, q);
+              const u4_t b = convert_codes<BITS, NC>(d, q);
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt) cg[g][mt] = mfma<BF16OP>(afrag[s][q][mt], b, cg[g][mt]);
             }
@@ -960,33 +988,46 @@ struct Fused {
       }
     }
     if constexpr (QUANT) {
-      // sum_g b[n, g] * (sum of group g's operands): one MFMA per row tile
+      // sum_g b[n, g] G_g (G_g: group g's operand sum, held times 2^-kGsumShift), and for
+      // normal codes sum_g s[n, g] G_g: acc = sum s P' - sum s G + 2^-bits sum b G, in units
+      // of 2^-bits (subnormal codes: acc = sum s P + 2^-24 sum b G, in units of 2^-24)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (NC) {
+          const f4_t cs = mfma<false>(gfrag[mt], sfr, (f4_t){0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(cs[v], -(float)(1 << kGsumShift), acc[mt][v]);
+        }
         const f4_t cb = mfma<false>(gfrag[mt], bfr, (f4_t){0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(cb[v], (float)(1 << kGsumShift) * kCodeScale, acc[mt][v]);
+        for (int v = 0; v < 4; ++v)
+          acc[mt][v] = fmaf(cb[v], (float)(1 << kGsumShift) / code_mul<BITS, NC>(), acc[mt][v]);
       }
     }
   }
 
   // A tile whose scales and biases came with its codes (chunked variant).
   __device__ __forceinline__ void compute_tile(int nsw, int c, const TileRegs& r, f4_t acc[MT]) {
-    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
+    u4_t bfr = (u4_t){0u, 0u, 0u, 0u}, sfr = (u4_t){0u, 0u, 0u, 0u};
     if constexpr (QUANT) {
-      uint32_t el[8];
+      // slot j of lane group c: group 8 (c & 1) + j's bias (scale); groups past this wave's
+      // slice get 0 (their loads were skipped)
+      auto operand = [&](const uint32_t (&v)[MAXS], u4_t& out) __attribute__((always_inline)) {
+        uint32_t el[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // groups past this wave's slice get 0 (their loads were skipped)
-        const uint32_t lo = (j < MAXS * NG && j < nsw * NG) ? (r.bi[j / NG] >> (16 * (j % NG))) & 0xFFFFu : 0u;
-        const uint32_t hi = (8 + j < MAXS * NG && 8 + j < nsw * NG)
-                                ? (r.bi[(8 + j) / NG] >> (16 * ((8 + j) % NG))) & 0xFFFFu : 0u;
-        el[j] = (c & 1) ? hi : lo;
-      }
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t lo = (j < MAXS * NG && j < nsw * NG) ? (v[j / NG] >> (16 * (j % NG))) & 0xFFFFu : 0u;
+          const uint32_t hi = (8 + j < MAXS * NG && 8 + j < nsw * NG)
+                                  ? (v[(8 + j) / NG] >> (16 * ((8 + j) % NG))) & 0xFFFFu : 0u;
+          el[j] = (c & 1) ? hi : lo;
+        }
 #pragma unroll
-      for (int w = 0; w < 4; ++w) bfr[w] = el[2 * w] | (el[2 * w + 1] << 16);
+        for (int w = 0; w < 4; ++w) out[w] = el[2 * w] | (el[2 * w + 1] << 16);
+      };
+      operand(r.bi, bfr);
+      if constexpr (NC) operand(r.sc, sfr);
     }
-    compute_core(nsw, r.dw, r.sc, bfr, acc);
+    compute_core(nsw, r.dw, r.sc, bfr, sfr, acc);
   }
 
   // ---- per-wave scales and biases (streaming variant) --------------------------------
@@ -1029,7 +1070,7 @@ struct Fused {
   __device__ __forceinline__ void compute_regs(int s_from, int c, const SbW& sb, const u4_t dw[MAXS], f4_t acc[MT]) {
     static_assert(NS > 0, "the streaming variant");
     uint32_t sc[MAXS];
-    u4_t bfr = (u4_t){0u, 0u, 0u, 0u};
+    u4_t bfr = (u4_t){0u, 0u, 0u, 0u}, sfr = (u4_t){0u, 0u, 0u, 0u};
     if constexpr (QUANT) {
       uint32_t scl[WD], bia[WD];
 #pragma unroll
@@ -1050,14 +1091,17 @@ struct Fused {
       for (int w = 0; w < 4; ++w) {
         const int g0 = 2 * w, g1 = 2 * w + 1;
         const uint32_t v = w < WD ? bia[w < WD ? w : 0] : 0u;
+        // the scale operand: even lane groups hold groups 0..7, odd ones groups 8..15 (none)
+        const uint32_t u = (w < WD && !(c & 1)) ? scl[w < WD ? w : 0] : 0u;
         const bool ok0 = g0 < WGR && g0 >= s_from * NG, ok1 = g1 < WGR && g1 >= s_from * NG;
         bfr[w] = (ok0 ? (v & 0xFFFFu) : 0u) | (ok1 ? (v & 0xFFFF0000u) : 0u);
+        sfr[w] = (ok0 ? (u & 0xFFFFu) : 0u) | (ok1 ? (u & 0xFFFF0000u) : 0u);
       }
     } else {
 #pragma unroll
       for (int s = 0; s < MAXS; ++s) sc[s] = 0u;
     }
-    compute_core(NS, dw, sc, bfr, acc);
+    compute_core(NS, dw, sc, bfr, sfr, acc);
   }
 
   // Epilogue inputs of the outputs a finishing lane owns (linear with residual or constant):
@@ -1291,11 +1335,12 @@ __device__ __forceinline__ void lds_wait_eq(const int* a, int v) {
 }
 
 // EPI (streaming variant): the call is a linear with residual or constant inputs.
-template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI>
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI, bool NC>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
   static_assert(CHUNKED == (NS == 0), "the streaming variant has a fixed step count");
+  static_assert(!NC || BITS == 4, "normal codes: 4-bit weights");
   static_assert(!(CHUNKED && EPI), "the chunked variant stages epilogue inputs in LDS");
-  using S = Fused<BITS, BF16OP, MT, NS>;
+  using S = Fused<BITS, BF16OP, MT, NS, NC>;
   constexpr int STEPK = S::STEPK;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   float* stat = reinterpret_cast<float*>(lds_raw);
@@ -1355,8 +1400,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     for (int mt = 0; mt < MT; ++mt) {
       f4_t v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)   // quantized partials carry the codes' 2^-24 (kCodeScale)
-        v[j] = (S::QUANT ? acc[mt][j] * 0x1p24f : acc[mt][j]) * st.unscale[mt][j];
+      for (int j = 0; j < 4; ++j)   // quantized partials are in units of 2^-bits (code_mul)
+        v[j] = (S::QUANT ? acc[mt][j] * code_mul<BITS, NC>() : acc[mt][j]) * st.unscale[mt][j];
       *reinterpret_cast<f4_t*>(rb + mt * 256 + lane * 4) = v;
     }
   };
@@ -1575,18 +1620,29 @@ __host__ __device__ constexpr long lds_bytes_for(int rows, int kc, int mt) {
          2L * kEpiSlot * 2;
 }
 
-template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI = false>
-hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t s) {
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI, bool NC>
+hipError_t launch_nc(const LinParams& p, int grid, size_t lds, hipStream_t s) {
   // Above 64 KiB of dynamic LDS the kernel must opt in once (a host-side attribute).
   static bool opted_in = false;
   if (!opted_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI, NC>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
     opted_in = true;
   }
-  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI>), dim3(grid), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<BITS, BF16OP, MT, CHUNKED, NS, EPI, NC>), dim3(grid), dim3(kThreads), lds, s, p);
   return hipGetLastError();
+}
+// Normal codes for 4-bit calls without LayerNorm (their rows have no large common part;
+// such calls have one operand term per activation row, so MT <= 2); subnormal codes
+// otherwise (see convert_codes).
+template <int BITS, bool BF16OP, int MT, bool CHUNKED, int NS, bool EPI = false>
+hipError_t launch_variant(const LinParams& p, int grid, size_t lds, hipStream_t s) {
+  if constexpr (BITS == 4 && MT <= 2) {
+    if (!p.ln) return launch_nc<BITS, BF16OP, MT, CHUNKED, NS, EPI, true>(p, grid, lds, s);
+  }
+  return launch_nc<BITS, BF16OP, MT, CHUNKED, NS, EPI, false>(p, grid, lds, s);
 }
 
 // The streaming variant with NS steps per wave, if its staging fits (pieces per lane and

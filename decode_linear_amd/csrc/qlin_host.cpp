@@ -118,9 +118,11 @@ qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, 
   if (bf16op) {            // dense bf16 weights: bf16 operands, exact 1- or 3-term activations
     // (bf16 x is one bf16 term; fp16 x and LN outputs need three)
     p.terms = (p.ln || x_dtype == QLIN_F16) ? 3 : 1; p.scale_act = 0; p.scale_gb = 0;
-  } else {                 // fp16 operands: 1 term when x is fp16 and there is no LN, else 2 scaled terms
+  } else {                 // fp16 operands: 1 term without LN, else 2; activation rows are always
+    // scaled by a power of two into [2^14, 2^15) at their maximum, so that small values stay
+    // normal (the matrix cores lose precision on subnormal inputs next to larger products)
     p.terms = p.ln ? 2 : 1;
-    p.scale_act = (p.ln || x_dtype == QLIN_BF16) ? 1 : 0;
+    p.scale_act = 1;
     p.scale_gb = (p.ln && x_dtype == QLIN_BF16) ? 1 : 0;
   }
   p.act = act; p.res = res; p.add = add; p.y = y; p.y_dtype = y_dtype;
@@ -326,6 +328,35 @@ void qlin_chain_destroy(qlin_chain* chain) {
   if (chain->exec) hipGraphExecDestroy(chain->exec);
   if (chain->graph) hipGraphDestroy(chain->graph);
   delete chain;
+}
+
+qlin_status qlin_mlp(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* gate, const qlin_weight* up,
+                     const qlin_weight* down, const qlin_ln* ln, const void* residual, void* h, void* y,
+                     qlin_dtype y_dtype, void* stream) {
+  if (!gate || !up || !down) return QLIN_ERR_NULL;
+  qlin_status st = validate(x, x_dtype, T, gate, up, ln, QLIN_ACT_NONE, nullptr, nullptr, h, x_dtype);
+  if (st != QLIN_OK) return st;
+  if (down->K != gate->N) return QLIN_ERR_SHAPE;
+  st = validate(h, x_dtype, T, down, nullptr, nullptr, QLIN_ACT_NONE, residual, nullptr, y, y_dtype);
+  if (st != QLIN_OK) return st;
+  if (T == 0 || down->N == 0) return QLIN_OK;   // empty y: a valid no-op (I = down->K >= 64)
+  const size_t hbytes = (size_t)T * (size_t)gate->N * 2;
+  const size_t ybytes = (size_t)T * (size_t)down->N * dtype_size(y_dtype);
+  if (overlaps(h, hbytes, x, (size_t)T * (size_t)gate->K * 2)) return QLIN_ERR_ARG;
+  if (overlaps(h, hbytes, residual, (size_t)T * (size_t)down->N * 2)) return QLIN_ERR_ARG;
+  if (overlaps(h, hbytes, y, ybytes)) return QLIN_ERR_ARG;
+  for (const qlin_weight* w : {gate, up, down}) {
+    const size_t wb = (size_t)w->N * (size_t)w->K * (size_t)w->bits / 8;
+    if (overlaps(h, hbytes, w->data, wb)) return QLIN_ERR_ARG;
+    if (w->bits != 16) {
+      const size_t sb = (size_t)w->N * (size_t)(w->K / 64) * 2;
+      if (overlaps(h, hbytes, w->scales, sb) || overlaps(h, hbytes, w->biases, sb)) return QLIN_ERR_ARG;
+    }
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch(x, x_dtype, T, gate, up, ln, QLIN_ACT_NONE, nullptr, nullptr, h, x_dtype, s);
+  if (st != QLIN_OK) return st;
+  return launch(h, x_dtype, T, down, nullptr, nullptr, QLIN_ACT_NONE, residual, nullptr, y, y_dtype, s);
 }
 
 qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream) {

@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
+qlin_mlp, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
 qlin_dispatch_count,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
@@ -78,13 +78,14 @@ def lib():
     L.qlin_chain_destroy.argtypes = [vp]
     L.qlin_chain_destroy.restype = None
     L.qlin_stream_read.argtypes = [vp, i64, vp, vp]
+    L.qlin_mlp.argtypes = [vp, i32, i32, W, W, W, Ln, vp, vp, vp, i32, vp]
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
-                 "qlin_stream_read"):
+                 "qlin_stream_read", "qlin_mlp"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -182,6 +183,25 @@ def qlin_gateup_swiglu(x: torch.Tensor, gate: QWeight, up: QWeight, ln=None, out
                                   None if lnc is None else ctypes.byref(lnc), _ptr(out), _dtype(out), _stream(stream))
     _check(st, "qlin_gateup_swiglu")
     return out
+
+
+def qlin_mlp(x: torch.Tensor, gate: QWeight, up: QWeight, down: QWeight, ln=None,
+             residual: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, stream=None):
+    """(y, h): h (T, I) = silu(LN?(x) @ Wg.T) * (LN?(x) @ Wu.T) in x's dtype, then
+    y (T, Hout) = [residual +] h @ Wd.T (two dispatches; h is the caller's workspace)."""
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((T, gate.N), dtype=x.dtype, device=x.device)
+    if out is None:
+        out = torch.empty((T, down.N), dtype=out_dtype or x.dtype, device=x.device)
+    lnc = _ln(ln)
+    gc, uc, dc = gate.c(), up.c(), down.c()
+    st = lib().qlin_mlp(_ptr(x), _dtype(x), T, ctypes.byref(gc), ctypes.byref(uc), ctypes.byref(dc),
+                        None if lnc is None else ctypes.byref(lnc), _ptr(residual), _ptr(h), _ptr(out), _dtype(out),
+                        _stream(stream))
+    _check(st, "qlin_mlp")
+    return out, h
 
 
 def qlin_attend(qkv: torch.Tensor, kv: Optional[torch.Tensor], heads: int, head_dim: int, last: bool = False,

@@ -108,6 +108,25 @@ qlin_status qlin_gateup_swiglu(const void* x, qlin_dtype x_dtype, int32_t T, con
                                const qlin_weight* up, const qlin_ln* ln, void* y, qlin_dtype y_dtype,
                                void* stream);
 
+/* The MLP of a decoder layer, gate+up then down ([p3] mlx-bun 0.0.10 -> 0.0.12,
+ * model/fused-mlp-kernel.ts, whose header comment states the whole-MLP product):
+ *     h = silu(LN?(x) . gate^T) * (LN?(x) . up^T)    (T, I), rounded once to x_dtype
+ *     y = [residual +] h . down^T                     (T, Hout), rounded once to y_dtype
+ * as two dispatches on `stream`: the gate/up kernel writes h, then the fused linear reads
+ * it with the residual in its epilogue.  The page's single dispatch adds the down partials
+ * with floating-point atomics; here no atomic touches data, so y is bitwise reproducible.
+ * The hidden activation is rounded to the activation dtype, as the page rounds it to bf16.
+ *   gate, up   (I, K) weights as for qlin_gateup_swiglu;  down (Hout, I): down->K == I.
+ *   h          caller-owned device workspace of T*I elements of x_dtype, 16-byte aligned;
+ *              it must not overlap x, the weights, residual or y.  On return its contents
+ *              are h (the call may be captured: h is written when the work runs).
+ *   residual   (T, Hout) of x_dtype or NULL;  y (T, Hout) of y_dtype, not overlapping x,
+ *              h or residual.
+ * Both stages are validated before anything is enqueued; errors as for qlin_linear. */
+qlin_status qlin_mlp(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* gate,
+                     const qlin_weight* up, const qlin_weight* down, const qlin_ln* ln,
+                     const void* residual, void* h, void* y, qlin_dtype y_dtype, void* stream);
+
 /* Quantize an fp32 (N, K) matrix w (device, 16-byte aligned) to the affine format above.
  * For each row n and group of 64 consecutive k, in IEEE binary32 with ties to even:
  *     lo = min, hi = max;  s = fp16(fl32(fl32(hi - lo) / (2^bits - 1)));  b = fp16(lo);
@@ -215,7 +234,7 @@ qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, 
 
 /* Number of kernels this library has enqueued in this process, by entry point:
  * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read (a test can
- * assert a kernel ran). */
+ * assert a kernel ran; qlin_mlp counts one gate/up and one linear). */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Static description of a status code. */

@@ -222,6 +222,19 @@ def gateup(x, x_dtype: int, bits: int, gate, up, w_dtype: int = F16,
     return y
 
 
+def mlp(x, x_dtype: int, bits: int, gate, up, down, down_bits: int = None, w_dtype: int = F16,
+        gamma=None, beta=None, eps: float = 1e-5, res=None):
+    """[p3] mlx-bun 0.0.10 -> 0.0.12, model/fused-mlp-kernel.ts (the whole MLP of its header
+    comment): h = silu(LN?(x) @ Wg.T) * (LN?(x) @ Wu.T), rounded once (RNE) to the activation
+    dtype as the page rounds the hidden activation to bf16; then y = [res +] h @ Wd.T.
+    gate / up / down: (data, scales, biases) tuples.  Returns (h bit patterns, y fp64)."""
+    h64 = gateup(x, x_dtype, bits, gate, up, w_dtype, gamma, beta, eps)
+    h = round_to(h64, x_dtype)
+    dd, ds, db = down
+    y = linear(h, x_dtype, bits if down_bits is None else down_bits, dd, w_dtype, ds, db, res=res)
+    return h, y
+
+
 def attend(qkv, kv, dtype: int, heads: int, head_dim: int, last: bool = False):
     """[p1] `attend`: qkv (T, 3D) and kv (2, H, P, HD) or None as fp16/bf16 bit patterns ->
     (out (T, D) fp64, or (1, D) with last; kv_out (2, H, P + T, HD) bit patterns)."""

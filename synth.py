@@ -26,6 +26,8 @@ N(0, 1/K) whose 1/K is the variance):
   6  attend over the depth decoder's band: D = 1024 as 16 heads of 64, P = 24 cached and
      T = 8 new positions (the 32-position cap); qkv (T, 3D) and the cache (2, 16, 24, 64)
      bf16 N(0,1), so that scores q.k / sqrt(64) are about N(0,1)
+  7  the MLP around workload 4: gate/up as in 4 (K=4096, I=14336, 4-bit) and a down
+     projection (Hout=4096, K=I) 4-bit from N(0, 0.02), residual bf16 N(0,1)
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ import numpy as np
 F32, F16, BF16 = 0, 1, 2
 NP_CODES = {F32: np.float32}
 
-TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9}
+TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9, "down": 10}
 CHAIN_PASSES = 124
 CHAIN_K = CHAIN_N = 1024
 CHAIN_TMAX = 8
@@ -230,3 +232,62 @@ def attend_workload() -> AttendCase:
     case = attend_case(0, ATTEND_H, ATTEND_HD, ATTEND_P, ATTEND_T, BF16, c=6)
     case.name = f"attend-H{ATTEND_H}-HD{ATTEND_HD}-P{ATTEND_P}-T{ATTEND_T}"
     return case
+
+
+@dataclass
+class MlpCase:
+    name: str
+    T: int
+    K: int
+    I: int
+    Hout: int
+    x_dtype: int
+    bits: int
+    x: np.ndarray
+    gate: np.ndarray          # float32 (I, K) to be quantized, or uint16 dense bits when bits == 16
+    up: np.ndarray
+    down: np.ndarray          # (Hout, I), same kinds
+    gamma: Optional[np.ndarray] = None
+    beta: Optional[np.ndarray] = None
+    eps: float = 1e-5
+    res: Optional[np.ndarray] = None
+
+
+def random_mlp(s: int, T: int, K: int, I: int, Hout: int, bits: int, x_dtype: int = BF16, ln: bool = False,
+               res: bool = False, c: Optional[int] = None) -> MlpCase:
+    """Gate/up (I, K) and down (Hout, I) drawn like workload 4 (stream ids offset by s)."""
+    c = 100 + s if c is None else c
+    kw = {}
+    if ln:
+        kw["gamma"] = draw(c, 0, "gamma", (K,), 1.0, 0.1, x_dtype)
+        kw["beta"] = draw(c, 0, "beta", (K,), 0.0, 0.1, x_dtype)
+    if res:
+        kw["res"] = draw(c, 0, "res", (T, Hout), 0.0, 1.0, x_dtype)
+    if bits == 16:
+        g = draw(c, 0, "w", (I, K), 0.0, 1.0 / np.sqrt(K), x_dtype)
+        u = draw(c, 0, "up", (I, K), 0.0, 1.0 / np.sqrt(K), x_dtype)
+        d = draw(c, 0, "down", (Hout, I), 0.0, 1.0 / np.sqrt(I), x_dtype)
+    else:
+        g = draw(c, 0, "w", (I, K), 0.0, 0.02, F32)
+        u = draw(c, 0, "up", (I, K), 0.0, 0.02, F32)
+        d = draw(c, 0, "down", (Hout, I), 0.0, 0.02, F32)
+    return MlpCase(f"mlp{s}-T{T}-K{K}-I{I}-H{Hout}-b{bits}", T, K, I, Hout, x_dtype, bits,
+                   x=draw(c, 0, "x", (T, K), 0.0, 1.0, x_dtype), gate=g, up=u, down=d, **kw)
+
+
+def mlp_workload() -> MlpCase:
+    case = random_mlp(0, 4, 4096, 14336, 4096, 4, BF16, res=True, c=7)
+    case.name = "mlp-q4-M4-K4096-I14336-H4096"
+    return case
+
+
+def wide_case(s: int, T: int, K: int, N: int, bits: int, x_dtype: int = BF16) -> LinearCase:
+    """A parity case whose activations spread over many binades (z1 * exp(1.5 z2), z1 and
+    z2 standard normal, a heavy-tailed draw like the hidden activations of an MLP), with
+    the weights of random_case."""
+    c = 100 + s
+    x64 = normal(seed(c, 0, "x"), (T, K)) * np.exp(1.5 * normal(seed(c, 0, "add"), (T, K)))
+    base = random_case(s, T, K, N, bits, x_dtype)
+    base.name = f"wide{s}-T{T}-K{K}-N{N}-b{bits}"
+    base.x = to_bits(x64, x_dtype)
+    return base

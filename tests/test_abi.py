@@ -228,3 +228,24 @@ def test_stream_read_validation(q):
     assert f(QKV, 1000, AO, None) == -2       # not a multiple of 16
     assert f(QKV + 8, 1024, AO, None) == -5
     assert f(QKV, 1024, AO + 2, None) == -5
+
+
+def test_mlp_validation(q):
+    f = q.lib().qlin_mlp
+    g = _w(q, bits=4, N=256, K=1024)
+    u = _w(q, bits=4, N=256, K=1024, data=W + 0x100000, scales=S + 0x100000, biases=B + 0x100000)
+    d = _w(q, bits=8, N=128, K=256, data=W + 0x200000, scales=S + 0x200000, biases=B + 0x200000)
+    H = 0x3000000   # (only invalid calls here: a valid one would launch on fake addresses)
+    bad_k = _w(q, bits=8, N=128, K=512, data=W + 0x200000, scales=S + 0x200000, biases=B + 0x200000)
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_k), None, None, H, Y,
+             q.QLIN_BF16, None) == -2
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), None, None, None, H, Y, q.QLIN_BF16, None) == -1
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, None, None, Y,
+             q.QLIN_BF16, None) == -1
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, None, H + 8, Y,
+             q.QLIN_BF16, None) == -5
+    # h overlapping x, or y
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, None, X + 64, Y,
+             q.QLIN_BF16, None) == -7
+    assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, None, H, H + 64,
+             q.QLIN_BF16, None) == -7

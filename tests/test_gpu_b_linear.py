@@ -135,3 +135,16 @@ def test_empty_calls_leave_output_untouched():
     qlin_linear(x, empty, out=out[:, :0])
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("T,K", [(1, 1024), (4, 1024), (16, 1024), (4, 8192), (4, 14336)])
+def test_wide_range_activations(bits, T, K):
+    # activations over many binades: every product of a 32-k MFMA block must keep its
+    # precision next to much larger ones (codes entering as subnormals did not)
+    run_linear_case(synth.wide_case(4000 + T + K + bits, T, K, 96, bits), y_dtypes=(synth.BF16,))
+
+
+@pytest.mark.parametrize("bits", [4, 8, 16])
+def test_wide_range_activations_fp16(bits):
+    run_linear_case(synth.wide_case(4100 + bits, 4, 2048, 80, bits, x_dtype=synth.F16), y_dtypes=(synth.F16,))

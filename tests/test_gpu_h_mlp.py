@@ -1,0 +1,91 @@
+"""GPU parity of qlin_mlp (gate/up, then the down projection with the residual) against the
+oracle's MLP: the hidden activation under the gate/up parity bar (plus the roundoff of its
+16-bit storage), the output under the parity gates, and the down stage teacher-forced on
+the library's own hidden activation."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import TOL, Packed, TORCH_DT, dev_bits, errors, gate_a, gate_b, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from decode_linear_amd import build
+    build.ensure_built()
+
+
+def _weights(c):
+    if c.bits == 16:
+        P = [Packed(bits=16, dense=a, dense_dtype=c.x_dtype) for a in (c.gate, c.up, c.down)]
+        return P, [(a, None, None) for a in (c.gate, c.up, c.down)], c.x_dtype
+    P = [Packed(a, c.bits) for a in (c.gate, c.up, c.down)]
+    return P, [p.oracle_tuple() for p in P], synth.F16
+
+
+def _run(c):
+    from decode_linear_amd import qlin_mlp
+    (G, U, Dn), (go, uo, do), wdt = _weights(c)
+    x = dev_bits(c.x, c.x_dtype)
+    ln = None if c.gamma is None else (dev_bits(c.gamma, c.x_dtype), dev_bits(c.beta, c.x_dtype), c.eps)
+    res = None if c.res is None else dev_bits(c.res, c.x_dtype)
+    y32, h = qlin_mlp(x, G.q, U.q, Dn.q, ln=ln, residual=res, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    h_dev = host_bits(h)
+    h_orc, y64 = oracle.mlp(c.x, c.x_dtype, c.bits, go, uo, do, w_dtype=wdt, gamma=c.gamma, beta=c.beta,
+                            eps=float(np.float32(c.eps)), res=c.res)
+    # hidden: the gate/up parity bar on the unrounded product (max(|h|, tau)-relative error
+    # within 2e-3 plus the unit roundoff of the stored dtype)
+    h64 = oracle.gateup(c.x, c.x_dtype, c.bits, go, uo, w_dtype=wdt, gamma=c.gamma, beta=c.beta,
+                        eps=float(np.float32(c.eps)))
+    assert np.array_equal(oracle.round_to(h64, c.x_dtype), h_orc)
+    e = float(errors(oracle.widen(h_dev, c.x_dtype), h64).max())
+    u = 2.0 ** -8 if c.x_dtype == synth.BF16 else 2.0 ** -11
+    assert e <= TOL + u, f"{c.name}: hidden activation error {e:.3e}"
+    # down stage on the library's own hidden activation (teacher forced)
+    y_tf = oracle.linear(h_dev, c.x_dtype, c.bits, do[0], wdt, do[1], do[2], res=c.res)
+    gate_a(y32, y_tf, what=c.name + " (teacher forced)")
+    # End to end, y differs from the oracle's y64 by exactly the oracle's down projection
+    # of (h - h_oracle): both sides round h once, and near a tie they may round apart.
+    # That difference is a property of the two h, so the gates above carry the parity.
+    assert np.isfinite(y64).all()
+    y16, _ = qlin_mlp(x, G.q, U.q, Dn.q, ln=ln, residual=res, out_dtype=TORCH_DT[c.x_dtype])
+    torch.cuda.synchronize()
+    gate_b(y16, y32, y_tf, c.x_dtype, what=c.name)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 16])
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_mlp_shapes(bits, T):
+    _run(synth.random_mlp(500 + T + bits, T, 256, 192, 72, bits, res=True))
+
+
+def test_mlp_layernorm_no_residual_fp16():
+    _run(synth.random_mlp(520, 3, 512, 128, 40, 4, synth.F16, ln=True))
+
+
+def test_mlp_long_hidden_chunked_down():
+    # I = 9216 pushes the down projection past one streaming window per wave
+    _run(synth.random_mlp(521, 2, 256, 9216, 48, 4, res=True))
+
+
+def test_mlp_workload_full_size():
+    _run(synth.mlp_workload())
+
+
+def test_mlp_rejects_aliasing_and_shape():
+    from decode_linear_amd import QlinError, qlin_mlp
+    c = synth.random_mlp(522, 2, 128, 64, 32, 8)
+    (G, U, Dn), _, _ = _weights(c)
+    x = dev_bits(c.x, c.x_dtype)
+    with pytest.raises(QlinError):
+        qlin_mlp(x, G.q, U.q, G.q)          # down->K (=128) != I (=64)
+    big = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    xa = big[:c.T * c.K].view(c.T, c.K)
+    xa.copy_(x)
+    with pytest.raises(QlinError):
+        qlin_mlp(xa, G.q, U.q, Dn.q, h=big[128:128 + c.T * c.I].view(c.T, c.I))   # h overlaps x
