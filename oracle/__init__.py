@@ -9,7 +9,7 @@ this module only marshals numpy arrays through ctypes.  Page citations for each
 function are in that file's comments:
   [p1] maya-mac src/maya_mac/mlx_kernels.py ("Custom Metal kernels for the depth decoder")
   [p2] @mlx-bun/inference 0.0.0-stage -> 1.0.0, kernels/trellis/mixed-gate-up.ts
-  [p3] mlx-bun 0.0.10 -> 0.0.12, model/fused-decode-kernel.ts
+  [p3] mlx-bun 0.0.10 -> 0.0.12, model/fused-decode-kernel.ts (and fused-mlp-kernel.ts)
 
 dtype codes: 0 = fp32, 1 = fp16, 2 = bf16.  16-bit arrays are passed as their
 uint16 bit patterns.
@@ -72,6 +72,8 @@ def load():
     lib.orc_gateup.restype = i32
     lib.orc_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i32, vp, vp]
     lib.orc_attend.restype = i32
+    lib.orc_sample.argtypes = [vp, i32, i64, vp, ctypes.c_float, i64, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.orc_sample.restype = i32
     _lib = lib
     return lib
 
@@ -252,3 +254,33 @@ def attend(qkv, kv, dtype: int, heads: int, head_dim: int, last: bool = False):
     if rc != 0:
         raise ValueError("oracle.attend: unsupported arguments")
     return out, kv_out
+
+
+def sample(logits, dtype: int, gumbel, inv_temp: float, top_k: int, table=None, prefix=None):
+    """[p1] `sample`: logits (n,) as fp32 values (dtype 0) or fp16/bf16 bit patterns; gumbel
+    (n,) float32 noise of this level; table (n, D) / prefix (n_prev, D) arrays of one dtype
+    (their bytes are copied).  Returns (code, out (n_prev [+ 1], D), kept count)."""
+    if dtype == F32:
+        logits = _c(logits, np.float32)
+    else:
+        logits = _c(logits, np.uint16)
+    gumbel = _c(gumbel, np.float32)
+    n = logits.shape[0]
+    ref = table if table is not None else prefix
+    D = 0 if ref is None else ref.shape[1]
+    edt = np.uint16 if ref is None else ref.dtype
+    es = np.dtype(edt).itemsize
+    n_prev = 0 if prefix is None else prefix.shape[0]
+    if table is not None:
+        table = np.ascontiguousarray(table)
+    if prefix is not None:
+        prefix = np.ascontiguousarray(prefix)
+    out = np.zeros((n_prev + (1 if table is not None else 0), D), edt)
+    code = np.zeros(1, np.int32)
+    kept = np.zeros(1, np.int64)
+    lib = load()
+    rc = lib.orc_sample(_p(logits), dtype, n, _p(gumbel), ctypes.c_float(inv_temp), top_k, _p(table), _p(prefix),
+                        n_prev, D, es, _p(out), _p(code), _p(kept))
+    if rc != 0:
+        raise ValueError("oracle.sample: unsupported arguments")
+    return int(code[0]), out, int(kept[0])

@@ -22,14 +22,18 @@
 //   gate/up  = silu(z_gate) * z_up
 //   attend   = the band's cache with this pass's keys and values appended, and causal
 //              softmax attention of the new positions over it (at most 32 positions)
+//   sample   = exact top-k by the logits' order-preserving keys (ties with the k-th kept),
+//              Gumbel-max over the kept codes, and the chosen code's embedding appended
 // Everything is computed in double precision from the exact bit patterns the GPU
 // receives.  Build: g++ -O2 -std=c++17 -fPIC -shared -ffp-contract=off (no fast-math).
 //
 // Parity pins for every function live in tests/test_oracle_*.py.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <functional>
 #include <vector>
 #include <limits>
 
@@ -390,6 +394,65 @@ int orc_attend(const uint16_t* qkv, const uint16_t* kv, int dtype, int64_t P, in
         out[row * D + h * HD + d] = o;
       }
     }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// sample — [p1] `_SAMPLE` and `sample()`: one sampling step of the depth decoder.
+//   key(f)   = the order-preserving 32-bit key of the fp32 value f: bits u of f, ~u when the
+//              sign bit is set, u | 2^31 otherwise (larger floats have larger keys; -0 < +0)
+//   kth      = the top_k-th largest key over the n codes (sorting, not a radix select)
+//   kept     = codes whose key >= kth (every code tied with the k-th is kept)
+//   s_i      = fl32(fl32(f_i * inv_temp) + gumbel_i)   (two fp32 roundings, no fused
+//              multiply-add: the argmax is an integer that fp32 rounding decides, so the
+//              library computes it in the same precision)
+//   code     = the kept i with the largest s_i, the smallest such i on ties; a NaN score
+//              never wins; -1 when no kept score is a number
+//   out      = prefix rows (n_prev, D) then, with a table, table row `code` (zeros when the
+//              code is -1): element bit patterns copied, es bytes each
+// logits: n values of dtype (0 fp32, 1 fp16, 2 bf16).  kept_count receives |kept|.
+// ---------------------------------------------------------------------------
+int orc_sample(const void* logits, int dtype, int64_t n, const float* gumbel, float inv_temp, int64_t top_k,
+               const void* table, const void* prefix, int64_t n_prev, int64_t D, int64_t es, void* out,
+               int32_t* code, int64_t* kept_count) {
+  if (n < 1 || top_k < 1 || top_k > n || (es != 2 && es != 4) || D < 0 || n_prev < 0) return -1;
+  std::vector<float> f((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (dtype == 0) f[(size_t)i] = static_cast<const float*>(logits)[i];
+    else {
+      const uint16_t b = static_cast<const uint16_t*>(logits)[i];
+      f[(size_t)i] = (float)(dtype == 1 ? f16_to_f64(b) : bf16_to_f64(b));   // exact widening
+    }
+  }
+  auto key = [](float v) {
+    uint32_t u;
+    std::memcpy(&u, &v, 4);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  std::vector<uint32_t> keys((size_t)n);
+  for (int64_t i = 0; i < n; ++i) keys[(size_t)i] = key(f[(size_t)i]);
+  std::vector<uint32_t> sorted = keys;
+  std::sort(sorted.begin(), sorted.end(), std::greater<uint32_t>());
+  const uint32_t kth = sorted[(size_t)(top_k - 1)];
+  int64_t best = -1, kept = 0;
+  float bs = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    if (keys[(size_t)i] < kth) continue;
+    ++kept;
+    const float scaled = f[(size_t)i] * inv_temp;   // rounded to fp32
+    const float sc = scaled + gumbel[i];             // rounded to fp32
+    if (std::isnan(sc)) continue;
+    if (best < 0 || sc > bs) { best = i; bs = sc; }   // ascending i: equal scores keep the smaller i
+  }
+  *code = (int32_t)best;
+  *kept_count = kept;
+  unsigned char* o = static_cast<unsigned char*>(out);
+  const size_t row = (size_t)D * (size_t)es;
+  if (n_prev > 0) std::memcpy(o, prefix, (size_t)n_prev * row);
+  if (table) {
+    if (best >= 0) std::memcpy(o + (size_t)n_prev * row, static_cast<const unsigned char*>(table) + (size_t)best * row, row);
+    else std::memset(o + (size_t)n_prev * row, 0, row);
   }
   return 0;
 }
