@@ -22,7 +22,7 @@ pure read reaches on this device, next to which the fused call's rate can be rea
 Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
 with 32 rows), the 124-pass LN+linear chain (hipGraph replay vs eager launches), the whole
 MLP around the headline projection (qlin_mlp: gate/up then down with the residual), one
-attend pass, and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
+attend pass, one sampling step (qlin_sample), and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
 the workload.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--only-main]
@@ -250,6 +250,31 @@ def bench_attend(steps, warmup):
                 gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
 
 
+def bench_sample(steps, warmup):
+    """One sampling step of the depth decoder (qlin_sample: 2048 bf16 logits, top-64,
+    Gumbel-max, a 1024-wide bf16 embedding row appended to a 16-row prefix): latency-bound,
+    cache-resident; bytes are logits, noise row, prefix and table row read, rows written."""
+    import synth
+    from decode_linear_amd import qlin_sample
+    torch = _torch()
+    case = synth.sample_workload()
+    lg = _dev(case.logits, case.logit_dtype)
+    g = torch.from_numpy(case.gumbel).cuda()
+    tb = _dev(case.table, case.emb_dtype)
+    pre = _dev(case.prefix, case.emb_dtype)
+    n_prev = case.prefix.shape[0]
+    out = torch.empty((n_prev + 1, case.D), dtype=torch.bfloat16, device="cuda")
+    code = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        qlin_sample(lg, g, 1, tb, pre, 1.0 / 0.9, 64, out=out, code=code)
+
+    us = _time_graph(step, 1, steps, warmup) * 1e3 / steps
+    nbytes = case.n * (2 + 4) + (2 * n_prev + 2) * case.D * 2 + 4
+    return dict(name=case.name, n=case.n, D=case.D, n_prev=n_prev, top_k=64, bytes=nbytes, us=us,
+                gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
+
+
 def bench_chain(replays, warmup):
     """124 dependent LN + linear passes (8-bit, K=N=1024, T = 1 + p mod 8): graph replay
     and eager launches, rotated over >= 1 GiB of chain copies."""
@@ -377,7 +402,7 @@ def main():
             extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
         ch = bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))
         extra[ch["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ch.items() if k != "name"}
-        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup)):
+        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup), bench_sample(a.steps, a.warmup)):
             extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
             extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
     us = main_r["us"]

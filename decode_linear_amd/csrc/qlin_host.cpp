@@ -12,7 +12,7 @@
 
 namespace {
 
-std::atomic<int64_t> g_dispatch[6];
+std::atomic<int64_t> g_dispatch[7];
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
 constexpr int64_t kMaxN = int64_t(1) << 28;
@@ -372,8 +372,47 @@ qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, 
   return QLIN_OK;
 }
 
+qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, const float* gumbel, float inv_temp,
+                        int32_t top_k, const void* table, const void* prefix, int32_t n_prev, int32_t D,
+                        qlin_dtype emb_dtype, void* out, int32_t* code, void* stream) {
+  if (!logits || !gumbel || !code) return QLIN_ERR_NULL;
+  if (logit_dtype != QLIN_F32 && logit_dtype != QLIN_F16 && logit_dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (emb_dtype != QLIN_F32 && emb_dtype != QLIN_F16 && emb_dtype != QLIN_BF16) return QLIN_ERR_DTYPE;
+  if (n < 1 || n > qlin::kSampleMaxCodes || top_k < 1 || top_k > n) return QLIN_ERR_SHAPE;
+  if (n_prev < 0 || n_prev > (1 << 20)) return QLIN_ERR_SHAPE;
+  if (!(inv_temp > 0.0f) || !std::isfinite(inv_temp)) return QLIN_ERR_ARG;
+  const size_t ls = dtype_size(logit_dtype), es = dtype_size(emb_dtype);
+  if (!aligned(logits, ls) || !aligned(gumbel, 4) || !aligned(code, 4)) return QLIN_ERR_ALIGN;
+  const bool rows = table != nullptr || n_prev > 0;
+  if (rows) {
+    if (D < 1 || ((size_t)D * es) % 16 != 0 || D > (1 << 20)) return QLIN_ERR_SHAPE;
+    if (!out || (n_prev > 0 && !prefix)) return QLIN_ERR_NULL;
+    if (!aligned(out, 16) || (table && !aligned(table, 16)) || (n_prev > 0 && !aligned(prefix, 16)))
+      return QLIN_ERR_ALIGN;
+  }
+  const size_t row = (size_t)D * es;
+  const size_t outb = rows ? (size_t)(n_prev + (table ? 1 : 0)) * row : 0;
+  const bool in_place = n_prev > 0 && out == prefix;
+  if (rows) {
+    if (n_prev > 0 && !in_place && overlaps(out, outb, prefix, (size_t)n_prev * row)) return QLIN_ERR_ARG;
+    if (in_place && table && overlaps(static_cast<const char*>(out) + (size_t)n_prev * row, row, prefix,
+                                      (size_t)n_prev * row)) return QLIN_ERR_ARG;
+    if (table && overlaps(out, outb, table, (size_t)n * row)) return QLIN_ERR_ARG;
+    if (overlaps(out, outb, logits, (size_t)n * ls) || overlaps(out, outb, gumbel, (size_t)n * 4) ||
+        overlaps(out, outb, code, 4)) return QLIN_ERR_ARG;
+  }
+  if (overlaps(code, 4, logits, (size_t)n * ls) || overlaps(code, 4, gumbel, (size_t)n * 4)) return QLIN_ERR_ARG;
+  qlin::SampleParams a{};
+  a.logits = logits; a.logit_dtype = logit_dtype; a.n = n; a.gumbel = gumbel; a.inv_temp = inv_temp;
+  a.top_k = top_k; a.table = table; a.prefix = prefix; a.n_prev = rows ? n_prev : 0; a.D = rows ? D : 0;
+  a.es = (int)es; a.out = out; a.code = code; a.copy_prefix = (n_prev > 0 && !in_place) ? 1 : 0;
+  if (qlin::launch_sample(a, static_cast<hipStream_t>(stream)) != hipSuccess) return QLIN_ERR_HIP;
+  g_dispatch[6].fetch_add(1, std::memory_order_relaxed);
+  return QLIN_OK;
+}
+
 int64_t qlin_dispatch_count(int32_t which) {
-  if (which < 0 || which > 5) return -1;
+  if (which < 0 || which > 6) return -1;
   return g_dispatch[which].load(std::memory_order_relaxed);
 }
 

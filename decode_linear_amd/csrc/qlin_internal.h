@@ -71,6 +71,24 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bits, uint32_t*
 hipError_t launch_unpack(const void* data, const uint16_t* scales, const uint16_t* biases, int bits,
                          int dtype, int64_t N, int64_t K, float* out, hipStream_t s);
 
+// Arguments of one sample launch (exact top-k, Gumbel-max, embedding append).
+constexpr int kSampleMaxCodes = 8192;
+struct SampleParams {
+  const void* logits;     // (n) of logit_dtype
+  int logit_dtype;        // 0 fp32, 1 fp16, 2 bf16
+  int n;                  // 1 .. kSampleMaxCodes
+  const float* gumbel;    // (n) this level's noise
+  float inv_temp;
+  int top_k;              // 1 .. n
+  const void* table;      // (n, D) this level's embeddings, or null
+  const void* prefix;     // (n_prev, D), or null when n_prev == 0
+  int n_prev, D, es;      // rows, row width, element bytes (D * es a multiple of 16)
+  void* out;              // (n_prev + (table != null), D)
+  int32_t* code;          // (1)
+  int copy_prefix;        // 0: out is the prefix itself (append in place)
+};
+hipError_t launch_sample(const SampleParams& a, hipStream_t s);
+
 // Plain 16-byte streaming read of `bytes` (a multiple of 16) at buf; block b writes the XOR
 // fold of the words it read to partial[b] (grid blocks of 512 threads).
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int grid, hipStream_t s);

@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_mlp, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
+qlin_mlp, qlin_sample, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
 qlin_dispatch_count,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
@@ -79,13 +79,14 @@ def lib():
     L.qlin_chain_destroy.restype = None
     L.qlin_stream_read.argtypes = [vp, i64, vp, vp]
     L.qlin_mlp.argtypes = [vp, i32, i32, W, W, W, Ln, vp, vp, vp, i32, vp]
+    L.qlin_sample.argtypes = [vp, i32, i32, vp, ctypes.c_float, i32, vp, vp, i32, i32, i32, vp, vp, vp]
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
-                 "qlin_stream_read", "qlin_mlp"):
+                 "qlin_stream_read", "qlin_mlp", "qlin_sample"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -319,3 +320,31 @@ def qlin_stream_read(buf: torch.Tensor, partial: Optional[torch.Tensor] = None, 
     if st != 0:
         raise QlinError(st, "qlin_stream_read")
     return partial
+
+
+def qlin_sample(logits: torch.Tensor, gumbel: torch.Tensor, level: int, table: Optional[torch.Tensor],
+                prefix: Optional[torch.Tensor], inv_temp: float, top_k: int, embed: bool = True,
+                out: Optional[torch.Tensor] = None, code: Optional[torch.Tensor] = None, stream=None):
+    """One sampling step ([p1] `sample`): logits (n,) or (1, n); gumbel (levels, n) fp32 (row
+    `level` is used); table (levels, n, D) (slice `level`) or None; prefix (n_prev, D) or
+    None.  Returns (code (1,) int32, out = prefix + [table[level, code]] (n_prev + 1, D), or
+    the prefix when embed is False)."""
+    lg = logits.reshape(-1)
+    n = lg.numel()
+    g = gumbel[level]
+    tb = table[level] if (embed and table is not None) else None
+    ref = tb if tb is not None else prefix
+    D = 0 if ref is None else ref.shape[-1]
+    n_prev = 0 if prefix is None else prefix.shape[0]
+    edt = ref.dtype if ref is not None else torch.float16
+    if code is None:
+        code = torch.empty(1, dtype=torch.int32, device=lg.device)
+    if out is None and (tb is not None or n_prev > 0):
+        out = torch.empty((n_prev + (1 if tb is not None else 0), D), dtype=edt, device=lg.device)
+    for t in (lg, g, tb, prefix, out):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("qlin_sample: tensors must be contiguous")
+    st = lib().qlin_sample(_ptr(lg), _dtype(lg), n, _ptr(g), ctypes.c_float(inv_temp), int(top_k), _ptr(tb),
+                           _ptr(prefix), n_prev, D, _TORCH_TO_QLIN[edt], _ptr(out), _ptr(code), _stream(stream))
+    _check(st, "qlin_sample")
+    return code, out

@@ -216,6 +216,33 @@ qlin_status qlin_attend_check(const void* qkv, const void* kv, qlin_dtype dtype,
                               int32_t heads, int32_t head_dim, int32_t last, const void* out, qlin_dtype out_dtype,
                               const void* kv_out);
 
+/* One sampling step of the depth decoder ([p1] maya-mac src/maya_mac/mlx_kernels.py,
+ * `_SAMPLE` and `sample()`): exact top-k of the logits, Gumbel-max over the kept codes, and
+ * the chosen code's embedding appended to the prefix.
+ *   logits     (n) of logit_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16), 1 <= n <= 8192,
+ *              aligned to its element size.  Each logit f (widened exactly to fp32) has the
+ *              order-preserving key of its bits u: ~u when the sign bit is set, u | 2^31
+ *              otherwise (larger floats have larger keys; -0 orders below +0).
+ *   top_k      1 <= top_k <= n: codes whose key is >= the top_k-th largest key are kept
+ *              (all codes tied with the k-th value are kept).
+ *   gumbel     (n) fp32 noise of this step (the caller draws it, e.g. one row per level).
+ *   inv_temp   finite and > 0.  The score of a kept code is fl32(fl32(f * inv_temp) + g),
+ *              two fp32 roundings (no fused multiply-add).
+ *   code       device int32: the kept code with the largest score, the smallest index among
+ *              equal scores; a NaN score never wins; -1 if no kept score is a number.
+ *   table      (n, D) of emb_dtype: this step's code embeddings, or NULL (nothing appended).
+ *   prefix     (n_prev, D) of emb_dtype, or NULL when n_prev == 0.
+ *   out        (n_prev + (table != NULL), D) of emb_dtype: the prefix rows, then table row
+ *              `code` (zeros when code is -1), bit patterns copied.  out may be the prefix
+ *              itself (then only the new row is written); otherwise it must not overlap it.
+ *   D          row width; D * sizeof(emb_dtype) a multiple of 16; table, prefix and out
+ *              16-byte aligned.
+ * Errors: QLIN_ERR_NULL, QLIN_ERR_SHAPE (n, top_k, D, n_prev), QLIN_ERR_DTYPE,
+ * QLIN_ERR_ALIGN, QLIN_ERR_ARG (inv_temp, overlaps) before any HIP call. */
+qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, const float* gumbel, float inv_temp,
+                        int32_t top_k, const void* table, const void* prefix, int32_t n_prev, int32_t D,
+                        qlin_dtype emb_dtype, void* out, int32_t* code, void* stream);
+
 /* ---- measurement aid ----------------------------------------------------------------
  * qlin_stream_read: the device's streaming-read ceiling for the weight stream's access (the
  * "HBM bandwidth" the pages' 8-bit-versus-fp16 timing comparison of the maya-mac depth
@@ -233,8 +260,8 @@ qlin_status qlin_attend_check(const void* qkv, const void* kv, qlin_dtype dtype,
 qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream);
 
 /* Number of kernels this library has enqueued in this process, by entry point:
- * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read (a test can
- * assert a kernel ran; qlin_mlp counts one gate/up and one linear). */
+ * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample (a
+ * test can assert a kernel ran; qlin_mlp counts one gate/up and one linear). */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Static description of a status code. */

@@ -28,6 +28,9 @@ N(0, 1/K) whose 1/K is the variance):
      bf16 N(0,1), so that scores q.k / sqrt(64) are about N(0,1)
   7  the MLP around workload 4: gate/up as in 4 (K=4096, I=14336, 4-bit) and a down
      projection (Hout=4096, K=I) 4-bit from N(0, 0.02), residual bf16 N(0,1)
+  8  one sampling step of the depth decoder: 2048 codes, logits bf16 N(0, 2), Gumbel(0, 1)
+     noise for 32 levels (fp32), code embeddings bf16 N(0, 1) of width 1024 for 4 levels,
+     a prefix of 16 rows
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ import numpy as np
 F32, F16, BF16 = 0, 1, 2
 NP_CODES = {F32: np.float32}
 
-TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9, "down": 10}
+TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9, "down": 10,
+              "logits": 11, "gumbel": 12, "table": 13, "prefix": 14}
 CHAIN_PASSES = 124
 CHAIN_K = CHAIN_N = 1024
 CHAIN_TMAX = 8
@@ -291,3 +295,41 @@ def wide_case(s: int, T: int, K: int, N: int, bits: int, x_dtype: int = BF16) ->
     base.name = f"wide{s}-T{T}-K{K}-N{N}-b{bits}"
     base.x = to_bits(x64, x_dtype)
     return base
+
+
+def gumbel(s: int, shape) -> np.ndarray:
+    """float32 Gumbel(0, 1) draws, -log(-log(U)) with U uniform on (0, 1), on a PCG64 stream
+    seeded with s (the noise a sampling step takes as input)."""
+    rng = np.random.Generator(np.random.PCG64(s))
+    u = rng.uniform(np.nextafter(0.0, 1.0), 1.0, size=shape)
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
+@dataclass
+class SampleCase:
+    name: str
+    n: int
+    D: int
+    levels: int
+    logits: np.ndarray        # (n,) fp32 values or 16-bit bit patterns
+    logit_dtype: int
+    gumbel: np.ndarray        # (32, n) float32
+    table: np.ndarray         # (levels, n, D) bit patterns of emb_dtype
+    prefix: np.ndarray        # (n_prev, D)
+    emb_dtype: int
+
+
+def sample_case(s: int, n: int, D: int, n_prev: int, levels: int = 2, logit_dtype: int = BF16,
+                emb_dtype: int = BF16, logit_sd: float = 2.0, c: Optional[int] = None) -> SampleCase:
+    c = 100 + s if c is None else c
+    return SampleCase(f"sample{s}-n{n}-D{D}-p{n_prev}", n, D, levels,
+                      logits=draw(c, 0, "logits", (n,), 0.0, logit_sd, logit_dtype), logit_dtype=logit_dtype,
+                      gumbel=gumbel(seed(c, 0, "gumbel"), (32, n)),
+                      table=draw(c, 0, "table", (levels, n, D), 0.0, 1.0, emb_dtype),
+                      prefix=draw(c, 0, "prefix", (n_prev, D), 0.0, 1.0, emb_dtype), emb_dtype=emb_dtype)
+
+
+def sample_workload() -> SampleCase:
+    case = sample_case(0, 2048, 1024, 16, levels=4, c=8)
+    case.name = "sample-n2048-D1024-p16"
+    return case

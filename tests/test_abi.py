@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
-                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read"):
+                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample"):
         assert must in names
 
 
@@ -164,10 +164,10 @@ def test_chain_argument_errors(q):
 
 
 def test_dispatch_counter_range(q):
-    assert q.qlin_dispatch_count(6) == -1
+    assert q.qlin_dispatch_count(7) == -1
     assert q.qlin_dispatch_count(-1) == -1
     assert q.qlin_dispatch_count(0) >= 0
-    assert q.qlin_dispatch_count(5) >= 0
+    assert q.qlin_dispatch_count(6) >= 0
 
 
 # attend: qkv, kv, out, kv_out at fake, 16-byte aligned addresses far apart
@@ -249,3 +249,27 @@ def test_mlp_validation(q):
              q.QLIN_BF16, None) == -7
     assert f(X, q.QLIN_BF16, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, None, H, H + 64,
              q.QLIN_BF16, None) == -7
+
+
+def test_sample_validation(q):
+    f = q.lib().qlin_sample
+    L, G, TB, P, O, C = (0x5000000 + 0x100000 * i for i in range(6))
+    ok = dict(logits=L, dt=q.QLIN_BF16, n=2048, g=G, it=1.0, k=50, table=TB, prefix=P, n_prev=4, D=1024,
+              edt=q.QLIN_BF16, out=O, code=C)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["logits"], a["dt"], a["n"], a["g"], ctypes.c_float(a["it"]), a["k"], a["table"], a["prefix"],
+                 a["n_prev"], a["D"], a["edt"], a["out"], a["code"], None)
+    # only invalid calls here: a valid one would launch on fake addresses
+    assert call(logits=None) == -1 and call(g=None) == -1 and call(code=None) == -1
+    assert call(n=0) == -2 and call(n=8193) == -2 and call(k=0) == -2 and call(k=2049) == -2
+    assert call(D=4) == -2            # 8 bytes per row: not a multiple of 16
+    assert call(n_prev=-1) == -2
+    assert call(dt=7) == -3 and call(edt=9) == -3
+    assert call(it=0.0) == -7 and call(it=float("inf")) == -7 and call(it=float("nan")) == -7
+    assert call(logits=L + 1) == -5 and call(out=O + 8) == -5 and call(table=TB + 8) == -5
+    assert call(prefix=None) == -1 and call(out=None) == -1
+    assert call(out=P + 16) == -7     # overlaps the prefix without being it
+    assert call(out=TB + 64) == -7    # overlaps the table
+    assert call(code=L + 8) == -7     # code inside the logits
