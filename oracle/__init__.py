@@ -74,6 +74,8 @@ def load():
     lib.orc_attend.restype = i32
     lib.orc_sample.argtypes = [vp, i32, i64, vp, ctypes.c_float, i64, vp, vp, i64, i64, i64, vp, vp, vp]
     lib.orc_sample.restype = i32
+    lib.orc_kvq_decode.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, vp]
+    lib.orc_kvq_decode.restype = i32
     _lib = lib
     return lib
 
@@ -284,3 +286,20 @@ def sample(logits, dtype: int, gumbel, inv_temp: float, top_k: int, table=None, 
     if rc != 0:
         raise ValueError("oracle.sample: unsupported arguments")
     return int(code[0]), out, int(kept[0])
+
+
+def kvq_decode(q, q_dtype: int, k, v, sb_dtype: int, kv_heads: int, group: int, bits: int) -> np.ndarray:
+    """[p3] fused-decode-kernel.ts: attention of one query position per head over a quantized
+    K/V cache.  q (H, D) bit patterns; k, v: (codes (KV, N, D*bits/32) uint32, scales,
+    biases (KV, N, D/group) bit patterns of sb_dtype).  Returns out (H, D) fp64."""
+    q = _c(q, np.uint16)
+    H, D = q.shape
+    kc, ks, kb = (_c(k[0], np.uint32), _c(k[1], np.uint16), _c(k[2], np.uint16))
+    vc, vs, vb = (_c(v[0], np.uint32), _c(v[1], np.uint16), _c(v[2], np.uint16))
+    N = kc.shape[1]
+    out = np.empty((H, D), np.float64)
+    rc = load().orc_kvq_decode(_p(q), q_dtype, _p(kc), _p(ks), _p(kb), _p(vc), _p(vs), _p(vb), sb_dtype, H,
+                               kv_heads, N, D, group, bits, _p(out))
+    if rc != 0:
+        raise ValueError("oracle.kvq_decode: unsupported arguments")
+    return out

@@ -24,6 +24,7 @@
 //              softmax attention of the new positions over it (at most 32 positions)
 //   sample   = exact top-k by the logits' order-preserving keys (ties with the k-th kept),
 //              Gumbel-max over the kept codes, and the chosen code's embedding appended
+//   kvq      = one query position's attention over an affine-quantized K/V cache
 // Everything is computed in double precision from the exact bit patterns the GPU
 // receives.  Build: g++ -O2 -std=c++17 -fPIC -shared -ffp-contract=off (no fast-math).
 //
@@ -453,6 +454,53 @@ int orc_sample(const void* logits, int dtype, int64_t n, const float* gumbel, fl
   if (table) {
     if (best >= 0) std::memcpy(o + (size_t)n_prev * row, static_cast<const unsigned char*>(table) + (size_t)best * row, row);
     else std::memset(o + (size_t)n_prev * row, 0, row);
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// kvq decode — [p3] mlx-bun 0.0.10 -> 0.0.12, model/fused-decode-kernel.ts: attention of one
+// query position over a quantized K/V cache (the kernel's own split into blocks and merge
+// is a schedule; this is the plain definition it computes).
+//   K[c, n, d] = qk * sk[c, n, d / GS] + bk[c, n, d / GS]      (affine, exact in fp64)
+//   V[c, n, d] likewise
+//   s[h, n]    = sum_d q[h, d] K[c, n, d]          c = h / (H / KV)  (query heads share KV heads)
+//   out[h, d]  = sum_n softmax_n(s[h, .]) V[c, n, d]
+// q arrives already scaled (the page's kernel applies no 1/sqrt(D)).  Codes: element d of
+// a row at word d / (32 / bits), bits (d mod (32 / bits)) * bits, low bits first.
+// q: (H, D) bit patterns of q_dtype; scales/biases bit patterns of sb_dtype (1 fp16, 2 bf16).
+// ---------------------------------------------------------------------------
+int orc_kvq_decode(const uint16_t* q, int q_dtype, const uint32_t* kc, const uint16_t* ks, const uint16_t* kb,
+                   const uint32_t* vc, const uint16_t* vs, const uint16_t* vb, int sb_dtype, int64_t H, int64_t KV,
+                   int64_t N, int64_t D, int64_t GS, int bits, double* out) {
+  if (H < 1 || KV < 1 || H % KV != 0 || N < 1 || D < 1 || GS < 1 || D % GS != 0 || (bits != 4 && bits != 8) ||
+      D % (32 / bits) != 0)
+    return -1;
+  auto val = [](uint16_t b, int dt) { return dt == 1 ? f16_to_f64(b) : bf16_to_f64(b); };
+  const int64_t per = 32 / bits, words = D / per, groups = D / GS, rep = H / KV;
+  const uint32_t mask = (1u << bits) - 1u;
+  auto deq = [&](const uint32_t* c, const uint16_t* s, const uint16_t* b, int64_t kvh, int64_t n, int64_t d) {
+    const int64_t row = kvh * N + n;
+    const uint32_t code = (c[row * words + d / per] >> ((d % per) * bits)) & mask;
+    return (double)code * val(s[row * groups + d / GS], sb_dtype) + val(b[row * groups + d / GS], sb_dtype);
+  };
+  std::vector<double> sc((size_t)N);
+  for (int64_t h = 0; h < H; ++h) {
+    const int64_t c = h / rep;
+    double m = -std::numeric_limits<double>::infinity();
+    for (int64_t n = 0; n < N; ++n) {
+      double a = 0.0;
+      for (int64_t d = 0; d < D; ++d) a += val(q[h * D + d], q_dtype) * deq(kc, ks, kb, c, n, d);
+      sc[(size_t)n] = a;
+      if (a > m) m = a;
+    }
+    double z = 0.0;
+    for (int64_t n = 0; n < N; ++n) { sc[(size_t)n] = std::exp(sc[(size_t)n] - m); z += sc[(size_t)n]; }
+    for (int64_t d = 0; d < D; ++d) {
+      double o = 0.0;
+      for (int64_t n = 0; n < N; ++n) o += sc[(size_t)n] / z * deq(vc, vs, vb, c, n, d);
+      out[h * D + d] = o;
+    }
   }
   return 0;
 }
