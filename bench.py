@@ -22,7 +22,8 @@ pure read reaches on this device, next to which the fused call's rate can be rea
 Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
 with 32 rows), the 124-pass LN+linear chain (hipGraph replay vs eager launches), the whole
 MLP around the headline projection (qlin_mlp: gate/up then down with the residual), one
-attend pass, one sampling step (qlin_sample), and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
+attend pass, one sampling step (qlin_sample), one quantized-KV decode attention step
+(qlin_kvq_decode), and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
 the workload.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--only-main]
@@ -275,6 +276,36 @@ def bench_sample(steps, warmup):
                 gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
 
 
+def bench_kvq(steps, warmup):
+    """One decode step of attention over a quantized K/V cache (qlin_kvq_decode: 16 query
+    heads on 8 KV heads, head_dim 256, 8192 rows, 4-bit groups of 64), the cache rotated over
+    >= 1 GiB of copies; bytes are the cache (codes, scales, biases of K and V, read once
+    each), q and the output."""
+    import synth
+    from decode_linear_amd import qlin_kvq_decode
+    torch = _torch()
+    c = synth.kvq_workload()
+    q = _dev(c.q, c.q_dtype)
+
+    def dev_cache(t):
+        return (torch.from_numpy(t[0].view(np.int32)).cuda(), _dev(t[1], c.sb_dtype), _dev(t[2], c.sb_dtype))
+    k0, v0 = dev_cache(c.k), dev_cache(c.v)
+    cache_bytes = sum(t.numel() * t.element_size() for t in k0 + v0)
+    n_copies = max(2, -(-ROTATE_BYTES // cache_bytes))
+    caches = [(k0, v0)] + [(tuple(t.clone() for t in k0), tuple(t.clone() for t in v0)) for _ in range(n_copies - 1)]
+    out = torch.empty((c.H, c.D), dtype=torch.bfloat16, device="cuda")
+    from decode_linear_amd.qlin import lib
+    ws = torch.empty(int(lib().qlin_kvq_decode_workspace(c.H, c.N, c.D)) // 4, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        qlin_kvq_decode(q, caches[i][0], caches[i][1], c.KV, c.GS, c.bits, out=out, workspace=ws)
+
+    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    nbytes = cache_bytes + 2 * c.H * c.D * 2
+    return dict(name=c.name, H=c.H, KV=c.KV, N=c.N, D=c.D, bits=c.bits, group=c.GS, cache_bytes=cache_bytes,
+                copies=n_copies, dispatches=2, us=us, gbs=nbytes / (us * 1e-6) / 1e9)
+
+
 def bench_chain(replays, warmup):
     """124 dependent LN + linear passes (8-bit, K=N=1024, T = 1 + p mod 8): graph replay
     and eager launches, rotated over >= 1 GiB of chain copies."""
@@ -402,7 +433,8 @@ def main():
             extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
         ch = bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))
         extra[ch["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ch.items() if k != "name"}
-        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup), bench_sample(a.steps, a.warmup)):
+        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup), bench_sample(a.steps, a.warmup),
+                  bench_kvq(a.steps, a.warmup)):
             extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
             extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
     us = main_r["us"]

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libqlin.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qlin_host.cpp", "qlin_pack.hip", "qlin_attend.hip", "qlin_stream.hip", "qlin_sample.hip", "qlin_fused_q4.hip", "qlin_fused_q8.hip",
+SOURCES = ["qlin_host.cpp", "qlin_pack.hip", "qlin_attend.hip", "qlin_stream.hip", "qlin_sample.hip", "qlin_kvq.hip", "qlin_fused_q4.hip", "qlin_fused_q8.hip",
            "qlin_fused_f16.hip", "qlin_fused_bf16.hip"]
 
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -89,6 +89,26 @@ struct SampleParams {
 };
 hipError_t launch_sample(const SampleParams& a, hipStream_t s);
 
+// Arguments of one quantized-KV decode attention (block partials + merge).
+struct KvqParams {
+  const void* q;            // (H, D), q_dtype
+  int q_dtype;              // 1 fp16, 2 bf16
+  const uint32_t* kc;       // (KV, N, D * bits / 32)
+  const void* ks;           // (KV, N, D / GS), sb_dtype
+  const void* kb;
+  const uint32_t* vc;
+  const void* vs;
+  const void* vb;
+  int sb_dtype;             // 1 fp16, 2 bf16
+  int H, KV, N, D, GS, bits;
+  int block, G;             // rows per block, blocks
+  float* opart;             // (H, G, D) workspace
+  float* stats;             // (H, G, 2) workspace: block max, block sum
+  void* out;                // (H, D), out_dtype
+  int out_dtype;            // 0 fp32, 1 fp16, 2 bf16
+};
+hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s);
+
 // Plain 16-byte streaming read of `bytes` (a multiple of 16) at buf; block b writes the XOR
 // fold of the words it read to partial[b] (grid blocks of 512 threads).
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int grid, hipStream_t s);

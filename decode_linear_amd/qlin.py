@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_mlp, qlin_sample, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
+qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
 qlin_dispatch_count,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
@@ -80,13 +80,17 @@ def lib():
     L.qlin_stream_read.argtypes = [vp, i64, vp, vp]
     L.qlin_mlp.argtypes = [vp, i32, i32, W, W, W, Ln, vp, vp, vp, i32, vp]
     L.qlin_sample.argtypes = [vp, i32, i32, vp, ctypes.c_float, i32, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.qlin_kvq_decode_workspace.argtypes = [i32, i32, i32]
+    L.qlin_kvq_decode_workspace.restype = i64
+    L.qlin_kvq_decode.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp,
+                                  i32, vp]
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
-                 "qlin_stream_read", "qlin_mlp", "qlin_sample"):
+                 "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -348,3 +352,28 @@ def qlin_sample(logits: torch.Tensor, gumbel: torch.Tensor, level: int, table: O
                            _ptr(prefix), n_prev, D, _TORCH_TO_QLIN[edt], _ptr(out), _ptr(code), _stream(stream))
     _check(st, "qlin_sample")
     return code, out
+
+
+def qlin_kvq_decode(q: torch.Tensor, k, v, kv_heads: int, group: int, bits: int, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Attention of one query position per head over a quantized K/V cache: q (H, D); k, v =
+    (codes (KV, N, D*bits/32) int32, scales, biases (KV, N, D/group) fp16 or bf16).  Returns
+    out (H, D)."""
+    H, D = q.shape
+    kc, ks, kb = k
+    vc, vs, vb = v
+    N = kc.shape[1]
+    need = int(lib().qlin_kvq_decode_workspace(H, N, D))
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((H, D), dtype=out_dtype or q.dtype, device=q.device)
+    for t in (q, kc, ks, kb, vc, vs, vb, out):
+        if not t.is_contiguous():
+            raise ValueError("qlin_kvq_decode: tensors must be contiguous")
+    st = lib().qlin_kvq_decode(_ptr(q), _dtype(q), H, kv_heads, N, D, group, bits, _ptr(kc), _ptr(ks), _ptr(kb),
+                               _ptr(vc), _ptr(vs), _ptr(vb), _dtype(ks), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(out), _dtype(out),
+                               _stream(stream))
+    _check(st, "qlin_kvq_decode")
+    return out

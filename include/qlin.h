@@ -243,6 +243,32 @@ qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, c
                         int32_t top_k, const void* table, const void* prefix, int32_t n_prev, int32_t D,
                         qlin_dtype emb_dtype, void* out, int32_t* code, void* stream);
 
+/* Attention of one query position per head over an affine-quantized K/V cache ([p3]
+ * mlx-bun 0.0.10 -> 0.0.12, model/fused-decode-kernel.ts, flash decoding split over rows):
+ *     s[h, n]   = sum_d q[h, d] K[c, n, d],    c = h / (heads / kv_heads)
+ *     out[h, d] = sum_n softmax_n(s[h, .]) V[c, n, d]
+ * with K (and V) = code * scale + bias per group of group_size elements along d (the weight
+ * format above, rows of head_dim elements).  q arrives already scaled (no 1/sqrt(head_dim)
+ * is applied).  Computed in fp32 (online softmax per block of rows, then a merge of the
+ * blocks in order) and rounded once to out_dtype.  Two dispatches; no atomics.
+ *   q          (heads, head_dim) of q_dtype (QLIN_F16 or QLIN_BF16), 2-byte aligned.
+ *   heads      1..65536, a multiple of kv_heads;  n_rows 1..2^24;  head_dim 64, 128, 256 or
+ *              512;  group_size 32, 64 or 128 (<= head_dim);  bits 4 or 8.
+ *   k_codes    (kv_heads, n_rows, head_dim*bits/32) uint32, 4-byte aligned; k_scales,
+ *              k_biases (kv_heads, n_rows, head_dim/group_size) of sb_dtype (QLIN_F16 or
+ *              QLIN_BF16); v_* likewise.
+ *   workspace  device scratch of at least qlin_kvq_decode_workspace(heads, n_rows, head_dim)
+ *              bytes, 4-byte aligned, owned by the caller (partials of the row blocks).
+ *   out        (heads, head_dim) of out_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16); it must not
+ *              overlap the inputs or the workspace.
+ * Errors as for qlin_linear, before any HIP call (QLIN_ERR_ARG for a small workspace). */
+int64_t qlin_kvq_decode_workspace(int32_t heads, int32_t n_rows, int32_t head_dim);
+qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads, int32_t n_rows,
+                            int32_t head_dim, int32_t group_size, int32_t bits, const uint32_t* k_codes,
+                            const void* k_scales, const void* k_biases, const uint32_t* v_codes,
+                            const void* v_scales, const void* v_biases, qlin_dtype sb_dtype, void* workspace,
+                            int64_t workspace_bytes, void* out, qlin_dtype out_dtype, void* stream);
+
 /* ---- measurement aid ----------------------------------------------------------------
  * qlin_stream_read: the device's streaming-read ceiling for the weight stream's access (the
  * "HBM bandwidth" the pages' 8-bit-versus-fp16 timing comparison of the maya-mac depth
@@ -260,8 +286,9 @@ qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, c
 qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream);
 
 /* Number of kernels this library has enqueued in this process, by entry point:
- * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample (a
- * test can assert a kernel ran; qlin_mlp counts one gate/up and one linear). */
+ * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample,
+ * 7 = quantized-KV decode (a test can assert a kernel ran; qlin_mlp counts one gate/up and
+ * one linear). */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Static description of a status code. */

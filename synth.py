@@ -31,6 +31,9 @@ N(0, 1/K) whose 1/K is the variance):
   8  one sampling step of the depth decoder: 2048 codes, logits bf16 N(0, 2), Gumbel(0, 1)
      noise for 32 levels (fp32), code embeddings bf16 N(0, 1) of width 1024 for 4 levels,
      a prefix of 16 rows
+  9  one decode step of attention over a quantized K/V cache: 16 query heads sharing 8 KV
+     heads, head_dim 256, 8192 cached rows, 4-bit codes in groups of 64 (uniform random
+     code words), scales bf16 0.05 U(0.5, 1.5), biases bf16 -0.4 U(0, 1); q bf16 N(0, 1/D)
 """
 from __future__ import annotations
 
@@ -43,7 +46,8 @@ F32, F16, BF16 = 0, 1, 2
 NP_CODES = {F32: np.float32}
 
 TENSOR_IDS = {"x": 1, "w": 2, "up": 3, "gamma": 4, "beta": 5, "res": 6, "add": 7, "qkv": 8, "kv": 9, "down": 10,
-              "logits": 11, "gumbel": 12, "table": 13, "prefix": 14}
+              "logits": 11, "gumbel": 12, "table": 13, "prefix": 14, "kcodes": 15, "ks": 16, "kb": 17,
+              "vcodes": 18, "vs": 19, "vb": 20}
 CHAIN_PASSES = 124
 CHAIN_K = CHAIN_N = 1024
 CHAIN_TMAX = 8
@@ -332,4 +336,45 @@ def sample_case(s: int, n: int, D: int, n_prev: int, levels: int = 2, logit_dtyp
 def sample_workload() -> SampleCase:
     case = sample_case(0, 2048, 1024, 16, levels=4, c=8)
     case.name = "sample-n2048-D1024-p16"
+    return case
+
+
+@dataclass
+class KvqCase:
+    name: str
+    H: int
+    KV: int
+    N: int
+    D: int
+    GS: int
+    bits: int
+    q_dtype: int
+    sb_dtype: int
+    q: np.ndarray             # (H, D) bit patterns
+    k: tuple                  # (codes (KV, N, D*bits/32) uint32, scales, biases bit patterns)
+    v: tuple
+
+
+def kvq_case(s: int, H: int, KV: int, N: int, D: int, GS: int, bits: int, q_dtype: int = BF16,
+             sb_dtype: int = BF16, q_sd: Optional[float] = None, c: Optional[int] = None) -> KvqCase:
+    """Codes are uniform random 32-bit words (every word is a valid packing of codes)."""
+    c = 100 + s if c is None else c
+    words = D * bits // 32
+
+    def cache(tag):
+        rng = np.random.Generator(np.random.PCG64(seed(c, 0, tag + "codes")))
+        codes = rng.integers(0, 2 ** 32, (KV, N, words), dtype=np.uint64).astype(np.uint32)
+        u = np.random.Generator(np.random.PCG64(seed(c, 0, tag + "s"))).uniform(0.5, 1.5, (KV, N, D // GS))
+        b = np.random.Generator(np.random.PCG64(seed(c, 0, tag + "b"))).uniform(0.0, 1.0, (KV, N, D // GS))
+        lo = 0.05 * (2 ** bits - 1) / 2
+        return codes, to_bits(0.05 * u * (15.0 / (2 ** bits - 1)), sb_dtype), to_bits(-lo * b * (15.0 / (2 ** bits - 1)), sb_dtype)
+
+    sd = 1.0 / np.sqrt(D) if q_sd is None else q_sd
+    return KvqCase(f"kvq{s}-H{H}-KV{KV}-N{N}-D{D}-g{GS}-b{bits}", H, KV, N, D, GS, bits, q_dtype, sb_dtype,
+                   q=draw(c, 0, "x", (H, D), 0.0, sd, q_dtype), k=cache("k"), v=cache("v"))
+
+
+def kvq_workload() -> KvqCase:
+    case = kvq_case(0, 16, 8, 8192, 256, 64, 4, c=9)
+    case.name = "kvq-decode-H16-KV8-D256-N8192-q4g64"
     return case

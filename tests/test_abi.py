@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
-                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample"):
+                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
         assert must in names
 
 
@@ -164,10 +164,10 @@ def test_chain_argument_errors(q):
 
 
 def test_dispatch_counter_range(q):
-    assert q.qlin_dispatch_count(7) == -1
+    assert q.qlin_dispatch_count(8) == -1
     assert q.qlin_dispatch_count(-1) == -1
     assert q.qlin_dispatch_count(0) >= 0
-    assert q.qlin_dispatch_count(6) >= 0
+    assert q.qlin_dispatch_count(7) >= 0
 
 
 # attend: qkv, kv, out, kv_out at fake, 16-byte aligned addresses far apart
@@ -273,3 +273,26 @@ def test_sample_validation(q):
     assert call(out=P + 16) == -7     # overlaps the prefix without being it
     assert call(out=TB + 64) == -7    # overlaps the table
     assert call(code=L + 8) == -7     # code inside the logits
+
+
+def test_kvq_validation(q):
+    f, ws = q.lib().qlin_kvq_decode, q.lib().qlin_kvq_decode_workspace
+    assert ws(16, 8192, 256) == 16 * 64 * 258 * 4 and ws(2, 100, 128) == 2 * 1 * 130 * 4 and ws(0, 1, 64) == 0
+    assert ws(1, 128 * 8192 + 1, 64) == 1 * 2049 * 66 * 4
+    Q, KC, KS, KB, VC, VS, VB, WS, O = (0x9000000 + 0x1000000 * i for i in range(9))
+    ok = dict(q=Q, qdt=q.QLIN_BF16, H=16, KV=8, N=8192, D=256, GS=64, bits=4, kc=KC, ks=KS, kb=KB, vc=VC, vs=VS,
+              vb=VB, sbdt=q.QLIN_BF16, ws=WS, wsb=ws(16, 8192, 256), out=O, odt=q.QLIN_BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["qdt"], a["H"], a["KV"], a["N"], a["D"], a["GS"], a["bits"], a["kc"], a["ks"], a["kb"],
+                 a["vc"], a["vs"], a["vb"], a["sbdt"], a["ws"], a["wsb"], a["out"], a["odt"], None)
+    # only invalid calls here: a valid one would launch on fake addresses
+    assert call(q=None) == -1 and call(vb=None) == -1 and call(ws=None) == -1 and call(out=None) == -1
+    assert call(qdt=q.QLIN_F32) == -3 and call(sbdt=q.QLIN_F32) == -3 and call(odt=5) == -3
+    assert call(bits=2) == -4
+    assert call(H=12) == -2 and call(KV=0) == -2 and call(N=0) == -2 and call(D=96) == -2 and call(GS=16) == -2
+    assert call(D=64, GS=128) == -2
+    assert call(q=Q + 1) == -5 and call(kc=KC + 2) == -5 and call(ws=WS + 2) == -5 and call(out=O + 1) == -5
+    assert call(wsb=ws(16, 8192, 256) - 4) == -7
+    assert call(out=WS + 64) == -7 and call(out=KC + 64) == -7
