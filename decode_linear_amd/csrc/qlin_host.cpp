@@ -439,7 +439,7 @@ qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, in
     return QLIN_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return QLIN_ERR_SHAPE;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || group_size > head_dim) return QLIN_ERR_SHAPE;
-  if (!aligned(q, 2) || !aligned(k_codes, 4) || !aligned(v_codes, 4) || !aligned(k_scales, 2) ||
+  if (!aligned(q, 2) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 2) ||
       !aligned(k_biases, 2) || !aligned(v_scales, 2) || !aligned(v_biases, 2) || !aligned(workspace, 4) ||
       !aligned(out, dtype_size(out_dtype)))
     return QLIN_ERR_ALIGN;

@@ -7,12 +7,13 @@
 //   out[h, d] = sum_n softmax_n(s[h, .]) V[c, n, d]
 //
 // The rows are split into G blocks (flash decoding).  block_kernel, one workgroup per
-// (block, head): each of its 4 waves walks the block's rows four at a time (their loads
-// issued together);
-// lane l holds elements d = E l .. E l + E - 1 (E = D / 64, inside one group), so the
-// dequantization is factored out of the dot product like the pages' qdot pattern
-// (s = scale sum q code + bias sum q), the row score is an xor butterfly over the wave, and
-// an online softmax keeps a running maximum, sum and value accumulator.  The waves merge in
+// (block, head): a wave takes 64 / L rows per step, L = (bytes of a row of codes) / 16
+// lanes per row, each lane one 16-byte slice (32 4-bit or 16 8-bit codes, inside one
+// quantization group), so the dequantization factors out of the dot product like the
+// pages' qdot pattern (s = scale sum q code + bias sum q); the row's score is an xor
+// butterfly over its L lanes, and an online softmax over the step's rows keeps a running
+// maximum, weight sum and per-slice value accumulator, summed over the row slots at the
+// end of the block.  The waves merge in
 // LDS in a fixed order into the block's unnormalized output and (max, sum).  merge_kernel
 // combines the blocks in block order.  No atomics: the result is bitwise reproducible.
 #include <hip/hip_runtime.h>
@@ -25,7 +26,7 @@ namespace {
 
 constexpr int kKvqThreads = 256;
 constexpr int kKvqWaves = kKvqThreads / 64;
-constexpr int kKvqRows = 4;   // rows a wave takes per step
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float half_to_float(uint16_t b, int dtype) {
   if (dtype == 1) return (float)__builtin_bit_cast(_Float16, b);
@@ -37,99 +38,80 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return v;
 }
 
-// The E codes of lane l in row `row` (E * BITS <= 64 bits, aligned to their size).
-template <int BITS, int E>
-__device__ __forceinline__ void row_codes(const uint32_t* __restrict__ c, long row, int words, int lane, float out[E]) {
-  constexpr uint32_t mask = (1u << BITS) - 1u;
-  const long bit = (long)lane * E * BITS;
-  if constexpr (E * BITS <= 32) {
-    const uint32_t w = c[row * words + (bit >> 5)];
-    const int sh = (int)(bit & 31);
-#pragma unroll
-    for (int e = 0; e < E; ++e) out[e] = (float)((w >> (sh + e * BITS)) & mask);
-  } else {
-    const uint32_t w0 = c[row * words + (bit >> 5)], w1 = c[row * words + (bit >> 5) + 1];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t w = e * BITS < 32 ? w0 : w1;
-      out[e] = (float)((w >> ((e * BITS) & 31)) & mask);
-    }
-  }
-}
-
-template <int BITS, int E>
+template <int BITS, int D>
 __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
-  constexpr int D = 64 * E;
+  constexpr int RB = D * BITS / 8;      // bytes of a row of codes
+  constexpr int LPR = RB / 16;          // lanes per row: each takes 16 bytes
+  constexpr int R = 64 / LPR;           // rows a wave takes per step
+  constexpr int EL = 128 / BITS;        // elements per lane (inside one quantization group)
+  constexpr int E = D / 64;             // elements per lane in the merge
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  static_assert(LPR >= 2 && LPR <= 32 && EL * LPR == D, "16-byte lane slices");
   __shared__ float tg_max[kKvqWaves], tg_sum[kKvqWaves];
   __shared__ float tg_o[kKvqWaves * D];
   const int g = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane / LPR, j = lane % LPR;   // row slot, slice of the row
   const int c = h / (a.H / a.KV);
   const int start = g * a.block, end = min(start + a.block, a.N);
-  const int words = D * BITS / 32, groups = D / a.GS, gi = (lane * E) / a.GS;
+  const int groups = D / a.GS, gi = (j * EL) / a.GS;
   const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
   const uint16_t* ks = static_cast<const uint16_t*>(a.ks);
   const uint16_t* kb = static_cast<const uint16_t*>(a.kb);
   const uint16_t* vs = static_cast<const uint16_t*>(a.vs);
   const uint16_t* vb = static_cast<const uint16_t*>(a.vb);
-  float qv[E], qsum = 0.0f;
+  const u4_t* kc = reinterpret_cast<const u4_t*>(a.kc);
+  const u4_t* vc = reinterpret_cast<const u4_t*>(a.vc);
+  float qv[EL], qsum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    qv[e] = half_to_float(q16[(long)h * D + lane * E + e], a.q_dtype);
+  for (int e = 0; e < EL; ++e) {
+    qv[e] = half_to_float(q16[(long)h * D + j * EL + e], a.q_dtype);
     qsum += qv[e];
   }
-  float mx = -__builtin_inff(), sum = 0.0f, o[E];
+  float mx = -__builtin_inff(), lsum = 0.0f, o[EL];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.0f;
-  // wave wv takes rows start + U wv + 4 U j + u (u < U): the U rows' loads are all issued
-  // before their scores are reduced, and their online-softmax update is one step
-  for (int n0 = start + kKvqRows * wv; n0 < end; n0 += kKvqWaves * kKvqRows) {
-    float kcode[kKvqRows][E], vcode[kKvqRows][E], ksc[kKvqRows], kbi[kKvqRows], vsc[kKvqRows], vbi[kKvqRows];
+  for (int e = 0; e < EL; ++e) o[e] = 0.0f;
+  for (int n0 = start + R * wv; n0 < end; n0 += kKvqWaves * R) {
+    const int n = n0 + slot;
+    const bool live = n < end;
+    const long row = (long)c * a.N + (live ? n : end - 1);   // rows past the block: masked below
+    const u4_t kw = kc[row * LPR + j], vw = vc[row * LPR + j];
+    const float ksc = half_to_float(ks[row * groups + gi], a.sb_dtype), kbi = half_to_float(kb[row * groups + gi], a.sb_dtype);
+    const float vsc = half_to_float(vs[row * groups + gi], a.sb_dtype), vbi = half_to_float(vb[row * groups + gi], a.sb_dtype);
+    float dot = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kKvqRows; ++u) {
-      const long row = (long)c * a.N + min(n0 + u, end - 1);   // rows past the block: masked below
-      row_codes<BITS, E>(a.kc, row, words, lane, kcode[u]);
-      row_codes<BITS, E>(a.vc, row, words, lane, vcode[u]);
-      ksc[u] = half_to_float(ks[row * groups + gi], a.sb_dtype);
-      kbi[u] = half_to_float(kb[row * groups + gi], a.sb_dtype);
-      vsc[u] = half_to_float(vs[row * groups + gi], a.sb_dtype);
-      vbi[u] = half_to_float(vb[row * groups + gi], a.sb_dtype);
-    }
-    float s[kKvqRows];
+    for (int e = 0; e < EL; ++e) dot = fmaf(qv[e], (float)((kw[(e * BITS) >> 5] >> ((e * BITS) & 31)) & mask), dot);
+    float s = fmaf(ksc, dot, kbi * qsum);
 #pragma unroll
-    for (int u = 0; u < kKvqRows; ++u) {
-      float dot = 0.0f;
+    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);   // the row's score on its LPR lanes
+    float smax = live ? s : -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < E; ++e) dot = fmaf(qv[e], kcode[u][e], dot);
-      s[u] = wave_sum64(fmaf(ksc[u], dot, kbi[u] * qsum));
-    }
-    float m = mx;
+    for (int m = LPR; m < 64; m <<= 1) smax = fmaxf(smax, __shfl_xor(smax, m, 64));   // over the step's rows
+    const float mnew = fmaxf(mx, smax);
+    const float f = expf(mx - mnew), p = live ? expf(s - mnew) : 0.0f;
+    lsum = fmaf(lsum, f, j == 0 ? p : 0.0f);   // one lane per row carries its weight
+    mx = mnew;
 #pragma unroll
-    for (int u = 0; u < kKvqRows; ++u)
-      if (n0 + u < end) m = fmaxf(m, s[u]);
-    const float f = expf(mx - m);
-    float p[kKvqRows];
-#pragma unroll
-    for (int u = 0; u < kKvqRows; ++u) p[u] = n0 + u < end ? expf(s[u] - m) : 0.0f;
-    float ps = sum * f;
-#pragma unroll
-    for (int u = 0; u < kKvqRows; ++u) ps += p[u];
-    sum = ps;
-    mx = m;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float acc = o[e] * f;
-#pragma unroll
-      for (int u = 0; u < kKvqRows; ++u) acc = fmaf(p[u], fmaf(vcode[u][e], vsc[u], vbi[u]), acc);
-      o[e] = acc;
+    for (int e = 0; e < EL; ++e) {
+      const float v = fmaf((float)((vw[(e * BITS) >> 5] >> ((e * BITS) & 31)) & mask), vsc, vbi);
+      o[e] = fmaf(o[e], f, p * v);
     }
   }
+  // sum over the row slots: lanes of one slice, then the wave's weight sum
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < EL; ++e) o[e] += __shfl_xor(o[e], m, 64);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m, 64);
   if (lane == 0) {
     tg_max[wv] = mx;
-    tg_sum[wv] = sum;
+    tg_sum[wv] = lsum;
   }
+  if (slot == 0) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) tg_o[wv * D + lane * E + e] = o[e];
+    for (int e = 0; e < EL; ++e) tg_o[wv * D + j * EL + e] = o[e];
+  }
   __syncthreads();
   if (wv == 0) {
     float M = tg_max[0];
@@ -154,34 +136,77 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
   }
 }
 
-// out[h, d] = sum_g opart[h, g, d] e^(M_g - M) / sum_g S_g e^(M_g - M), blocks in order.
-__global__ __launch_bounds__(512) void merge_kernel(const KvqParams a) {
-  const int h = blockIdx.x, d = threadIdx.x, D = a.D;
-  if (d >= D) return;
-  const float* st = a.stats + (long)h * a.G * 2;
-  float M = st[0];
-  for (int g = 1; g < a.G; ++g) M = fmaxf(M, st[2 * g]);
-  float den = 0.0f, o = 0.0f;
-  for (int g = 0; g < a.G; ++g) {
-    const float w = expf(st[2 * g] - M);
-    den = fmaf(st[2 * g + 1], w, den);
-    o = fmaf(a.opart[((long)h * a.G + g) * D + d], w, o);
+// out[h, d] = sum_g opart[h, g, d] e^(M_g - M) / sum_g S_g e^(M_g - M), one workgroup per
+// head.  M and the denominator are fixed-order reductions (thread t takes blocks t, t + 256,
+// ... in order, then the 256 partials are combined in thread order); the block weights
+// e^(M_g - M) go to LDS in chunks, and each thread sums its columns over the blocks in block
+// order with the loads of a chunk independent of each other.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 4096;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const KvqParams a) {
+  __shared__ float part[kMergeThreads];
+  __shared__ float wgt[kMergeChunk];
+  __shared__ float sh_m, sh_den;
+  const int h = blockIdx.x, t = threadIdx.x, D = a.D, G = a.G;
+  const float* st = a.stats + (long)h * G * 2;
+  float m = -__builtin_inff();
+  for (int g = t; g < G; g += kMergeThreads) m = fmaxf(m, st[2 * g]);
+  part[t] = m;
+  __syncthreads();
+  if (t == 0) {
+    float M = part[0];
+    for (int i = 1; i < kMergeThreads; ++i) M = fmaxf(M, part[i]);
+    sh_m = M;
   }
-  const float v = o / den;
-  const long idx = (long)h * D + d;
-  if (a.out_dtype == 0) static_cast<float*>(a.out)[idx] = v;
-  else if (a.out_dtype == 1) static_cast<_Float16*>(a.out)[idx] = (_Float16)v;
-  else static_cast<__bf16*>(a.out)[idx] = (__bf16)v;
+  __syncthreads();
+  const float M = sh_m;
+  float den = 0.0f;
+  for (int g = t; g < G; g += kMergeThreads) den = fmaf(st[2 * g + 1], expf(st[2 * g] - M), den);
+  __syncthreads();
+  part[t] = den;
+  __syncthreads();
+  if (t == 0) {
+    float s = 0.0f;
+    for (int i = 0; i < kMergeThreads; ++i) s += part[i];
+    sh_den = s;
+  }
+  float o0 = 0.0f, o1 = 0.0f;   // columns t and t + 256 (D <= 512)
+  const float* op = a.opart + (long)h * G * D;
+  for (int g0 = 0; g0 < G; g0 += kMergeChunk) {
+    const int gn = min(kMergeChunk, G - g0);
+    __syncthreads();   // the previous chunk's weights are read
+    for (int i = t; i < gn; i += kMergeThreads) wgt[i] = expf(st[2 * (g0 + i)] - M);
+    __syncthreads();
+    if (t < D) {
+#pragma unroll 8
+      for (int i = 0; i < gn; ++i) o0 = fmaf(op[(long)(g0 + i) * D + t], wgt[i], o0);
+    }
+    if (t + kMergeThreads < D) {
+#pragma unroll 8
+      for (int i = 0; i < gn; ++i) o1 = fmaf(op[(long)(g0 + i) * D + t + kMergeThreads], wgt[i], o1);
+    }
+  }
+  __syncthreads();
+  const float den_all = sh_den;
+  for (int k = 0; k < 2; ++k) {
+    const int d = t + k * kMergeThreads;
+    if (d >= D) continue;
+    const float v = (k == 0 ? o0 : o1) / den_all;
+    const long idx = (long)h * D + d;
+    if (a.out_dtype == 0) static_cast<float*>(a.out)[idx] = v;
+    else if (a.out_dtype == 1) static_cast<_Float16*>(a.out)[idx] = (_Float16)v;
+    else static_cast<__bf16*>(a.out)[idx] = (__bf16)v;
+  }
 }
 
 template <int BITS>
 hipError_t launch_block(const KvqParams& a, hipStream_t s) {
   const dim3 grid(a.G, a.H);
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((block_kernel<BITS, 1>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((block_kernel<BITS, 2>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((block_kernel<BITS, 4>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((block_kernel<BITS, 8>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512>), grid, dim3(kKvqThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -192,7 +217,7 @@ hipError_t launch_block(const KvqParams& a, hipStream_t s) {
 hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s) {
   const hipError_t e = a.bits == 4 ? launch_block<4>(a, s) : launch_block<8>(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.H), dim3(a.D), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.H), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -254,7 +254,7 @@ qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, c
  *   q          (heads, head_dim) of q_dtype (QLIN_F16 or QLIN_BF16), 2-byte aligned.
  *   heads      1..65536, a multiple of kv_heads;  n_rows 1..2^24;  head_dim 64, 128, 256 or
  *              512;  group_size 32, 64 or 128 (<= head_dim);  bits 4 or 8.
- *   k_codes    (kv_heads, n_rows, head_dim*bits/32) uint32, 4-byte aligned; k_scales,
+ *   k_codes    (kv_heads, n_rows, head_dim*bits/32) uint32, 16-byte aligned; k_scales,
  *              k_biases (kv_heads, n_rows, head_dim/group_size) of sb_dtype (QLIN_F16 or
  *              QLIN_BF16); v_* likewise.
  *   workspace  device scratch of at least qlin_kvq_decode_workspace(heads, n_rows, head_dim)

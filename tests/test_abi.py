@@ -293,6 +293,7 @@ def test_kvq_validation(q):
     assert call(bits=2) == -4
     assert call(H=12) == -2 and call(KV=0) == -2 and call(N=0) == -2 and call(D=96) == -2 and call(GS=16) == -2
     assert call(D=64, GS=128) == -2
-    assert call(q=Q + 1) == -5 and call(kc=KC + 2) == -5 and call(ws=WS + 2) == -5 and call(out=O + 1) == -5
+    assert call(q=Q + 1) == -5 and call(kc=KC + 4) == -5 and call(vc=VC + 8) == -5 and call(ws=WS + 2) == -5
+    assert call(out=O + 1) == -5
     assert call(wsb=ws(16, 8192, 256) - 4) == -7
     assert call(out=WS + 64) == -7 and call(out=KC + 64) == -7
