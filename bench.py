@@ -427,16 +427,21 @@ def main():
     ceil_r = read_ceiling(main_r["weight_bytes"], a.steps, a.warmup)
     extra = {}
     if not a.only_main:
-        for c in (1, 2, 3):
-            r = bench_linear(c, a.steps, a.warmup)
+        # each secondary workload is reported on its own: one that fails records its error
+        # and does not take the headline line down with it
+        runs = [(f"linear-config-{c}", lambda c=c: bench_linear(c, a.steps, a.warmup)) for c in (1, 2, 3)]
+        runs += [("chain", lambda: bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))),
+                 ("mlp", lambda: bench_mlp(a.steps, a.warmup)), ("attend", lambda: bench_attend(a.steps, a.warmup)),
+                 ("sample", lambda: bench_sample(a.steps, a.warmup)), ("kvq", lambda: bench_kvq(a.steps, a.warmup))]
+        for label, run in runs:
+            try:
+                r = run()
+            except Exception as exc:   # reported, not hidden: the line carries the error
+                extra[label] = {"error": f"{type(exc).__name__}: {exc}"}
+                continue
             extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
-            extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
-        ch = bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))
-        extra[ch["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ch.items() if k != "name"}
-        for r in (bench_mlp(a.steps, a.warmup), bench_attend(a.steps, a.warmup), bench_sample(a.steps, a.warmup),
-                  bench_kvq(a.steps, a.warmup)):
-            extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
-            extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
+            if "gbs" in r:
+                extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
     us = main_r["us"]
     achieved = main_r["weight_bytes"] / (us * 1e-6) / 1e9
     line = {
