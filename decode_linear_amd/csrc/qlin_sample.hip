@@ -15,7 +15,8 @@
 // counts do not depend on their order), and wave 0 scans the bins from the top with a lane
 // prefix sum to find the digit that holds the need-th largest key.  The argmax is a
 // per-thread scan, an xor butterfly over each wave (a total order on (score, index)) and a
-// fixed-order pass over the four waves.  The rows are copied with 16-byte accesses.
+// fixed-order pass over the four waves.  The rows are copied with 16-byte accesses, the
+// prefix first of all (it does not depend on the code).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,6 +57,23 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const SamplePara
   __shared__ int32_t sh_code;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = a.n;
+  // the prefix rows do not depend on the code: they are copied first, their loads in
+  // flight together, while the keys load and the selection runs
+  const long W = (long)a.D * a.es / 16;   // 16-byte pieces per row
+  u4_t* out = static_cast<u4_t*>(a.out);
+  if (a.copy_prefix) {
+    const u4_t* pre = static_cast<const u4_t*>(a.prefix);
+    const long total = (long)a.n_prev * W;
+    long v = tid;
+    for (; v + 7 * kSampleThreads < total; v += 8 * kSampleThreads) {
+      u4_t t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = pre[v + u * kSampleThreads];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) out[v + u * kSampleThreads] = t[u];
+    }
+    for (; v < total; v += kSampleThreads) out[v] = pre[v];
+  }
 
   uint32_t key[kSamplePerThread];
 #pragma unroll
@@ -154,13 +172,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const SamplePara
     *a.code = c;
   }
   __syncthreads();
-  // rows: the prefix (unless appending in place), then the code's table row
-  const long W = (long)a.D * a.es / 16;   // 16-byte pieces per row
-  u4_t* out = static_cast<u4_t*>(a.out);
-  if (a.copy_prefix) {
-    const u4_t* pre = static_cast<const u4_t*>(a.prefix);
-    for (long v = tid; v < (long)a.n_prev * W; v += kSampleThreads) out[v] = pre[v];
-  }
+  // the code's table row after the prefix
   if (a.table) {
     const int32_t c = sh_code;
     const u4_t* row = static_cast<const u4_t*>(a.table) + (long)(c < 0 ? 0 : c) * W;
