@@ -136,58 +136,74 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
   }
 }
 
+// A workgroup-wide reduction of one value per thread in a fixed order: an xor butterfly in
+// each wave, then the four waves' results in wave order, read by every thread.
+template <bool MAX>
+__device__ __forceinline__ float merge_reduce(float v, float* part) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = __shfl_xor(v, m, 64);
+    v = MAX ? fmaxf(v, o) : v + o;
+  }
+  __syncthreads();   // earlier readers of part are done
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = part[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) r = MAX ? fmaxf(r, part[w]) : r + part[w];
+  return r;
+}
+
 // out[h, d] = sum_g opart[h, g, d] e^(M_g - M) / sum_g S_g e^(M_g - M), one workgroup per
 // head.  M and the denominator are fixed-order reductions (thread t takes blocks t, t + 256,
-// ... in order, then the 256 partials are combined in thread order); the block weights
-// e^(M_g - M) go to LDS in chunks, and each thread sums its columns over the blocks in block
-// order with the loads of a chunk independent of each other.
+// ... in order, then merge_reduce: a butterfly per wave and the waves in order; one thread
+// walking 256 LDS partials cost about 2.5 us); the block weights e^(M_g - M) go to LDS in
+// chunks, and each thread sums its columns over the blocks in block order with the loads of
+// a chunk independent of each other.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeChunk = 4096;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const KvqParams a) {
   __shared__ float part[kMergeThreads];
   __shared__ float wgt[kMergeChunk];
-  __shared__ float sh_m, sh_den;
   const int h = blockIdx.x, t = threadIdx.x, D = a.D, G = a.G;
   const float* st = a.stats + (long)h * G * 2;
-  float m = -__builtin_inff();
-  for (int g = t; g < G; g += kMergeThreads) m = fmaxf(m, st[2 * g]);
-  part[t] = m;
-  __syncthreads();
-  if (t == 0) {
-    float M = part[0];
-    for (int i = 1; i < kMergeThreads; ++i) M = fmaxf(M, part[i]);
-    sh_m = M;
+  // up to 256 blocks (every head with at most 32768 rows): each thread reads its block's
+  // statistics once and keeps them for the weights
+  const bool one = G <= kMergeThreads;
+  float m_t = -__builtin_inff(), s_t = 0.0f;
+  if (one && t < G) {
+    m_t = st[2 * t];
+    s_t = st[2 * t + 1];
   }
-  __syncthreads();
-  const float M = sh_m;
-  float den = 0.0f;
-  for (int g = t; g < G; g += kMergeThreads) den = fmaf(st[2 * g + 1], expf(st[2 * g] - M), den);
-  __syncthreads();
-  part[t] = den;
-  __syncthreads();
-  if (t == 0) {
-    float s = 0.0f;
-    for (int i = 0; i < kMergeThreads; ++i) s += part[i];
-    sh_den = s;
-  }
+  float m = m_t;
+  if (!one)
+    for (int g = t; g < G; g += kMergeThreads) m = fmaxf(m, st[2 * g]);
+  const float M = merge_reduce<true>(m, part);
+  const float w_t = expf(m_t - M);
+  float den = one ? fmaf(s_t, w_t, 0.0f) : 0.0f;
+  if (!one)
+    for (int g = t; g < G; g += kMergeThreads) den = fmaf(st[2 * g + 1], expf(st[2 * g] - M), den);
+  const float den_all = merge_reduce<false>(den, part);
   float o0 = 0.0f, o1 = 0.0f;   // columns t and t + 256 (D <= 512)
   const float* op = a.opart + (long)h * G * D;
   for (int g0 = 0; g0 < G; g0 += kMergeChunk) {
     const int gn = min(kMergeChunk, G - g0);
     __syncthreads();   // the previous chunk's weights are read
-    for (int i = t; i < gn; i += kMergeThreads) wgt[i] = expf(st[2 * (g0 + i)] - M);
+    if (one) {
+      if (t < G) wgt[t] = w_t;
+    } else {
+      for (int i = t; i < gn; i += kMergeThreads) wgt[i] = expf(st[2 * (g0 + i)] - M);
+    }
     __syncthreads();
     if (t < D) {
-#pragma unroll 8
+#pragma unroll 16
       for (int i = 0; i < gn; ++i) o0 = fmaf(op[(long)(g0 + i) * D + t], wgt[i], o0);
     }
     if (t + kMergeThreads < D) {
-#pragma unroll 8
+#pragma unroll 16
       for (int i = 0; i < gn; ++i) o1 = fmaf(op[(long)(g0 + i) * D + t + kMergeThreads], wgt[i], o1);
     }
   }
-  __syncthreads();
-  const float den_all = sh_den;
   for (int k = 0; k < 2; ++k) {
     const int d = t + k * kMergeThreads;
     if (d >= D) continue;
