@@ -1,5 +1,6 @@
-"""GPU: fused calls captured into a HIP graph (the way the bench times them) give, on every
-replay, the bits the same calls give when launched eagerly.  Replays are separated by eager
+"""GPU: calls of every compute entry point (fused linear, gate/up, MLP, attend, sample,
+quantized-KV decode, streaming read) captured into a HIP graph (the way the bench times
+them) give, on every replay, the bits the same calls give when launched eagerly.  Replays are separated by eager
 work and synchronizations, and each replay is checked (a captured library call that only
 the first replay gets right would fail here)."""
 import numpy as np
@@ -66,3 +67,48 @@ def test_graph_replay_stream_read():
     buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
     part = torch.zeros(1024, dtype=torch.int32, device="cuda")
     _replays_match([lambda: qlin_stream_read(buf, part)], [part])
+
+
+def test_graph_replay_mlp():
+    # the long-K down projection (K = I = 8192 > the streaming windows) with the residual
+    from decode_linear_amd import qlin_mlp
+    c = synth.random_mlp(7003, 4, 1024, 8192, 512, 4, res=True)
+    gq, uq, dq = (Packed(a, 4) for a in (c.gate, c.up, c.down))
+    x, res = dev_bits(c.x, synth.BF16), dev_bits(c.res, synth.BF16)
+    h = torch.empty((4, 8192), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((4, 512), dtype=torch.bfloat16, device="cuda")
+    _replays_match([lambda: qlin_mlp(x, gq.q, uq.q, dq.q, residual=res, h=h, out=y)], [h, y])
+
+
+def test_graph_replay_attend():
+    from decode_linear_amd import qlin_attend
+    c = synth.attend_workload()
+    qkv, kv = dev_bits(c.qkv, c.dtype), dev_bits(c.kv, c.dtype)
+    out = torch.empty((c.T, c.H * c.HD), dtype=torch.bfloat16, device="cuda")
+    kv_out = torch.empty((2, c.H, c.P + c.T, c.HD), dtype=torch.bfloat16, device="cuda")
+    _replays_match([lambda: qlin_attend(qkv, kv, c.H, c.HD, out=out, kv_out=kv_out)], [out, kv_out])
+
+
+def test_graph_replay_sample():
+    from decode_linear_amd import qlin_sample
+    c = synth.sample_workload()
+    lg = dev_bits(c.logits, c.logit_dtype)
+    g = torch.from_numpy(c.gumbel).cuda()
+    tb, pre = dev_bits(c.table, c.emb_dtype), dev_bits(c.prefix, c.emb_dtype)
+    out = torch.empty((c.prefix.shape[0] + 1, c.D), dtype=torch.bfloat16, device="cuda")
+    code = torch.empty(1, dtype=torch.int32, device="cuda")
+    _replays_match([lambda: qlin_sample(lg, g, 1, tb, pre, 1.0 / 0.9, 64, out=out, code=code)], [out, code])
+
+
+def test_graph_replay_kvq_decode():
+    from decode_linear_amd import qlin_kvq_decode
+    from decode_linear_amd.qlin import lib
+    c = synth.kvq_case(7004, 4, 2, 5000, 128, 64, 4)
+    q = dev_bits(c.q, c.q_dtype)
+
+    def cache(t):
+        return (torch.from_numpy(t[0].view(np.int32)).cuda(), dev_bits(t[1], c.sb_dtype), dev_bits(t[2], c.sb_dtype))
+    k, v = cache(c.k), cache(c.v)
+    ws = torch.empty(int(lib().qlin_kvq_decode_workspace(c.H, c.N, c.D)) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((c.H, c.D), dtype=torch.bfloat16, device="cuda")
+    _replays_match([lambda: qlin_kvq_decode(q, k, v, c.KV, c.GS, c.bits, out=out, workspace=ws)], [out])
