@@ -413,7 +413,7 @@ def measured_traffic():
 def main():
     a = _args()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU: the library has no multi-GPU path; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
         sys.exit(2)
     from decode_linear_amd import build
