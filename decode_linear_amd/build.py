@@ -7,6 +7,8 @@ decode_linear_amd/libqlin.so.  Flags:
                                   no packed FP32 instructions (v_pk_{add,mul,fma}_f32)
   -fhip-fp32-correctly-rounded-divide-sqrt
                                   IEEE division (the quantizer must be bit exact)
+  -mllvm -amdgpu-kernarg-preload-count=16
+                                  leading kernel arguments arrive in SGPRs at wave launch
 """
 from __future__ import annotations
 
@@ -23,11 +25,13 @@ LIB_PATH = os.path.join(PKG, "libqlin.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qlin_host.cpp", "qlin_pack.hip", "qlin_attend.hip", "qlin_stream.hip", "qlin_sample.hip", "qlin_kvq.hip", "qlin_fused_q4.hip", "qlin_fused_q8.hip",
-           "qlin_fused_f16.hip", "qlin_fused_bf16.hip"]
+           "qlin_fused_f16.hip", "qlin_fused_bf16.hip", "qlin_s8_q4_ln0.hip", "qlin_s8_q4_ln1.hip",
+           "qlin_s8_q8_ln0.hip", "qlin_s8_q8_ln1.hip"]
 
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

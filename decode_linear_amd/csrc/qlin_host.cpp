@@ -102,10 +102,76 @@ int cu_count() {
   return v;
 }
 
+// Which kernel family serves quantized calls: 0 the int8 streaming kernel where its shape
+// rules admit the call (else the general kernel), 1 always the general kernel.
+std::atomic<int> g_path{0};
+
+int pow2_ceil(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// The int8 streaming kernel (qlin_s8.h) for 4- and 8-bit codes.  Returns false when its
+// shape rules do not admit the call (the general kernel takes it then).
+bool try_s8(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up, const qlin_ln* ln,
+            int act, const void* res, const void* add, void* y, int y_dtype, hipStream_t stream, hipError_t* err) {
+  using namespace qlin;
+  if (g_path.load(std::memory_order_relaxed) == 1) return false;
+  if (w->bits != 4 && w->bits != 8) return false;
+  if (up && ln) return false;
+  const int G = (int)(w->K / 64);
+  for (const qlin_weight* q : {w, up}) {
+    if (q && (!aligned(q->scales, 16) || !aligned(q->biases, 16))) return false;
+  }
+  const int R = T + (ln ? 2 : 0);
+  const int mt = R <= 4 ? 1 : (R <= 8 ? 2 : (R <= 12 ? 3 : 9));
+  const int ntiles = (int)(up ? (w->N + 7) / 8 : (w->N + 15) / 16);
+  // The window of K per wave (a power of two, >= 2 groups): one wave per SIMD (4 per
+  // workgroup) when a workgroup takes several tiles, where the older of two waves sharing a
+  // SIMD would run ahead of the younger and the workgroup wait for it; up to 8 waves when
+  // each workgroup has one tile (latency-bound calls: more loads issue at once).
+  auto window = [&](int waves) { return pow2_ceil(G <= 2 * waves ? 2 : (G + waves - 1) / waves); };
+  auto usable = [&](int g) { return g <= 32 && G % (g < 8 ? g : 8) == 0 && s8::max_tiles(mt, g) > 0; };
+  int gw = window(ntiles > cu_count() ? 4 : 8);
+  if (!usable(gw)) gw = window(8);
+  if (!usable(gw)) return false;
+  const int dm = s8::max_tiles(mt, gw);
+  S8Launch a{};
+  a.x = x;
+  a.w0 = w->data; a.s0 = w->scales; a.b0 = w->biases;
+  if (up) { a.p1 = up->data; a.p2 = up->scales; a.p3 = up->biases; }
+  else if (ln) { a.p1 = ln->gamma; a.p2 = ln->beta; a.p3 = nullptr; }
+  a.K = (int)w->K; a.T = T; a.N = (int)w->N; a.x_bf16 = x_dtype == QLIN_BF16 ? 1 : 0;
+  a.gateup = up ? 1 : 0; a.ln = ln ? 1 : 0; a.bits = w->bits;
+  a.y = y; a.res = res; a.add = add; a.eps = ln ? ln->eps : 0.0f; a.y_dtype = y_dtype; a.act = act;
+  a.MT = mt; a.GWM = gw; a.waves = (G + gw - 1) / gw;
+  int tpw = (ntiles + cu_count() - 1) / cu_count();
+  if (tpw > dm) tpw = dm;
+  a.grid = (ntiles + tpw - 1) / tpw;
+  a.D = (ntiles + a.grid - 1) / a.grid;   // tiles of the fullest workgroup
+  // the shape rides in the top 16 bits of the pointer arguments (qlin_s8.h)
+  if (a.grid > 0xFFFF) return false;
+  for (const void* q : {a.x, a.w0, a.s0, a.b0, a.p1, a.p2, a.p3}) {
+    if ((reinterpret_cast<uintptr_t>(q) >> s8::kTagShift) != 0) return false;
+  }
+  if (w->bits == 4) *err = ln ? launch_s8_q4_ln1(a, stream) : launch_s8_q4_ln0(a, stream);
+  else *err = ln ? launch_s8_q8_ln1(a, stream) : launch_s8_q8_ln0(a, stream);
+  return true;
+}
+
 qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up,
                    const qlin_ln* ln, int act, const void* res, const void* add, void* y, int y_dtype,
                    hipStream_t stream) {
   using namespace qlin;
+  {
+    hipError_t e = hipSuccess;
+    if (try_s8(x, x_dtype, T, w, up, ln, act, res, add, y, y_dtype, stream, &e)) {
+      if (e != hipSuccess) return QLIN_ERR_HIP;
+      g_dispatch[up ? 1 : 0].fetch_add(1, std::memory_order_relaxed);
+      return QLIN_OK;
+    }
+  }
   LinParams p{};
   p.x = x; p.x_dtype = x_dtype; p.T = T; p.K = (int)w->K; p.N = (int)w->N;
   p.w[0] = w->data; p.sc[0] = static_cast<const uint16_t*>(w->scales); p.bi[0] = static_cast<const uint16_t*>(w->biases);
@@ -468,6 +534,11 @@ qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, in
   if (qlin::launch_kvq_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return QLIN_ERR_HIP;
   g_dispatch[7].fetch_add(1, std::memory_order_relaxed);
   return QLIN_OK;
+}
+
+int32_t qlin_set_path(int32_t path) {
+  if (path != 0 && path != 1) return -1;
+  return g_path.exchange(path, std::memory_order_relaxed);
 }
 
 int64_t qlin_dispatch_count(int32_t which) {

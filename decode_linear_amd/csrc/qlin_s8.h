@@ -1,0 +1,689 @@
+// The streaming fused linear on the int8 matrix cores of gfx950 (CDNA4, wave64), for
+// 8-bit and 4-bit affine codes.  Shared by the instantiation units qlin_s8_*.hip.
+//
+// What it computes ([p1] maya-mac src/maya_mac/mlx_kernels.py, `_linear_kernel`):
+//   y[t, n] = epi( LN?(x_t) . W_n ),   W[n, k] = q[n, k] * s[n, k/64] + b[n, k/64]
+// with LayerNorm folded into the weight stream by the identity of that kernel's docstring,
+//   LN(x) . w = rstd * (sum (x - x0) g w - (mean - x0) sum g w) + sum b w,
+// the statistics taken in one pass over x shifted by x0 = x[t, 0], and the per-group
+// dequantization factored out of the dot product ([p3] mlx-bun 0.0.10 -> 0.0.12,
+// fused-decode-kernel.ts, the "qdot pattern"):
+//   sum_k (s q_k + b) a_k = s * sum_k q_k a_k + b * sum_k a_k.
+//
+// How it maps onto CDNA4:
+//   * A workgroup of up to 8 waves takes up to D output tiles of 16 weight rows (8 gate +
+//     8 up rows for gate/up).  Wave w owns a window of GWM quantization groups of K for the
+//     whole launch; every lane of it issues the loads of ALL of the workgroup's tiles at
+//     kernel entry (16-byte loads: lane (c, j) reads 16 bytes of weight row j, c = lane/16),
+//     so the weight stream starts with the kernel and the staging below runs under it.
+//   * Exact products on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  Each operand row
+//     a (an activation row; with LayerNorm also gamma and beta) becomes, per wave window, a
+//     24-bit fixed-point integer X = trunc(a * 2^(16+e)), e the power of two that puts the
+//     window's max |a| in [64, 128).  X is split into three bytes: the signed top byte and
+//     the two low bytes, each taken as (byte - 128).  Codes enter as int8 values: 4-bit codes
+//     as they are (0..15), 8-bit codes as q - 128.  One more operand row of ones gives the
+//     group's code sum, which restores the byte offsets:
+//       sum_k X_k q_k = 65536 C_hi + 256 C_mid + C_lo + 32896 C_ones    (4-bit),
+//     with 128 * sum_k X_k added for 8-bit codes.  Every product and every sum inside the
+//     MFMA is an exact integer; fp32 rounding enters only per group, where the exact group
+//     dot product is scaled by its fp16 scale, and in the final sums.
+//   * A 16-row MFMA block holds four operand rows: C rows 4r .. 4r + 3 are the three bytes
+//     of operand row r and the ones row, so a lane holds all parts of one (row, column)
+//     and combines them in registers.
+//   * Merge: each wave writes its partial per tile (already in absolute units) to LDS; after
+//     the workgroup's single barrier the threads sum the waves' partials in wave order, apply
+//     the LayerNorm fold, the epilogue (GELU, residual, constant; or silu(g) * u) and store
+//     with one rounding.  No atomics touch data and no wave waits on another before the end,
+//     so results are bitwise reproducible and no wait can stall.
+#pragma once
+
+#include "qlin_internal.h"
+
+namespace qlin {
+namespace s8 {
+
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
+
+#define QLIN_S8_GLOBAL __attribute__((address_space(1)))
+template <typename T> using gp = const T QLIN_S8_GLOBAL*;
+
+// Zero-filled memory that masked lanes load from, so that every path issues the same loads
+// (the compiler's wait counts stay exact).  Every masked offset stays below 64 bytes.
+static __device__ __attribute__((aligned(256))) uint32_t g_zero[64];
+
+template <typename T> __device__ __forceinline__ gp<T> gaddr(const void* p, long byte_off) {
+  return reinterpret_cast<gp<T>>(reinterpret_cast<uintptr_t>(p) + (uintptr_t)byte_off);
+}
+template <typename T> __device__ __forceinline__ gp<T> zaddr(int byte_off) {
+  return reinterpret_cast<gp<T>>(reinterpret_cast<uintptr_t>(g_zero) + (uintptr_t)byte_off);
+}
+
+// Arguments needed after the weight loads are issued.  The ones before it in the kernel's
+// argument list fit the SGPRs that gfx950 preloads at wave launch (the shape words first),
+// so the first loads wait for no kernel-argument fetch.
+struct Tail {
+  void* y;
+  const void* res;   // (T, N) in x's dtype, or null
+  const void* add;   // (N,) in x's dtype, or null
+  float eps;
+  int y_dtype;       // 0 fp32, 1 fp16, 2 bf16
+  int act;           // 0 none, 1 GELU
+};
+
+// Shape words ride in the top 16 bits of the pointer arguments (device addresses use the
+// low 48 bits), so that all of them arrive in the SGPRs preloaded at wave launch:
+//   x: K / 64 | (x is bf16) << 15;  w0: T - 1 | gateup << 5;  s0: N & 0xFFFF;
+//   b0: N >> 16;  p1: the grid size.
+constexpr uint64_t kAddrMask = (uint64_t(1) << kTagShift) - 1;
+__host__ __device__ inline uint64_t tag(const void* p, uint32_t v) {
+  return (uint64_t)(uintptr_t)p | ((uint64_t)(v & 0xFFFFu) << kTagShift);
+}
+__device__ __forceinline__ uint32_t tag_of(const void* p) { return (uint32_t)((uint64_t)(uintptr_t)p >> kTagShift); }
+template <typename T> __device__ __forceinline__ const T* untag(const void* p) {
+  return reinterpret_cast<const T*>((uint64_t)(uintptr_t)p & kAddrMask);
+}
+
+// Compile-time shape of one instantiation.
+//   MT  16-row MFMA blocks (4 operand rows each: RMAX = 4 MT operand rows)
+//   GWM quantization groups in a wave's window (power of two, 2 .. 32)
+//   R   ring slots: tiles whose loads are in flight while the wave computes (1 or 2)
+template <int BITS, bool LN, int MT, int GWM, int R>
+struct Cfg {
+  static constexpr int RMAX = 4 * MT;
+  // The operand fragments of the whole window stay in VGPRs when they are few enough;
+  // otherwise (a long window, one tile per workgroup) they are staged chunk by chunk,
+  // each chunk right before the groups that use it.
+  static constexpr bool RES = GWM * MT * 4 <= 72;
+  static constexpr int CG = GWM < 8 ? GWM : 8;        // groups staged at once
+  static constexpr int NCH = GWM / CG;                 // staging chunks
+  static constexpr int AG = RES ? GWM : CG;            // groups of fragments in VGPRs
+  static constexpr int W8 = 8 * GWM;                   // 8-element pieces per operand row window
+  static constexpr int NPX = MT * GWM / 2;             // pieces per lane (RMAX * W8 / 64)
+  static constexpr int UPR = GWM >= 8 ? GWM / 8 : 1;   // piece rounds (u) per operand row
+  static constexpr int LC = BITS == 8 ? GWM : GWM / 2; // 16-byte code loads per tile and lane
+  static constexpr int SBB = 2 * GWM;                  // scale (or bias) bytes per lane and tile
+  static constexpr int LS = SBB <= 16 ? 1 : SBB / 16;  // scale/bias loads per tile and lane
+  static constexpr int SBW = SBB < 16 ? SBB / 4 : 4;   // dwords per scale/bias load (1, 2 or 4)
+  static constexpr int SBD = SBB / 4;                  // scale (bias) dwords per lane
+  // LDS: per wave, then the partials of all tiles
+  static constexpr int IP = CG * 64 + 16;              // image row pitch (bytes)
+  static constexpr int IMG = (3 * RMAX + 1) * IP;      // operand image: 3 byte planes per operand row + a row of ones
+  static constexpr int OFF_MAX = 0;                    // rowmax[RMAX] (u32)
+  static constexpr int OFF_ST = OFF_MAX + RMAX * 4;    // LN: S1, S2 [RMAX][GWM][2]
+  static constexpr int OFF_IMG = (OFF_ST + (LN ? RMAX * GWM * 8 : 0) + 15) / 16 * 16;
+  static constexpr int WAVE_BYTES = OFF_IMG + IMG;
+  static constexpr int PMAX = max_tiles(MT, GWM);        // tiles of one workgroup, at most
+  static constexpr int PART_BYTES = PMAX * kWaves * MT * 256;
+  static constexpr int LDS_BYTES = kWaves * WAVE_BYTES + PART_BYTES;
+  static_assert(GWM >= 2 && (GWM & (GWM - 1)) == 0 && GWM <= 32, "windows of 2..32 groups");
+  static_assert(PMAX >= 1, "an instantiated shape");
+  static_assert(RES || (R == 1 && PMAX == 1), "streamed fragments serve one tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// 8 consecutive 16-bit elements of a 16-byte piece, widened to fp32.
+__device__ __forceinline__ void widen8(const u4_t r, bool bf, float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf ? bf16_lo(r[i]) : f16_lo(r[i]);
+    v[2 * i + 1] = bf ? bf16_hi(r[i]) : f16_hi(r[i]);
+  }
+}
+
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Reductions over aligned groups of 8 lanes (xor 1, xor 2, then the mirrored half-row):
+// every lane of a group ends with the group's value, and the order is fixed.
+__device__ __forceinline__ float sum8f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v;
+}
+__device__ __forceinline__ int sum8i(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t max8u(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+  return v;
+}
+
+// Max over aligned groups of N lanes (N a power of two, 8..64): DPP moves within 16-lane
+// rows (xor 1, xor 2, the mirrored half-row, the mirrored row), then the gfx950 row swaps
+// (v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two halves).
+template <int N> __device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  static_assert(N >= 8 && N <= 64, "groups of 8..64 lanes");
+  v = max8u(v);
+  if constexpr (N >= 16) v = max(v, (uint32_t)dpp_i<0x140>((int)v));
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  return v;
+}
+
+// Window exponent e of an operand row from its max |a| (bit pattern): max * 2^e in
+// [64, 128).  A zero row takes 0; the exponent is clamped so that 2^-(16+e) stays normal.
+__device__ __forceinline__ int row_exp(uint32_t amax_bits) {
+  const int be = (int)(amax_bits >> 23);
+  if (amax_bits == 0u) return 0;
+  const int e = 6 - (be - 127);
+  return e > 100 ? 100 : e;
+}
+
+// Bytes of four 24-bit integers X0..X3 (two's complement in int32): term 0 = the signed
+// top bytes, terms 1 and 2 = bytes 1 and 0 minus 128 (as int8: the byte xor 0x80).
+__device__ __forceinline__ void split4(int x0, int x1, int x2, int x3, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)x1, (uint32_t)x0, 0x05010400u);   // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)x3, (uint32_t)x2, 0x05010400u);
+  const uint32_t q01 = __builtin_amdgcn_perm((uint32_t)x1, (uint32_t)x0, 0x07030602u);   // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t q23 = __builtin_amdgcn_perm((uint32_t)x3, (uint32_t)x2, 0x07030602u);
+  lo = __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u;    // p01.b0 p01.b1 p23.b0 p23.b1
+  mid = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;   // p01.b2 p01.b3 p23.b2 p23.b3
+  hi = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
+}
+
+__device__ __forceinline__ void store_y(void* y, int dtype, long idx, float v) {
+  if (dtype == 0) reinterpret_cast<float*>(y)[idx] = v;
+  else if (dtype == 1) reinterpret_cast<_Float16*>(y)[idx] = (_Float16)v;
+  else reinterpret_cast<__bf16*>(y)[idx] = (__bf16)v;
+}
+__device__ __forceinline__ float elem(uint32_t h, bool bf) {
+  return bf ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <int BITS, bool LN, int MT, int GWM, int R>
+struct Kern {
+  using C = Cfg<BITS, LN, MT, GWM, R>;
+
+  // One tile's loads: the codes of this wave's window and the scales (even lane groups) or
+  // biases (odd lane groups) of its groups.
+  struct TileRegs {
+    u4_t code[C::LC];
+    uint32_t sb[C::LS * C::SBW];
+  };
+
+  // Issue the loads of tile `tile` (rows past N and tiles past the last read zeros).
+  __device__ __forceinline__ static void issue(TileRegs& r, int tile, int ntiles, const uint8_t* w0, const void* w1,
+                                               const uint16_t* s0, const void* s1, const uint16_t* b0, const void* b1,
+                                               int N, int gateup, int row_bytes, int G, int g_lo, int c, int j) {
+    int proj, n;
+    if (gateup) { proj = j >> 3; n = tile * 8 + (j & 7); }
+    else { proj = 0; n = tile * 16 + j; }
+    const bool valid = tile < ntiles && n < N;
+    const void* wb = proj ? w1 : (const void*)w0;
+    const long rowoff = (long)n * row_bytes;
+#pragma unroll
+    for (int q = 0; q < C::LC; ++q) {
+      // 8-bit: group g_lo + q, bytes 16c of it; 4-bit: step g_lo/2 + q (groups 2 step + c/2)
+      const int g = BITS == 8 ? g_lo + q : g_lo + 2 * q + (c >> 1);
+      const long off = BITS == 8 ? rowoff + 64L * (g_lo + q) + 16 * c : rowoff + 32L * (g_lo + 2 * q) + 16 * c;
+      const bool ok = valid && g < G;
+      r.code[q] = *(ok ? gaddr<u4_t>(wb, off) : zaddr<u4_t>(16 * c));
+    }
+    const void* sp = (c & 1) ? (proj ? b1 : (const void*)b0) : (proj ? s1 : (const void*)s0);
+    const long sbo = ((long)n * G + g_lo) * 2;
+#pragma unroll
+    for (int q = 0; q < C::LS; ++q) {
+      const bool ok = valid && g_lo + q * 8 < G;
+      const long off = sbo + 16L * q;
+      if constexpr (C::SBW == 4) {
+        const u4_t v = *(ok ? gaddr<u4_t>(sp, off) : zaddr<u4_t>(0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.sb[4 * q + i] = v[i];
+      } else if constexpr (C::SBW == 2) {
+        const u2_t v = *(ok ? gaddr<u2_t>(sp, off) : zaddr<u2_t>(0));
+        r.sb[0] = v[0];
+        r.sb[1] = v[1];
+      } else {
+        r.sb[0] = *(ok ? gaddr<uint32_t>(sp, off) : zaddr<uint32_t>(0));
+      }
+    }
+  }
+
+  // B operand of group gg of the window (16 int8 codes of column j, this lane's k-quarter).
+  // 4-bit: after the lane-half exchange (see compute), dwords 0-1 hold the even group and
+  // dwords 2-3 the odd group of a step; nibbles split into low (even k) and high (odd k).
+  __device__ __forceinline__ static i4_t operand_b(const u4_t d, int gg) {
+    if constexpr (BITS == 8) {
+      return (i4_t){(int)(d[0] ^ 0x80808080u), (int)(d[1] ^ 0x80808080u), (int)(d[2] ^ 0x80808080u),
+                    (int)(d[3] ^ 0x80808080u)};
+    } else {
+      const uint32_t a = (gg & 1) ? d[2] : d[0], b = (gg & 1) ? d[3] : d[1];
+      return (i4_t){(int)(a & 0x0F0F0F0Fu), (int)((a >> 4) & 0x0F0F0F0Fu), (int)(b & 0x0F0F0F0Fu),
+                    (int)((b >> 4) & 0x0F0F0F0Fu)};
+    }
+  }
+};
+
+// Inverse of the 4-bit k order: the lane group that feeds 16-code run (k >> 4) of a group.
+__device__ __forceinline__ constexpr int kq4(int run) { return run == 0 ? 0 : (run == 1 ? 2 : (run == 2 ? 1 : 3)); }
+
+template <int BITS, bool LN, int MT, int GWM, int R>
+__global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void* w0t, const void* s0t,
+                                                      const void* b0t, const void* p1t, const void* p2t,
+                                                      const void* p3t, const Tail tail) {
+  using C = Cfg<BITS, LN, MT, GWM, R>;
+  using Kx = Kern<BITS, LN, MT, GWM, R>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
+
+  const uint32_t tx = tag_of(xt), tw = tag_of(w0t);
+  const int G = (int)(tx & 0x7FFFu), K = G << 6;
+  const bool xbf = (tx >> 15) != 0;
+  const int T = (int)(tw & 31u) + 1;
+  const int gateup = (int)((tw >> 5) & 1u);
+  const int N = (int)(tag_of(s0t) | (tag_of(b0t) << 16));
+  const int grid = (int)tag_of(p1t);
+  const uint16_t* x = untag<uint16_t>(xt);
+  const uint8_t* w0 = untag<uint8_t>(w0t);
+  const uint16_t* s0 = untag<uint16_t>(s0t);
+  const uint16_t* b0 = untag<uint16_t>(b0t);
+  const void* p1 = untag<void>(p1t);
+  const void* p2 = untag<void>(p2t);
+  const void* p3 = untag<void>(p3t);
+  const int row_bytes = K * BITS / 8;
+  const int ntiles = gateup ? (N + 7) >> 3 : (N + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane >> 4, j = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int waves = (G + GWM - 1) / GWM;
+  const int g_lo = wv * GWM;
+  const int ntw = (ntiles - (int)blockIdx.x + grid - 1) / grid;   // tiles of this workgroup (1 .. PMAX)
+  const int RS = T + (LN ? 2 : 0);                                   // operand rows in use
+  const uint16_t* gam = LN ? static_cast<const uint16_t*>(p1) : nullptr;
+  const uint16_t* bet = LN ? static_cast<const uint16_t*>(p2) : nullptr;
+
+  unsigned char* wbase = lds + wv * C::WAVE_BYTES;
+  uint32_t* rowmax = reinterpret_cast<uint32_t*>(wbase + C::OFF_MAX);
+  float* sts = reinterpret_cast<float*>(wbase + C::OFF_ST);
+  unsigned char* img = wbase + C::OFF_IMG;
+  float* parts = reinterpret_cast<float*>(lds + kWaves * C::WAVE_BYTES);
+
+  // ---- 1. this wave's window of the operand rows (x; with LN also gamma and beta) -------
+  // Piece p = lane + 64 u: operand row rho = p / W8, piece kp = p % W8 of the window
+  // (elements 64 g_lo + 8 kp .. + 7).  Pieces past the rows in use or past K read zeros.
+  u4_t raw[C::NPX];
+  u4_t graw[LN ? C::NPX : 1];
+#pragma unroll
+  for (int u = 0; u < C::NPX; ++u) {
+    const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
+    const int g = g_lo + (kp >> 3);
+    const bool real = rho < RS && g < G;
+    const long k = 64L * g_lo + 8 * kp;
+    const void* src = x;
+    long off = ((long)rho * K + k) * 2;
+    if constexpr (LN) {
+      if (rho >= T) { src = rho == T ? (const void*)gam : (const void*)bet; off = k * 2; }
+    }
+    raw[u] = *(real ? gaddr<u4_t>(src, off) : zaddr<u4_t>(0));
+    if constexpr (LN) graw[u] = *(real ? gaddr<u4_t>(gam, k * 2) : zaddr<u4_t>(0));
+  }
+  uint32_t x0v = 0u;   // LN: x[lane, 0] for lanes < T (the shift of the row's statistics)
+  if constexpr (LN) x0v = *(lane < T ? gaddr<uint16_t>(x, (long)lane * K * 2) : zaddr<uint16_t>(0));
+
+  // ---- 2. every tile of the workgroup, at once -------------------------------------
+  // A ring of R tile slots.  Step q of the workgroup's sequence carries its tile q - z; the
+  // z = (R - ntw mod R) mod R leading steps carry zeros (they are computed, while the real
+  // tiles are in flight, and discarded), so that every step is computed: no branch separates
+  // the steps (the compiler would join the paths and wait for every load in flight).
+  typename Kx::TileRegs tr[R];
+  const int nq = (ntw + R - 1) / R * R;   // steps
+  const int z = nq - ntw;
+  auto tile_of = [&](int q) __attribute__((always_inline)) {
+    return (q < z || q >= nq) ? ntiles : (int)blockIdx.x + (q - z) * grid;
+  };
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    Kx::issue(tr[r], tile_of(r), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+
+  // epilogue inputs of this thread's first output (loaded now, used at the end)
+  const int nthreads = waves * 64;
+  const int per_tile = gateup ? 8 * T : 16 * T;
+  uint32_t res0 = 0u, add0 = 0u;
+  {
+    const int o = tid, i = o / per_tile, rem = o - i * per_tile;
+    const int t = gateup ? rem >> 3 : rem >> 4, jj = gateup ? rem & 7 : rem & 15;
+    const int tile = (int)blockIdx.x + i * grid;
+    const int n = gateup ? tile * 8 + jj : tile * 16 + jj;
+    const bool ok = i < ntw && n < N && !gateup;
+    res0 = *((ok && tail.res) ? gaddr<uint16_t>(tail.res, ((long)t * N + n) * 2) : zaddr<uint16_t>(0));
+    add0 = *((ok && tail.add) ? gaddr<uint16_t>(tail.add, (long)n * 2) : zaddr<uint16_t>(0));
+  }
+
+  // ---- 3. staging, pass 1: row maxima (and the LN sums) -----------------------------
+  // A row's pieces fill an aligned group of min(W8, 64) lanes of one round u (or whole
+  // rounds when W8 > 64): a max over the group by lane exchanges, then over the row's rounds.
+  // One lane per row writes it.
+  auto values = [&](int u, float a[8], float dsh[8]) __attribute__((always_inline)) {
+    const int p = lane + 64 * u, rho = p / C::W8;
+    widen8(raw[u], xbf, a);
+    if constexpr (LN) {
+      float gm[8];
+      widen8(graw[u], xbf, gm);
+      const uint32_t x0b = (uint32_t)__shfl((int)x0v, rho < 32 ? rho : 0);
+      const float x0 = elem(x0b & 0xFFFFu, xbf);
+      const bool xr = rho < T;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dsh[e] = a[e] - x0;
+        a[e] = xr ? dsh[e] * gm[e] : a[e];
+      }
+    }
+  };
+  uint32_t rmx[C::NPX];   // max |a| (bit pattern) of the row of each of this lane's pieces
+#pragma unroll
+  for (int u = 0; u < C::NPX; ++u) {
+    const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
+    uint32_t m;
+    if constexpr (LN) {
+      float a[8], dsh[8];
+      values(u, a, dsh);
+      m = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, a[e]) & 0x7FFFFFFFu);
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { s1 += dsh[e]; s2 += dsh[e] * dsh[e]; }
+      s1 = sum8f(s1);
+      s2 = sum8f(s2);
+      const int g = g_lo + (kp >> 3);
+      if ((lane & 7) == 0 && rho < T) {
+        const bool real = g < G;
+        sts[(rho * GWM + (kp >> 3)) * 2] = real ? s1 : 0.0f;
+        sts[(rho * GWM + (kp >> 3)) * 2 + 1] = real ? s2 : 0.0f;
+      }
+    } else {
+      // magnitudes of the 16-bit values, two per dword (their bit patterns order like the
+      // values), widened once at the end
+      us2_t hm = __builtin_bit_cast(us2_t, raw[u][0] & 0x7FFF7FFFu);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) hm = __builtin_elementwise_max(hm, __builtin_bit_cast(us2_t, raw[u][i] & 0x7FFF7FFFu));
+      const uint32_t h = max((uint32_t)hm[0], (uint32_t)hm[1]);
+      m = xbf ? h << 16 : __builtin_bit_cast(uint32_t, f16_lo(h));
+    }
+    rmx[u] = group_max<(C::W8 < 64 ? C::W8 : 64)>(m);
+  }
+  if constexpr (C::W8 > 64) {   // a row spans UPR rounds: combine them
+#pragma unroll
+    for (int u0 = 0; u0 < C::NPX; u0 += C::UPR) {
+      uint32_t m = rmx[u0];
+#pragma unroll
+      for (int k = 1; k < C::UPR; ++k) m = max(m, rmx[u0 + k]);
+#pragma unroll
+      for (int k = 0; k < C::UPR; ++k) rmx[u0 + k] = m;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C::NPX; ++u) {   // one lane per row publishes it (for the lanes' units)
+    const int p = lane + 64 * u, rho = p / C::W8;
+    if ((p % C::W8) == 0) rowmax[rho] = rmx[u];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+  // this lane's operand rows (one per block) and their unit 2^-(16 + e)
+  float unscale[MT];
+  bool poison[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t mb = rowmax[4 * mt + c];
+    unscale[mt] = __builtin_bit_cast(float, (uint32_t)(127 - 16 - row_exp(mb)) << 23);
+    poison[mt] = (mb >> 23) >= 255u;   // a non-finite operand value: the row's outputs become NaN
+  }
+
+  // ---- 4. staging, pass 2 (per chunk): X, its group sums and the byte-plane image ----
+  // Image row 3 rho + v (v = 0 top bytes, 1 middle, 2 low) holds, per group of the chunk,
+  // the 64 bytes in the order lane group kq reads them: 8-bit k = 16 kq + b; 4-bit
+  // k = {0, 32, 16, 48}[kq] + 8 (b >> 3) + 2 (b & 3) + ((b >> 2) & 1).
+  // the ones row (operand rows 4r + 3 of every block read it)
+  if (lane < C::CG * 8) *reinterpret_cast<u2_t*>(img + 3 * C::RMAX * C::IP + 8 * lane) = (u2_t){0x01010101u, 0x01010101u};
+  auto stage_chunk = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < C::NPX; ++u) {
+      if (C::NCH > 1 && (u % C::UPR) != ch) continue;   // compile-time per (u, ch) when unrolled
+      const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
+      const int gg = kp >> 3, pp = kp & 7;
+      float a[8], dsh[8];
+      values(u, a, dsh);
+      const int ex = 16 + row_exp(rmx[u]);
+      int X[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) X[e] = (int)__builtin_amdgcn_ldexpf(a[e], ex);
+      uint32_t h0, m0, l0, h1, m1, l1;
+      if constexpr (BITS == 8) {
+        split4(X[0], X[1], X[2], X[3], h0, m0, l0);
+        split4(X[4], X[5], X[6], X[7], h1, m1, l1);
+      } else {
+        split4(X[0], X[2], X[4], X[6], h0, m0, l0);
+        split4(X[1], X[3], X[5], X[7], h1, m1, l1);
+      }
+      const int kq = BITS == 8 ? (pp >> 1) : kq4(pp >> 1);
+      const int col = (gg % C::CG) * 64 + kq * 16 + 8 * (pp & 1);
+      if (rho < C::RMAX) {
+        *reinterpret_cast<u2_t*>(img + (3 * rho + 0) * C::IP + col) = (u2_t){h0, h1};
+        *reinterpret_cast<u2_t*>(img + (3 * rho + 1) * C::IP + col) = (u2_t){m0, m1};
+        *reinterpret_cast<u2_t*>(img + (3 * rho + 2) * C::IP + col) = (u2_t){l0, l1};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+  };
+  // fragments of groups [ch CG, (ch + 1) CG) into slots [base, base + CG)
+  i4_t af[C::AG][MT];
+  float gxf[C::AG][MT];
+  const int arow = lane & 15, akq = lane >> 4;   // A operand: row arow, k-quarter akq
+  auto load_frags = [&](int ch, int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < C::CG; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int rho = 4 * mt + (arow >> 2), v = arow & 3;
+        af[base + q][mt] = *reinterpret_cast<const i4_t*>(img + (v < 3 ? 3 * rho + v : 3 * C::RMAX) * C::IP + q * 64 +
+                                                            akq * 16);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    // Group sums of X: the fragments against a B of ones give, in this lane's C rows, the
+    // byte sums of its operand row (and 64 for the ones row); X = 65536 hi + 256 mid + lo +
+    // 32896 per element.
+    const i4_t ones = (i4_t){0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+    for (int q = 0; q < C::CG; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i4_t cs = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[base + q][mt], ones, (i4_t){0, 0, 0, 0}, 0, 0, 0);
+        gxf[base + q][mt] = fmaf((float)cs[0], 65536.0f, fmaf((float)cs[1], 256.0f, (float)cs[2] + 2105344.0f));
+      }
+  };
+
+  // ---- 5. the tiles --------------------------------------------------------------
+  // acc (per block) in units of 2^-(16 + e) of this lane's operand row.
+  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot, float acc[MT])
+      __attribute__((always_inline)) {
+    const i4_t bop = Kx::operand_b(d, gg);
+    // scale and bias of group gg for column j: dword gg/2 of the lane's scales (biases), half gg&1
+    const uint32_t sw = r.sb[gg >> 1];
+    const auto sbp = __builtin_amdgcn_permlane16_swap(sw, sw, false, false);
+    const uint32_t swd = (uint32_t)sbp[0], bwd = (uint32_t)sbp[1];
+    const float s = (gg & 1) ? f16_hi(swd) : f16_lo(swd);
+    const float b = (gg & 1) ? f16_hi(bwd) : f16_lo(bwd);
+    const float bb = BITS == 8 ? fmaf(128.0f, s, b) : b;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const i4_t cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[slot][mt], bop, (i4_t){0, 0, 0, 0}, 0, 0, 0);
+      const float cf = fmaf((float)cc[0], 65536.0f, fmaf((float)cc[1], 256.0f, fmaf((float)cc[3], 32896.0f, (float)cc[2])));
+      acc[mt] = fmaf(s, cf, acc[mt]);
+      acc[mt] = fmaf(bb, gxf[slot][mt], acc[mt]);
+    }
+  };
+  // the code dword set of group gg (4-bit: exchange lane halves once per step)
+  auto codes_of = [&](const typename Kx::TileRegs& r, int gg) __attribute__((always_inline)) {
+    if constexpr (BITS == 8) {
+      return r.code[gg];
+    } else {
+      const u4_t d = r.code[gg >> 1];
+      const auto e02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+      const auto e13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+      return (u4_t){(uint32_t)e02[0], (uint32_t)e13[0], (uint32_t)e02[1], (uint32_t)e13[1]};
+    }
+  };
+  auto put_partial = [&](int i, const float acc[MT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float v = poison[mt] ? __builtin_nanf("") : acc[mt] * unscale[mt];
+      parts[((i * kWaves + wv) * MT + mt) * 64 + lane] = v;
+    }
+  };
+
+  if constexpr (C::RES) {
+#pragma unroll
+    for (int ch = 0; ch < C::NCH; ++ch) {
+      stage_chunk(ch);
+      load_frags(ch, ch * C::CG);
+    }
+    for (int q0 = 0; q0 < nq; q0 += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < GWM; ++gg) {
+          if (BITS == 4 && (gg & 1)) continue;
+          const u4_t dd = codes_of(tr[r], gg);
+          group_step(tr[r], dd, gg, gg, acc);
+          if constexpr (BITS == 4) group_step(tr[r], dd, gg + 1, gg + 1, acc);
+        }
+        const int q = q0 + r;
+        if (q >= z) put_partial(q - z, acc);
+        Kx::issue(tr[r], tile_of(q + R), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+      }
+    }
+  } else {
+    // one tile: stage a chunk, then contract its groups
+    float acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < C::NCH; ++ch) {
+      stage_chunk(ch);
+      load_frags(ch, 0);
+#pragma unroll
+      for (int q = 0; q < C::CG; ++q) {
+        const int gg = ch * C::CG + q;
+        if (BITS == 4 && (gg & 1)) continue;
+        const u4_t dd = codes_of(tr[0], gg);
+        group_step(tr[0], dd, gg, q, acc);
+        if constexpr (BITS == 4) group_step(tr[0], dd, gg + 1, q + 1, acc);
+      }
+    }
+    put_partial(0, acc);   // one tile: ntw == 1
+  }
+
+  // ---- 6. merge, LayerNorm fold, epilogue, store -------------------------------------
+  __syncthreads();
+  const float inv_k = 1.0f / (float)K;
+  for (int o = tid; o < ntw * per_tile; o += nthreads) {
+    const int i = o / per_tile, rem = o - i * per_tile;
+    const int t = gateup ? rem >> 3 : rem >> 4, jj = gateup ? rem & 7 : rem & 15;
+    const int tile = (int)blockIdx.x + i * grid;
+    const int n = gateup ? tile * 8 + jj : tile * 16 + jj;
+    if (n >= N) continue;
+    auto merged = [&](int rho, int col) __attribute__((always_inline)) {
+      float v = 0.0f;
+      for (int w = 0; w < waves; ++w) v += parts[((i * kWaves + w) * MT + (rho >> 2)) * 64 + (rho & 3) * 16 + col];
+      return v;
+    };
+    float v = merged(t, jj);
+    float u = gateup ? merged(t, jj + 8) : 0.0f;
+    if constexpr (LN) {
+      float s1 = 0.0f, s2 = 0.0f;
+      for (int w = 0; w < waves; ++w) {
+        const float* st = reinterpret_cast<const float*>(lds + w * C::WAVE_BYTES + C::OFF_ST);
+        for (int q = 0; q < GWM; ++q) { s1 += st[(t * GWM + q) * 2]; s2 += st[(t * GWM + q) * 2 + 1]; }
+      }
+      const float m = s1 * inv_k;
+      const float var = fmaxf(s2 * inv_k - m * m, 0.0f);
+      const float rstd = 1.0f / sqrtf(var + tail.eps);
+      const float Gn = merged(T, jj), Bn = merged(T + 1, jj);
+      v = rstd * (v - m * Gn) + Bn;
+      if (gateup) u = rstd * (u - m * merged(T, jj + 8)) + merged(T + 1, jj + 8);
+    }
+    if (gateup) {
+      v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
+    } else {
+      if (tail.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
+      if (tail.res) v += elem(o == tid ? res0 : reinterpret_cast<const uint16_t*>(tail.res)[(long)t * N + n], xbf);
+      if (tail.add) v += elem(o == tid ? add0 : reinterpret_cast<const uint16_t*>(tail.add)[n], xbf);
+    }
+    store_y(tail.y, tail.y_dtype, (long)t * N + n, v);
+  }
+}
+
+}  // namespace s8
+}  // namespace qlin
+
+namespace qlin {
+namespace s8 {
+
+// Launch of one instantiation (the caller has checked the shape against it).
+template <int BITS, bool LN, int MT, int GWM, int R>
+hipError_t launch_one(const S8Launch& a, hipStream_t s) {
+  const Tail tail{a.y, a.res, a.add, a.eps, a.y_dtype, a.act};
+  auto tp = [](const void* p, uint32_t v) { return reinterpret_cast<const void*>(tag(p, v)); };
+  hipLaunchKernelGGL((s8_kernel<BITS, LN, MT, GWM, R>), dim3(a.grid), dim3(a.waves * 64), 0, s,
+                     tp(a.x, (uint32_t)(a.K / 64) | ((uint32_t)a.x_bf16 << 15)),
+                     tp(a.w0, (uint32_t)(a.T - 1) | ((uint32_t)a.gateup << 5)), tp(a.s0, (uint32_t)a.N & 0xFFFFu),
+                     tp(a.b0, (uint32_t)a.N >> 16), tp(a.p1, (uint32_t)a.grid), a.p2, a.p3, tail);
+  return hipGetLastError();
+}
+
+// One tile per workgroup: no ring (a second slot would only carry zeros); more: two slots.
+template <int BITS, bool LN, int MT, int GWM>
+hipError_t launch_d(const S8Launch& a, hipStream_t s) {
+  if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1>(a, s);
+  if constexpr (max_tiles(MT, GWM) >= 2) return launch_one<BITS, LN, MT, GWM, 2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, bool LN>
+hipError_t launch_bits_ln(const S8Launch& a, hipStream_t s) {
+  switch (a.MT * 100 + a.GWM) {
+    case 102: return launch_d<BITS, LN, 1, 2>(a, s);
+    case 104: return launch_d<BITS, LN, 1, 4>(a, s);
+    case 108: return launch_d<BITS, LN, 1, 8>(a, s);
+    case 116: return launch_d<BITS, LN, 1, 16>(a, s);
+    case 132: return launch_d<BITS, LN, 1, 32>(a, s);
+    case 202: return launch_d<BITS, LN, 2, 2>(a, s);
+    case 204: return launch_d<BITS, LN, 2, 4>(a, s);
+    case 208: return launch_d<BITS, LN, 2, 8>(a, s);
+    case 302: return launch_d<BITS, LN, 3, 2>(a, s);
+    case 304: return launch_d<BITS, LN, 3, 4>(a, s);
+    case 902: return launch_d<BITS, LN, 9, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace s8
+}  // namespace qlin

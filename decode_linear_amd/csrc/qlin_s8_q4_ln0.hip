@@ -1,0 +1,7 @@
+// Instantiations of the int8 streaming kernel for 4-bit codes, LayerNorm off
+// (one unit per format and prologue, so that they compile in parallel).
+#include "qlin_s8.h"
+
+namespace qlin {
+hipError_t launch_s8_q4_ln0(const S8Launch& a, hipStream_t s) { return s8::launch_bits_ln<4, false>(a, s); }
+}  // namespace qlin

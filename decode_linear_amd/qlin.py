@@ -4,7 +4,7 @@ Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
 qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
-qlin_dispatch_count,
+qlin_dispatch_count, qlin_set_path,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
 
@@ -84,6 +84,8 @@ def lib():
     L.qlin_kvq_decode_workspace.restype = i64
     L.qlin_kvq_decode.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp,
                                   i32, vp]
+    L.qlin_set_path.argtypes = [i32]
+    L.qlin_set_path.restype = i32
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
@@ -102,6 +104,15 @@ def qlin_status_string(status: int) -> str:
 
 def qlin_dispatch_count(which: int) -> int:
     return int(lib().qlin_dispatch_count(int(which)))
+
+
+def qlin_set_path(path: int) -> int:
+    """0: automatic kernel choice (the default); 1: always the general kernel.  Returns the
+    previous setting."""
+    prev = int(lib().qlin_set_path(int(path)))
+    if prev < 0:
+        raise ValueError(f"qlin_set_path: unknown path {path}")
+    return prev
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -291,6 +291,15 @@ qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, 
  * one linear). */
 int64_t qlin_dispatch_count(int32_t which);
 
+/* Selects the kernel family for 4- and 8-bit qlin_linear / qlin_gateup_swiglu / qlin_mlp
+ * calls made after it, process-wide: 0 (the default) lets the library pick the int8 streaming
+ * kernel wherever its shape rules admit the call and the general kernel elsewhere; 1 sends
+ * every call to the general kernel.  Both compute the same operation to the same tolerance;
+ * this exists so that tests and measurements can exercise each one.  Returns the previous
+ * setting, or -1 (and changes nothing) for any other value.  Not synchronized with calls
+ * in flight on other host threads. */
+int32_t qlin_set_path(int32_t path);
+
 /* Static description of a status code. */
 const char* qlin_status_string(qlin_status s);
 
