@@ -128,12 +128,12 @@ bool try_s8(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const q
   const int mt = R <= 4 ? 1 : (R <= 8 ? 2 : (R <= 12 ? 3 : 9));
   const int ntiles = (int)(up ? (w->N + 7) / 8 : (w->N + 15) / 16);
   // The window of K per wave (a power of two, >= 2 groups): one wave per SIMD (4 per
-  // workgroup) when a workgroup takes several tiles, where the older of two waves sharing a
-  // SIMD would run ahead of the younger and the workgroup wait for it; up to 8 waves when
-  // each workgroup has one tile (latency-bound calls: more loads issue at once).
+  // workgroup) when a workgroup takes four or more tiles, where the older of two waves
+  // sharing a SIMD would run ahead of the younger and the workgroup wait for it; up to 8
+  // waves otherwise (more loads issue at once, and staging is shorter per wave).
   auto window = [&](int waves) { return pow2_ceil(G <= 2 * waves ? 2 : (G + waves - 1) / waves); };
   auto usable = [&](int g) { return g <= 32 && G % (g < 8 ? g : 8) == 0 && s8::max_tiles(mt, g) > 0; };
-  int gw = window(ntiles > cu_count() ? 4 : 8);
+  int gw = window(ntiles > 3 * cu_count() ? 4 : 8);
   if (!usable(gw)) gw = window(8);
   if (!usable(gw)) return false;
   const int dm = s8::max_tiles(mt, gw);

@@ -100,6 +100,10 @@ struct Cfg {
   static constexpr int CG = GWM < 8 ? GWM : 8;        // groups staged at once
   static constexpr int NCH = GWM / CG;                 // staging chunks
   static constexpr int AG = RES ? GWM : CG;            // groups of fragments in VGPRs
+  // Streamed fragments: chunks whose loads are in flight ahead of the one being staged.  Two
+  // measured best on the MLP's down projection (K = 14336): 17.1 us, against 18.7 with three;
+  // windows of 64 groups on four waves were slower still (19.1 us with two, 21.8 with four).
+  static constexpr int CA = 2;
   static constexpr int W8 = 8 * GWM;                   // 8-element pieces per operand row window
   static constexpr int NPX = MT * GWM / 2;             // pieces per lane (RMAX * W8 / 64)
   static constexpr int UPR = GWM >= 8 ? GWM / 8 : 1;   // piece rounds (u) per operand row
@@ -224,41 +228,42 @@ struct Kern {
     uint32_t sb[C::LS * C::SBW];
   };
 
-  // Issue the loads of tile `tile` (rows past N and tiles past the last read zeros).
-  __device__ __forceinline__ static void issue(TileRegs& r, int tile, int ntiles, const uint8_t* w0, const void* w1,
-                                               const uint16_t* s0, const void* s1, const uint16_t* b0, const void* b1,
-                                               int N, int gateup, int row_bytes, int G, int g_lo, int c, int j) {
+  // Issue the loads of chunk ch (groups [ch CG, (ch + 1) CG) of the window) of tile `tile`:
+  // the chunk's scales (even lane groups) or biases (odd lane groups), then its codes.  Rows
+  // past N and tiles past the last read zeros.
+  __device__ __forceinline__ static void issue_chunk(TileRegs& r, int ch, int tile, int ntiles, const uint8_t* w0,
+                                                     const void* w1, const uint16_t* s0, const void* s1,
+                                                     const uint16_t* b0, const void* b1, int N, int gateup,
+                                                     int row_bytes, int G, int g_lo, int c, int j) {
     int proj, n;
     if (gateup) { proj = j >> 3; n = tile * 8 + (j & 7); }
     else { proj = 0; n = tile * 16 + j; }
     const bool valid = tile < ntiles && n < N;
+    const void* sp = (c & 1) ? (proj ? b1 : (const void*)b0) : (proj ? s1 : (const void*)s0);
+    const long sbo = ((long)n * G + g_lo) * 2;
+    if constexpr (C::SBW == 4) {   // one 16-byte load per chunk of 8 groups
+      const bool ok = valid && g_lo + ch * 8 < G;
+      const u4_t v = *(ok ? gaddr<u4_t>(sp, sbo + 16L * ch) : zaddr<u4_t>(0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.sb[4 * ch + i] = v[i];
+    } else if constexpr (C::SBW == 2) {
+      const u2_t v = *(valid ? gaddr<u2_t>(sp, sbo) : zaddr<u2_t>(0));
+      r.sb[0] = v[0];
+      r.sb[1] = v[1];
+    } else {
+      r.sb[0] = *(valid ? gaddr<uint32_t>(sp, sbo) : zaddr<uint32_t>(0));
+    }
     const void* wb = proj ? w1 : (const void*)w0;
     const long rowoff = (long)n * row_bytes;
+    constexpr int LCC = C::LC / C::NCH;   // code loads per chunk
 #pragma unroll
-    for (int q = 0; q < C::LC; ++q) {
+    for (int qq = 0; qq < LCC; ++qq) {
+      const int q = ch * LCC + qq;
       // 8-bit: group g_lo + q, bytes 16c of it; 4-bit: step g_lo/2 + q (groups 2 step + c/2)
       const int g = BITS == 8 ? g_lo + q : g_lo + 2 * q + (c >> 1);
       const long off = BITS == 8 ? rowoff + 64L * (g_lo + q) + 16 * c : rowoff + 32L * (g_lo + 2 * q) + 16 * c;
       const bool ok = valid && g < G;
       r.code[q] = *(ok ? gaddr<u4_t>(wb, off) : zaddr<u4_t>(16 * c));
-    }
-    const void* sp = (c & 1) ? (proj ? b1 : (const void*)b0) : (proj ? s1 : (const void*)s0);
-    const long sbo = ((long)n * G + g_lo) * 2;
-#pragma unroll
-    for (int q = 0; q < C::LS; ++q) {
-      const bool ok = valid && g_lo + q * 8 < G;
-      const long off = sbo + 16L * q;
-      if constexpr (C::SBW == 4) {
-        const u4_t v = *(ok ? gaddr<u4_t>(sp, off) : zaddr<u4_t>(0));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.sb[4 * q + i] = v[i];
-      } else if constexpr (C::SBW == 2) {
-        const u2_t v = *(ok ? gaddr<u2_t>(sp, off) : zaddr<u2_t>(0));
-        r.sb[0] = v[0];
-        r.sb[1] = v[1];
-      } else {
-        r.sb[0] = *(ok ? gaddr<uint32_t>(sp, off) : zaddr<uint32_t>(0));
-      }
     }
   }
 
@@ -319,30 +324,33 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
   unsigned char* img = wbase + C::OFF_IMG;
   float* parts = reinterpret_cast<float*>(lds + kWaves * C::WAVE_BYTES);
 
-  // ---- 1. this wave's window of the operand rows (x; with LN also gamma and beta) -------
-  // Piece p = lane + 64 u: operand row rho = p / W8, piece kp = p % W8 of the window
-  // (elements 64 g_lo + 8 kp .. + 7).  Pieces past the rows in use or past K read zeros.
+  // ---- 1. loads -------------------------------------------------------------------
+  // Operand pieces: piece p = lane + 64 u is operand row rho = p / W8, piece kp = p % W8 of
+  // the window (elements 64 g_lo + 8 kp .. + 7), in staging chunk (u mod UPR) when the window
+  // has several chunks.  Pieces past the rows in use or past K read zeros.
   u4_t raw[C::NPX];
   u4_t graw[LN ? C::NPX : 1];
+  auto load_pieces = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < C::NPX; ++u) {
-    const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
-    const int g = g_lo + (kp >> 3);
-    const bool real = rho < RS && g < G;
-    const long k = 64L * g_lo + 8 * kp;
-    const void* src = x;
-    long off = ((long)rho * K + k) * 2;
-    if constexpr (LN) {
-      if (rho >= T) { src = rho == T ? (const void*)gam : (const void*)bet; off = k * 2; }
+    for (int u = 0; u < C::NPX; ++u) {
+      if (C::NCH > 1 && (u % C::UPR) != ch) continue;
+      const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
+      const int g = g_lo + (kp >> 3);
+      const bool real = rho < RS && g < G;
+      const long k = 64L * g_lo + 8 * kp;
+      const void* src = x;
+      long off = ((long)rho * K + k) * 2;
+      if constexpr (LN) {
+        if (rho >= T) { src = rho == T ? (const void*)gam : (const void*)bet; off = k * 2; }
+      }
+      raw[u] = *(real ? gaddr<u4_t>(src, off) : zaddr<u4_t>(0));
+      if constexpr (LN) graw[u] = *(real ? gaddr<u4_t>(gam, k * 2) : zaddr<u4_t>(0));
     }
-    raw[u] = *(real ? gaddr<u4_t>(src, off) : zaddr<u4_t>(0));
-    if constexpr (LN) graw[u] = *(real ? gaddr<u4_t>(gam, k * 2) : zaddr<u4_t>(0));
-  }
+  };
   uint32_t x0v = 0u;   // LN: x[lane, 0] for lanes < T (the shift of the row's statistics)
   if constexpr (LN) x0v = *(lane < T ? gaddr<uint16_t>(x, (long)lane * K * 2) : zaddr<uint16_t>(0));
 
-  // ---- 2. every tile of the workgroup, at once -------------------------------------
-  // A ring of R tile slots.  Step q of the workgroup's sequence carries its tile q - z; the
+  // Tiles: a ring of R slots.  Step q of the workgroup's sequence carries its tile q - z; the
   // z = (R - ntw mod R) mod R leading steps carry zeros (they are computed, while the real
   // tiles are in flight, and discarded), so that every step is computed: no branch separates
   // the steps (the compiler would join the paths and wait for every load in flight).
@@ -352,9 +360,28 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
   auto tile_of = [&](int q) __attribute__((always_inline)) {
     return (q < z || q >= nq) ? ntiles : (int)blockIdx.x + (q - z) * grid;
   };
+  auto issue_tile = [&](typename Kx::TileRegs& r, int tile) __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    Kx::issue(tr[r], tile_of(r), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+    for (int ch = 0; ch < C::NCH; ++ch)
+      Kx::issue_chunk(r, ch, tile, ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+  };
+  if constexpr (C::RES) {
+    // every operand piece, then the ring's first tiles (staging waits for its pieces only:
+    // loads complete in order)
+#pragma unroll
+    for (int ch = 0; ch < C::NCH; ++ch) load_pieces(ch);
+#pragma unroll
+    for (int r = 0; r < R; ++r) issue_tile(tr[r], tile_of(r));
+  } else {
+    // one tile, chunk by chunk: each chunk's operand pieces, then its scales, biases and codes;
+    // CA chunks ahead (the rest are issued as chunks complete: a wave whose loads fill the
+    // memory queue stalls at the issue and could not stage what has arrived)
+#pragma unroll
+    for (int ch = 0; ch < (C::NCH < C::CA ? C::NCH : C::CA); ++ch) {
+      load_pieces(ch);
+      Kx::issue_chunk(tr[0], ch, tile_of(0), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+    }
+  }
 
   // epilogue inputs of this thread's first output (loaded now, used at the end)
   const int nthreads = waves * 64;
@@ -370,10 +397,11 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
     add0 = *((ok && tail.add) ? gaddr<uint16_t>(tail.add, (long)n * 2) : zaddr<uint16_t>(0));
   }
 
-  // ---- 3. staging, pass 1: row maxima (and the LN sums) -----------------------------
-  // A row's pieces fill an aligned group of min(W8, 64) lanes of one round u (or whole
-  // rounds when W8 > 64): a max over the group by lane exchanges, then over the row's rounds.
-  // One lane per row writes it.
+  // ---- 2. staging, per chunk ----------------------------------------------------------
+  // Each (operand row, chunk) takes its own exponent e: the chunk's max |a| * 2^e lies in
+  // [64, 128).  The lane's partial sums are kept in absolute units: a group's scale and bias
+  // are multiplied by 2^-(16 + e) of the lane's operand row in that chunk (an exact power of
+  // two) before they scale the group's exact integer dot product.
   auto values = [&](int u, float a[8], float dsh[8]) __attribute__((always_inline)) {
     const int p = lane + 64 * u, rho = p / C::W8;
     widen8(raw[u], xbf, a);
@@ -390,78 +418,69 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
       }
     }
   };
-  uint32_t rmx[C::NPX];   // max |a| (bit pattern) of the row of each of this lane's pieces
+  float unit[C::NCH][MT];   // 2^-(16 + e) of this lane's C-row operand row (4 mt + c), per chunk
+  bool poison[MT];          // a non-finite operand value: the row's outputs become NaN
 #pragma unroll
-  for (int u = 0; u < C::NPX; ++u) {
-    const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
-    uint32_t m;
-    if constexpr (LN) {
-      float a[8], dsh[8];
-      values(u, a, dsh);
-      m = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, a[e]) & 0x7FFFFFFFu);
-      float s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { s1 += dsh[e]; s2 += dsh[e] * dsh[e]; }
-      s1 = sum8f(s1);
-      s2 = sum8f(s2);
-      const int g = g_lo + (kp >> 3);
-      if ((lane & 7) == 0 && rho < T) {
-        const bool real = g < G;
-        sts[(rho * GWM + (kp >> 3)) * 2] = real ? s1 : 0.0f;
-        sts[(rho * GWM + (kp >> 3)) * 2 + 1] = real ? s2 : 0.0f;
-      }
-    } else {
-      // magnitudes of the 16-bit values, two per dword (their bit patterns order like the
-      // values), widened once at the end
-      us2_t hm = __builtin_bit_cast(us2_t, raw[u][0] & 0x7FFF7FFFu);
-#pragma unroll
-      for (int i = 1; i < 4; ++i) hm = __builtin_elementwise_max(hm, __builtin_bit_cast(us2_t, raw[u][i] & 0x7FFF7FFFu));
-      const uint32_t h = max((uint32_t)hm[0], (uint32_t)hm[1]);
-      m = xbf ? h << 16 : __builtin_bit_cast(uint32_t, f16_lo(h));
-    }
-    rmx[u] = group_max<(C::W8 < 64 ? C::W8 : 64)>(m);
-  }
-  if constexpr (C::W8 > 64) {   // a row spans UPR rounds: combine them
-#pragma unroll
-    for (int u0 = 0; u0 < C::NPX; u0 += C::UPR) {
-      uint32_t m = rmx[u0];
-#pragma unroll
-      for (int k = 1; k < C::UPR; ++k) m = max(m, rmx[u0 + k]);
-#pragma unroll
-      for (int k = 0; k < C::UPR; ++k) rmx[u0 + k] = m;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < C::NPX; ++u) {   // one lane per row publishes it (for the lanes' units)
-    const int p = lane + 64 * u, rho = p / C::W8;
-    if ((p % C::W8) == 0) rowmax[rho] = rmx[u];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-
-  // this lane's operand rows (one per block) and their unit 2^-(16 + e)
-  float unscale[MT];
-  bool poison[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint32_t mb = rowmax[4 * mt + c];
-    unscale[mt] = __builtin_bit_cast(float, (uint32_t)(127 - 16 - row_exp(mb)) << 23);
-    poison[mt] = (mb >> 23) >= 255u;   // a non-finite operand value: the row's outputs become NaN
-  }
-
-  // ---- 4. staging, pass 2 (per chunk): X, its group sums and the byte-plane image ----
-  // Image row 3 rho + v (v = 0 top bytes, 1 middle, 2 low) holds, per group of the chunk,
-  // the 64 bytes in the order lane group kq reads them: 8-bit k = 16 kq + b; 4-bit
-  // k = {0, 32, 16, 48}[kq] + 8 (b >> 3) + 2 (b & 3) + ((b >> 2) & 1).
+  for (int mt = 0; mt < MT; ++mt) poison[mt] = false;
   // the ones row (operand rows 4r + 3 of every block read it)
   if (lane < C::CG * 8) *reinterpret_cast<u2_t*>(img + 3 * C::RMAX * C::IP + 8 * lane) = (u2_t){0x01010101u, 0x01010101u};
-  auto stage_chunk = [&](int ch) __attribute__((always_inline)) {
+  i4_t af[C::AG][MT];
+  float gxf[C::AG][MT];
+  const int arow = lane & 15, akq = lane >> 4;   // A operand: row arow, k-quarter akq
+  // Pass 1: the max |a| of each (row, chunk) over a group of min(W8, 64) lanes (a chunk of a
+  // longer row fills one round u), published by one lane; with LN also the shifted sums.
+  // Pass 2: X = trunc(a 2^(16 + e)) split into its three bytes, written in the order lane
+  // group kq reads them (image row 3 rho + v: v = 0 top bytes, 1 middle, 2 low; 8-bit
+  // k = 16 kq + b, 4-bit k = {0, 32, 16, 48}[kq] + 8 (b >> 3) + 2 (b & 3) + ((b >> 2) & 1)).
+  // Then the chunk's fragments into slots [base, base + CG), and their group sums of X.
+  auto stage = [&](int ch, int base) __attribute__((always_inline)) {
+    uint32_t rmx[C::NPX];
 #pragma unroll
     for (int u = 0; u < C::NPX; ++u) {
-      if (C::NCH > 1 && (u % C::UPR) != ch) continue;   // compile-time per (u, ch) when unrolled
+      if (C::NCH > 1 && (u % C::UPR) != ch) continue;
+      const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
+      uint32_t m;
+      if constexpr (LN) {
+        float a[8], dsh[8];
+        values(u, a, dsh);
+        m = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, a[e]) & 0x7FFFFFFFu);
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { s1 += dsh[e]; s2 += dsh[e] * dsh[e]; }
+        s1 = sum8f(s1);
+        s2 = sum8f(s2);
+        const int g = g_lo + (kp >> 3);
+        if ((lane & 7) == 0 && rho < T) {
+          const bool real = g < G;
+          sts[(rho * GWM + (kp >> 3)) * 2] = real ? s1 : 0.0f;
+          sts[(rho * GWM + (kp >> 3)) * 2 + 1] = real ? s2 : 0.0f;
+        }
+      } else {
+        // magnitudes of the 16-bit values, two per dword (their bit patterns order like the
+        // values), widened once at the end
+        us2_t hm = __builtin_bit_cast(us2_t, raw[u][0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) hm = __builtin_elementwise_max(hm, __builtin_bit_cast(us2_t, raw[u][i] & 0x7FFF7FFFu));
+        const uint32_t h = max((uint32_t)hm[0], (uint32_t)hm[1]);
+        m = xbf ? h << 16 : __builtin_bit_cast(uint32_t, f16_lo(h));
+      }
+      rmx[u] = group_max<(C::W8 < 64 ? C::W8 : 64)>(m);
+      if ((p % (C::W8 < 64 ? C::W8 : 64)) == 0) rowmax[rho] = rmx[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t mb = rowmax[4 * mt + c];
+      unit[ch][mt] = __builtin_bit_cast(float, (uint32_t)(127 - 16 - row_exp(mb)) << 23);
+      poison[mt] = poison[mt] || (mb >> 23) >= 255u;
+    }
+#pragma unroll
+    for (int u = 0; u < C::NPX; ++u) {
+      if (C::NCH > 1 && (u % C::UPR) != ch) continue;
       const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
       const int gg = kp >> 3, pp = kp & 7;
       float a[8], dsh[8];
@@ -480,20 +499,12 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
       }
       const int kq = BITS == 8 ? (pp >> 1) : kq4(pp >> 1);
       const int col = (gg % C::CG) * 64 + kq * 16 + 8 * (pp & 1);
-      if (rho < C::RMAX) {
-        *reinterpret_cast<u2_t*>(img + (3 * rho + 0) * C::IP + col) = (u2_t){h0, h1};
-        *reinterpret_cast<u2_t*>(img + (3 * rho + 1) * C::IP + col) = (u2_t){m0, m1};
-        *reinterpret_cast<u2_t*>(img + (3 * rho + 2) * C::IP + col) = (u2_t){l0, l1};
-      }
+      *reinterpret_cast<u2_t*>(img + (3 * rho + 0) * C::IP + col) = (u2_t){h0, h1};
+      *reinterpret_cast<u2_t*>(img + (3 * rho + 1) * C::IP + col) = (u2_t){m0, m1};
+      *reinterpret_cast<u2_t*>(img + (3 * rho + 2) * C::IP + col) = (u2_t){l0, l1};
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-  };
-  // fragments of groups [ch CG, (ch + 1) CG) into slots [base, base + CG)
-  i4_t af[C::AG][MT];
-  float gxf[C::AG][MT];
-  const int arow = lane & 15, akq = lane >> 4;   // A operand: row arow, k-quarter akq
-  auto load_frags = [&](int ch, int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::CG; ++q)
 #pragma unroll
@@ -517,10 +528,10 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
       }
   };
 
-  // ---- 5. the tiles --------------------------------------------------------------
-  // acc (per block) in units of 2^-(16 + e) of this lane's operand row.
-  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot, float acc[MT])
-      __attribute__((always_inline)) {
+  // ---- 3. the tiles --------------------------------------------------------------
+  // acc (per block): this lane's partial of (operand row 4 mt + c, column j), absolute units.
+  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot, const float un[MT],
+                        float acc[MT]) __attribute__((always_inline)) {
     const i4_t bop = Kx::operand_b(d, gg);
     // scale and bias of group gg for column j: dword gg/2 of the lane's scales (biases), half gg&1
     const uint32_t sw = r.sb[gg >> 1];
@@ -533,8 +544,8 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
     for (int mt = 0; mt < MT; ++mt) {
       const i4_t cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[slot][mt], bop, (i4_t){0, 0, 0, 0}, 0, 0, 0);
       const float cf = fmaf((float)cc[0], 65536.0f, fmaf((float)cc[1], 256.0f, fmaf((float)cc[3], 32896.0f, (float)cc[2])));
-      acc[mt] = fmaf(s, cf, acc[mt]);
-      acc[mt] = fmaf(bb, gxf[slot][mt], acc[mt]);
+      acc[mt] = fmaf(s * un[mt], cf, acc[mt]);
+      acc[mt] = fmaf(bb * un[mt], gxf[slot][mt], acc[mt]);
     }
   };
   // the code dword set of group gg (4-bit: exchange lane halves once per step)
@@ -548,20 +559,25 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
       return (u4_t){(uint32_t)e02[0], (uint32_t)e13[0], (uint32_t)e02[1], (uint32_t)e13[1]};
     }
   };
+  // the groups of chunk ch of one tile, fragments from slots [base, base + CG)
+  auto chunk_step = [&](const typename Kx::TileRegs& r, int ch, int base, float acc[MT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < C::CG; q += (BITS == 4 ? 2 : 1)) {
+      const int gg = ch * C::CG + q;
+      const u4_t dd = codes_of(r, gg);
+      group_step(r, dd, gg, base + q, unit[ch], acc);
+      if constexpr (BITS == 4) group_step(r, dd, gg + 1, base + q + 1, unit[ch], acc);
+    }
+  };
   auto put_partial = [&](int i, const float acc[MT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float v = poison[mt] ? __builtin_nanf("") : acc[mt] * unscale[mt];
-      parts[((i * kWaves + wv) * MT + mt) * 64 + lane] = v;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      parts[((i * kWaves + wv) * MT + mt) * 64 + lane] = poison[mt] ? __builtin_nanf("") : acc[mt];
   };
 
   if constexpr (C::RES) {
 #pragma unroll
-    for (int ch = 0; ch < C::NCH; ++ch) {
-      stage_chunk(ch);
-      load_frags(ch, ch * C::CG);
-    }
+    for (int ch = 0; ch < C::NCH; ++ch) stage(ch, ch * C::CG);
     for (int q0 = 0; q0 < nq; q0 += R) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -569,33 +585,24 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
 #pragma unroll
-        for (int gg = 0; gg < GWM; ++gg) {
-          if (BITS == 4 && (gg & 1)) continue;
-          const u4_t dd = codes_of(tr[r], gg);
-          group_step(tr[r], dd, gg, gg, acc);
-          if constexpr (BITS == 4) group_step(tr[r], dd, gg + 1, gg + 1, acc);
-        }
+        for (int ch = 0; ch < C::NCH; ++ch) chunk_step(tr[r], ch, ch * C::CG, acc);
         const int q = q0 + r;
         if (q >= z) put_partial(q - z, acc);
-        Kx::issue(tr[r], tile_of(q + R), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo, c, j);
+        issue_tile(tr[r], tile_of(q + R));
       }
     }
   } else {
-    // one tile: stage a chunk, then contract its groups
     float acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
 #pragma unroll
     for (int ch = 0; ch < C::NCH; ++ch) {
-      stage_chunk(ch);
-      load_frags(ch, 0);
-#pragma unroll
-      for (int q = 0; q < C::CG; ++q) {
-        const int gg = ch * C::CG + q;
-        if (BITS == 4 && (gg & 1)) continue;
-        const u4_t dd = codes_of(tr[0], gg);
-        group_step(tr[0], dd, gg, q, acc);
-        if constexpr (BITS == 4) group_step(tr[0], dd, gg + 1, q + 1, acc);
+      stage(ch, 0);
+      chunk_step(tr[0], ch, 0, acc);
+      if (ch + C::CA < C::NCH) {
+        load_pieces(ch + C::CA);
+        Kx::issue_chunk(tr[0], ch + C::CA, tile_of(0), ntiles, w0, p1, s0, p2, b0, p3, N, gateup, row_bytes, G, g_lo,
+                        c, j);
       }
     }
     put_partial(0, acc);   // one tile: ntw == 1
