@@ -10,21 +10,26 @@ projections, each byte read once (activations and outputs are reported separatel
 Weights rotate over enough copies to total >= 1 GiB, so the 256 MB Infinity Cache cannot
 serve them; everything is resident in HBM before the timed region.  The timed steps are
 captured into one HIP graph (after eager warmup steps and one untimed replay) and replayed
-once, bracketed by HIP events on the stream the graph runs on, with device synchronization
-on both sides: that is the GPU time of the calls, without the ~10 us of host work a Python
-call costs (which would otherwise bound every call under ~10 us).  The same steps launched
-eagerly from Python are reported too (us_per_call_eager).
+several times, each replay bracketed by HIP events on the stream the graph runs on, with
+device synchronization on both sides: that is the GPU time of the calls, without the
+~10 us of host work a Python call costs.  The headline value is the median over the
+replays; p10 / median / p90 are reported with it (us_per_call_stats).  Also reported: the
+same steps launched eagerly from Python (us_per_call_eager) and on one weight set that
+stays cache-resident (us_per_call_warm).
 
-read_ceiling: the library's plain streaming read (qlin_stream_read, 16-byte loads and
-nothing else) over the same number of bytes, rotated and timed the same way: the rate a
-pure read reaches on this device, next to which the fused call's rate can be read.
+read_ceiling: the library's plain streaming read (qlin_stream_read_config, 16-byte loads
+and nothing else) over the same number of bytes, rotated and timed the same way, the best
+of a small sweep of launches (grid, loads in flight, non-temporal or not): the rate a pure
+read of that size reaches on this device.
 
-Also reported: the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual 8-bit
-with 32 rows), the 124-pass LN+linear chain (hipGraph replay vs eager launches), the whole
-MLP around the headline projection (qlin_mlp: gate/up then down with the residual), one
-attend pass, one sampling step (qlin_sample), one quantized-KV decode attention step
-(qlin_kvq_decode), and a CPU baseline: the fp64 oracle timed on the host on a bounded sample of
-the workload.
+Also reported: the headline workload at one shard's shape of an 8-way split along N (1792
+rows per projection), the other workloads (plain fp16 linear, LN+GELU 8-bit, LN+residual
+8-bit with 32 rows), the 124-pass LN+linear chain (hipGraph replay vs eager launches), the
+whole MLP around the headline projection (qlin_mlp: gate/up then down with the residual),
+one attend pass, one sampling step (qlin_sample), one quantized-KV decode attention step
+(qlin_kvq_decode), and a CPU baseline: the fp64 oracle timed on the host on a bounded
+sample of the workload, on one thread and on every host core (the core count and CPU model
+are reported).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu] [--only-main]
 """
@@ -81,11 +86,12 @@ def _time_calls(fn, n_copies, steps, warmup):
     return start.elapsed_time(end)
 
 
-def _time_graph(fn, n_copies, steps, warmup):
+def _time_graph(fn, n_copies, steps, warmup, replays=1):
     """Warmup calls eagerly, then exactly `steps` calls (cycling over the weight copies)
-    captured into one HIP graph; one untimed replay uploads it, one timed replay runs the
-    steps back to back, bracketed by events on the stream the graph runs on.  Returns ms
-    of the timed replay (GPU time of the calls, without per-call host overhead)."""
+    captured into one HIP graph; one untimed replay uploads it, then `replays` timed replays
+    run the steps back to back, each bracketed by events on the stream the graph runs on.
+    Returns the ms of each timed replay (GPU time of the calls, without per-call host
+    overhead)."""
     torch = _torch()
     for i in range(warmup):
         fn(i % n_copies)
@@ -96,28 +102,53 @@ def _time_graph(fn, n_copies, steps, warmup):
             fn((warmup + i) % n_copies)
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
+    out = []
+    for _ in range(replays):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end))
     del g
-    return start.elapsed_time(end)
+    return out
+
+
+def _stats(us_list):
+    """p10 / median / p90 of per-call microseconds over the replays."""
+    a = np.sort(np.asarray(us_list, dtype=np.float64))
+    return dict(p10=round(float(np.quantile(a, 0.1)), 3), median=round(float(np.median(a)), 3),
+                p90=round(float(np.quantile(a, 0.9)), 3), replays=int(a.size))
+
+
+# (blocks of 512 threads, loads in flight per thread, non-temporal): the launches of the
+# plain streaming read the ceiling takes the best of
+READ_SWEEP = [(256, 4, True), (256, 4, False), (512, 4, True), (256, 8, True), (1024, 8, True), (1024, 16, False),
+              (1024, 16, True)]
 
 
 def read_ceiling(nbytes, steps, warmup):
-    """The device's streaming-read rate over nbytes (qlin_stream_read: 16-byte loads, no
-    other work), rotated over >= 1 GiB of buffers and timed like the fused calls."""
-    from decode_linear_amd import qlin_stream_read
+    """The device's streaming-read rate over nbytes: the best of a small sweep of launches of
+    the library's plain 16-byte read (qlin_stream_read_config: no work beyond the loads),
+    rotated over >= 1 GiB of buffers and timed like the fused calls.  The ceiling depends on
+    the size (the launch's fixed cost weighs more on small reads): it is reported for this
+    size only."""
+    from decode_linear_amd import qlin_stream_read_config
     torch = _torch()
     nbytes = -(-nbytes // 16) * 16
     n_copies = max(2, -(-ROTATE_BYTES // nbytes))
     bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_copies)]
     part = torch.zeros(1024, dtype=torch.int32, device="cuda")
-    ms = _time_graph(lambda i: qlin_stream_read(bufs[i], part), n_copies, steps, warmup)
-    us = ms * 1e3 / steps
+    sweep = []
+    for blocks, unroll, nt in READ_SWEEP:
+        ms = _time_graph(lambda i: qlin_stream_read_config(bufs[i], blocks, unroll, nt, part), n_copies, steps, warmup,
+                         replays=3)
+        us = min(ms) * 1e3 / steps
+        sweep.append(dict(blocks=blocks, unroll=unroll, nontemporal=nt, us=round(us, 3)))
+    best = min(sweep, key=lambda r: r["us"])
     del bufs
-    return dict(bytes=nbytes, copies=n_copies, us=us, gbs=nbytes / (us * 1e-6) / 1e9)
+    return dict(bytes=nbytes, copies=n_copies, us=best["us"], gbs=nbytes / (best["us"] * 1e-6) / 1e9,
+                best=best, sweep=sweep)
 
 
 def _rotated(make, nbytes):
@@ -152,11 +183,14 @@ def _pack(w_f32, bits):
     return q
 
 
-def bench_swiglu(steps, warmup):
+def bench_swiglu(steps, warmup, n_override=None, replays=7):
+    """The headline workload (or its N cut to one shard's rows per projection): cold (weights
+    rotated over >= 1 GiB) p10/median/p90 over graph replays, eager, and warm (one weight
+    set, MALL-resident)."""
     import synth
     from decode_linear_amd import qlin_gateup_swiglu
     torch = _torch()
-    case = synth.workload(4)
+    case = synth.workload(4, scale_n=n_override)
     g0, u0 = _pack(case.gate, 4), _pack(case.up, 4)
     del case.gate, case.up
     wbytes = g0.nbytes + u0.nbytes
@@ -169,11 +203,15 @@ def bench_swiglu(steps, warmup):
         g, u = weights[i]
         qlin_gateup_swiglu(x, g, u, out=y)
 
-    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    per = [ms * 1e3 / steps for ms in _time_graph(step, n_copies, steps, warmup, replays=replays)]
+    st = _stats(per)
     us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
+    warm = [ms * 1e3 / steps for ms in _time_graph(step, 1, steps, warmup, replays=3)]
     other = case.x.size * 2 + y.numel() * 2
-    return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=4, weight_bytes=wbytes, other_bytes=other,
-                copies=n_copies, us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
+    name = case.name if n_override is None else f"{case.name}-shard{14336 // case.N}"
+    return dict(name=name, T=case.T, K=case.K, N=case.N, bits=4, weight_bytes=wbytes, other_bytes=other,
+                copies=n_copies, us=st["median"], us_stats=st, gbs=wbytes / (st["median"] * 1e-6) / 1e9,
+                us_eager=us_eager, us_warm=round(float(np.median(warm)), 3))
 
 
 def bench_linear(c, steps, warmup):
@@ -197,10 +235,12 @@ def bench_linear(c, steps, warmup):
     def step(i):
         qlin_linear(x, weights[i], ln=ln, act=case.act, residual=res, out=y)
 
-    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    st = _stats([ms * 1e3 / steps for ms in _time_graph(step, n_copies, steps, warmup, replays=5)])
+    us = st["median"]
     us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
+    us_warm = float(np.median([ms * 1e3 / steps for ms in _time_graph(step, 1, steps, warmup, replays=3)]))
     return dict(name=case.name, T=case.T, K=case.K, N=case.N, bits=case.bits, weight_bytes=wbytes, copies=n_copies,
-                us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
+                us=us, us_stats=st, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager, us_warm=us_warm)
 
 
 def bench_mlp(steps, warmup):
@@ -223,10 +263,11 @@ def bench_mlp(steps, warmup):
     def step(i):
         qlin_mlp(x, *weights[i], residual=res, h=h, out=y)
 
-    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    st = _stats([ms * 1e3 / steps for ms in _time_graph(step, n_copies, steps, warmup, replays=5)])
+    us = st["median"]
     us_eager = _time_calls(step, n_copies, steps, warmup) * 1e3 / steps
     return dict(name=case.name, T=case.T, K=case.K, I=case.I, Hout=case.Hout, bits=4, weight_bytes=wbytes,
-                copies=n_copies, dispatches=2, us=us, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
+                copies=n_copies, dispatches=2, us=us, us_stats=st, gbs=wbytes / (us * 1e-6) / 1e9, us_eager=us_eager)
 
 
 def bench_attend(steps, warmup):
@@ -245,7 +286,7 @@ def bench_attend(steps, warmup):
     def step(i):
         qlin_attend(qkv, kv, case.H, case.HD, out=out, kv_out=kv_out)
 
-    us = _time_graph(step, 1, steps, warmup) * 1e3 / steps
+    us = _time_graph(step, 1, steps, warmup)[0] * 1e3 / steps
     nbytes = (qkv.numel() + kv.numel() + kv_out.numel() + out.numel()) * 2
     return dict(name=case.name, H=case.H, HD=case.HD, P=case.P, T=case.T, bytes=nbytes, us=us,
                 gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
@@ -270,7 +311,7 @@ def bench_sample(steps, warmup):
     def step(i):
         qlin_sample(lg, g, 1, tb, pre, 1.0 / 0.9, 64, out=out, code=code)
 
-    us = _time_graph(step, 1, steps, warmup) * 1e3 / steps
+    us = _time_graph(step, 1, steps, warmup)[0] * 1e3 / steps
     nbytes = case.n * (2 + 4) + (2 * n_prev + 2) * case.D * 2 + 4
     return dict(name=case.name, n=case.n, D=case.D, n_prev=n_prev, top_k=64, bytes=nbytes, us=us,
                 gbs=nbytes / (us * 1e-6) / 1e9, bound="latency")
@@ -300,7 +341,7 @@ def bench_kvq(steps, warmup):
     def step(i):
         qlin_kvq_decode(q, caches[i][0], caches[i][1], c.KV, c.GS, c.bits, out=out, workspace=ws)
 
-    us = _time_graph(step, n_copies, steps, warmup) * 1e3 / steps
+    us = _time_graph(step, n_copies, steps, warmup)[0] * 1e3 / steps
     nbytes = cache_bytes + 2 * c.H * c.D * 2
     return dict(name=c.name, H=c.H, KV=c.KV, N=c.N, D=c.D, bits=c.bits, group=c.GS, cache_bytes=cache_bytes,
                 copies=n_copies, dispatches=2, us=us, gbs=nbytes / (us * 1e-6) / 1e9)
@@ -346,10 +387,21 @@ def bench_chain(replays, warmup):
                 us_per_frame_graph=us_graph * P, gbs_graph=per_pass / (us_graph * 1e-6) / 1e9)
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s):
     """The oracle (plain fp64 C++, untuned) on the host: the SwiGLU workload restricted to
-    its first Ns output rows per projection, called repeatedly from one thread per core
-    until about target_s seconds of wall time; reported in weight GB/s of that sample."""
+    its first Ns output rows per projection, called repeatedly on one thread and then from
+    one thread per host core until about target_s seconds of wall time in all; reported in
+    weight GB/s of that sample (the all-core rate is the value)."""
     import oracle
     import synth
     case = synth.workload(4, scale_n=1024)      # same distributions; N cut to the sample
@@ -360,27 +412,32 @@ def cpu_baseline(target_s):
     t0 = time.time()
     oracle.gateup(case.x, case.x_dtype, 4, gw[:3], uw[:3])
     one = time.time() - t0
-    threads = max(1, min(os.cpu_count() or 1, 16))
-    per_thread = max(1, int(target_s / max(one, 1e-3) / 1.5))
-    done = [0] * threads
 
-    def work(k):
-        for _ in range(per_thread):
-            oracle.gateup(case.x, case.x_dtype, 4, gw[:3], uw[:3])
-            done[k] += 1
+    def run(threads, seconds):
+        per_thread = max(1, int(seconds / max(one, 1e-3) / 1.2 / (1 if threads == 1 else 1)))
+        done = [0] * threads
 
-    t0 = time.time()
-    ts = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
-    for t in ts:
-        t.start()
-    for t in ts:
-        t.join()
-    wall = time.time() - t0
-    calls = sum(done)
-    return {"value": round(calls * wbytes / wall / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"SwiGLU workload cut to N={Ns} rows per projection (K=4096, 4-bit): {calls} oracle calls "
-                      f"on {threads} host threads in {wall:.1f} s; {one * 1e3:.0f} ms per call single-threaded",
-            "us_per_call_full_workload_est": round(one * (14336 / Ns) * 1e6, 1)}
+        def work(k):
+            for _ in range(per_thread):
+                oracle.gateup(case.x, case.x_dtype, 4, gw[:3], uw[:3])
+                done[k] += 1
+        t0 = time.time()
+        ts = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        wall = time.time() - t0
+        return sum(done), wall
+
+    cores = os.cpu_count() or 1
+    c1, w1 = run(1, target_s * 0.3)
+    cn, wn = run(cores, target_s * 0.7)
+    return {"value": round(cn * wbytes / wn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"SwiGLU workload cut to N={Ns} rows per projection (K=4096, 4-bit): {cn} oracle calls on "
+                      f"{cores} host threads in {wn:.1f} s, and {c1} calls on 1 thread in {w1:.1f} s",
+            "value_1_thread": round(c1 * wbytes / w1 / 1e9, 4), "cpu_model": _cpu_model(),
+            "us_per_call_full_workload_est_1_thread": round(w1 / c1 * (14336 / Ns) * 1e6, 1)}
 
 
 def copy_probe(nbytes):
@@ -429,7 +486,8 @@ def main():
     if not a.only_main:
         # each secondary workload is reported on its own: one that fails records its error
         # and does not take the headline line down with it
-        runs = [(f"linear-config-{c}", lambda c=c: bench_linear(c, a.steps, a.warmup)) for c in (1, 2, 3)]
+        runs = [("swiglu-shard8", lambda: bench_swiglu(a.steps, a.warmup, n_override=14336 // 8, replays=5))]
+        runs += [(f"linear-config-{c}", lambda c=c: bench_linear(c, a.steps, a.warmup)) for c in (1, 2, 3)]
         runs += [("chain", lambda: bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))),
                  ("mlp", lambda: bench_mlp(a.steps, a.warmup)), ("attend", lambda: bench_attend(a.steps, a.warmup)),
                  ("sample", lambda: bench_sample(a.steps, a.warmup)), ("kvq", lambda: bench_kvq(a.steps, a.warmup))]
@@ -440,6 +498,8 @@ def main():
                 extra[label] = {"error": f"{type(exc).__name__}: {exc}"}
                 continue
             extra[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
+            if label == "swiglu-shard8":
+                extra[r["name"]]["note"] = "one shard of an 8-way split along N (N = 1792 per projection)"
             if "gbs" in r:
                 extra[r["name"]]["pct_peak"] = round(100 * r["gbs"] / PEAK_HBM_GBS, 2)
     us = main_r["us"]
@@ -461,11 +521,15 @@ def main():
                    "weights": "4-bit affine, group 64, fp16 scale/bias", "activations": "bf16",
                    "weight_bytes_per_call": main_r["weight_bytes"], "rotation_copies": main_r["copies"]},
         "us_per_call": round(us, 3),
+        "us_per_call_stats": main_r["us_stats"],
         "us_per_call_eager": round(main_r["us_eager"], 3),
+        "us_per_call_warm": main_r["us_warm"],
         "pct_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
         "read_ceiling": {"gbs": round(ceil_r["gbs"], 2), "us": round(ceil_r["us"], 3), "bytes": ceil_r["bytes"],
                          "frac_of_peak": round(ceil_r["gbs"] / PEAK_HBM_GBS, 4),
-                         "fused_frac_of_ceiling": round(achieved / ceil_r["gbs"], 4)},
+                         "fused_frac_of_ceiling": round(achieved / ceil_r["gbs"], 4),
+                         "best_launch": ceil_r["best"], "sweep": ceil_r["sweep"],
+                         "note": "plain 16-byte reads of the same byte count; size-dependent"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic()},
     }

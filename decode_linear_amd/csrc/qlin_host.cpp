@@ -425,17 +425,26 @@ qlin_status qlin_mlp(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_we
   return launch(h, x_dtype, T, down, nullptr, nullptr, QLIN_ACT_NONE, residual, nullptr, y, y_dtype, s);
 }
 
-qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream) {
+qlin_status qlin_stream_read_config(const void* buf, int64_t bytes, uint32_t* partial, int32_t blocks, int32_t unroll,
+                                   int32_t nontemporal, void* stream) {
   if (!buf || !partial) return QLIN_ERR_NULL;
   if (bytes < 16 || bytes % 16 != 0) return QLIN_ERR_SHAPE;
+  if (blocks < 1 || blocks > QLIN_STREAM_READ_BLOCKS) return QLIN_ERR_ARG;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16) return QLIN_ERR_ARG;
+  if (nontemporal != 0 && nontemporal != 1) return QLIN_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || (reinterpret_cast<uintptr_t>(partial) & 3u) != 0)
     return QLIN_ERR_ALIGN;
-  const int cus = cu_count();
-  const int grid = cus < QLIN_STREAM_READ_BLOCKS ? cus : QLIN_STREAM_READ_BLOCKS;
-  if (qlin::launch_stream_read(buf, bytes, partial, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (qlin::launch_stream_read(buf, bytes, partial, blocks, unroll, nontemporal != 0,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
     return QLIN_ERR_HIP;
   g_dispatch[5].fetch_add(1, std::memory_order_relaxed);
   return QLIN_OK;
+}
+
+qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream) {
+  const int cus = cu_count();
+  return qlin_stream_read_config(buf, bytes, partial, cus < QLIN_STREAM_READ_BLOCKS ? cus : QLIN_STREAM_READ_BLOCKS,
+                                 4, 1, stream);
 }
 
 qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, const float* gumbel, float inv_temp,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qlin_s8_shape.h"
+
 namespace qlin {
 
 // Waves per workgroup of the fused kernel.  Each wave owns a fixed slice of K and keeps
@@ -52,33 +54,6 @@ hipError_t launch_fused_bf16(const LinParams& p, int mt, int grid, size_t lds, h
 int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K);
 size_t fused_lds_bytes(int bits, int rows, int chunk_steps, long K, int mt);
 
-// Arguments of one launch of the int8 streaming kernel (qlin_s8.h), chosen by the host.
-struct S8Launch {
-  const void* x;                            // (T, K), fp16 or bf16
-  const void* w0; const void* s0; const void* b0;   // codes, scales, biases (gate for gate/up)
-  const void* p1; const void* p2; const void* p3;   // gate/up: up's codes, scales, biases; LN: gamma, beta
-  int K, T, N, x_bf16, gateup, ln, bits;
-  void* y; const void* res; const void* add;
-  float eps;
-  int y_dtype, act;
-  int MT, GWM, D, waves, grid;   // D: tiles of the fullest workgroup
-};
-namespace s8 {
-// Device addresses fit in the low 48 bits; the kernel's shape words ride above them.
-constexpr int kTagShift = 48;
-// Largest tile count a workgroup of this shape takes (VGPRs for the loads of every tile in
-// flight at once, and LDS for their partials); 0 when the shape is not instantiated.
-constexpr int max_tiles(int mt, int gwm) {
-  return mt == 1 ? (gwm <= 16 ? 8 : (gwm == 32 ? 1 : 0))
-       : mt == 2 ? (gwm <= 4 ? 8 : (gwm == 8 ? 4 : 0))
-       : mt == 3 ? (gwm <= 4 ? 4 : 0)
-       : mt == 9 ? (gwm == 2 ? 1 : 0) : 0;
-}
-// Ring slots for workgroups of more than one tile: the next tile's loads are in flight
-// while the wave computes.  Deeper rings measured slower on the SwiGLU workload (3 and 4
-// slots: 18.2 and 17.3 against 17.0 us): with more requests outstanding the weight
-// stream's rate drops.
-}  // namespace s8
 // One launcher per code width and prologue (qlin_s8_q{4,8}_ln{0,1}.hip).
 hipError_t launch_s8_q4_ln0(const S8Launch& a, hipStream_t s);
 hipError_t launch_s8_q4_ln1(const S8Launch& a, hipStream_t s);
@@ -143,7 +118,9 @@ struct KvqParams {
 hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s);
 
 // Plain 16-byte streaming read of `bytes` (a multiple of 16) at buf; block b writes the XOR
-// fold of the words it read to partial[b] (grid blocks of 512 threads).
-hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int grid, hipStream_t s);
+// fold of the words it read to partial[b] (grid blocks of 512 threads, `unroll` loads in
+// flight per thread: 1, 2, 4, 8 or 16; non-temporal loads when nt).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* partial, int grid, int unroll, bool nt,
+                              hipStream_t s);
 
 }  // namespace qlin

@@ -11,22 +11,30 @@
 //   sum_k (s q_k + b) a_k = s * sum_k q_k a_k + b * sum_k a_k.
 //
 // How it maps onto CDNA4:
-//   * A workgroup of up to 8 waves takes up to D output tiles of 16 weight rows (8 gate +
-//     8 up rows for gate/up).  Wave w owns a window of GWM quantization groups of K for the
-//     whole launch; every lane of it issues the loads of ALL of the workgroup's tiles at
-//     kernel entry (16-byte loads: lane (c, j) reads 16 bytes of weight row j, c = lane/16),
-//     so the weight stream starts with the kernel and the staging below runs under it.
+//   * A workgroup of up to 8 waves takes the output tiles blockIdx.x, + grid, ... (16 weight
+//     rows each; 8 gate + 8 up rows for gate/up).  Wave w owns a window of GWM quantization
+//     groups of K for the whole launch; lane (c, j) reads 16-byte pieces of weight row j
+//     (c = lane / 16).  The shape words ride in the pointer arguments that gfx950 preloads
+//     into SGPRs, so the first loads go out at wave launch, before any kernel-argument fetch.
+//   * Short windows (the activation fragments of the whole window fit in VGPRs): the wave
+//     issues every activation piece and then the loads of a ring of R tiles at entry, stages
+//     the activations under those loads, and computes the ring slot by slot, issuing the
+//     next tile's loads into the slot it has just finished.  Every slot is computed, with
+//     leading all-zero tiles where the tile count is not a multiple of R, so no branch joins
+//     the paths (a join would wait for every load in flight).
+//   * Long windows (one tile per workgroup): the window is staged and consumed in chunks of
+//     8 groups; the loads of CA chunks are in flight ahead of the chunk being staged.
 //   * Exact products on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  Each operand row
-//     a (an activation row; with LayerNorm also gamma and beta) becomes, per wave window, a
-//     24-bit fixed-point integer X = trunc(a * 2^(16+e)), e the power of two that puts the
-//     window's max |a| in [64, 128).  X is split into three bytes: the signed top byte and
+//     a (an activation row; with LayerNorm also gamma and beta) becomes, per staging chunk,
+//     a 24-bit fixed-point integer X = trunc(a * 2^(16+e)), e the power of two that puts the
+//     chunk's max |a| in [64, 128).  X is split into three bytes: the signed top byte and
 //     the two low bytes, each taken as (byte - 128).  Codes enter as int8 values: 4-bit codes
 //     as they are (0..15), 8-bit codes as q - 128.  One more operand row of ones gives the
 //     group's code sum, which restores the byte offsets:
 //       sum_k X_k q_k = 65536 C_hi + 256 C_mid + C_lo + 32896 C_ones    (4-bit),
 //     with 128 * sum_k X_k added for 8-bit codes.  Every product and every sum inside the
 //     MFMA is an exact integer; fp32 rounding enters only per group, where the exact group
-//     dot product is scaled by its fp16 scale, and in the final sums.
+//     dot product is scaled by its fp16 scale times 2^-(16+e), and in the final sums.
 //   * A 16-row MFMA block holds four operand rows: C rows 4r .. 4r + 3 are the three bytes
 //     of operand row r and the ones row, so a lane holds all parts of one (row, column)
 //     and combines them in registers.

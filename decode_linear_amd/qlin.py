@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_status_string,
+qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_stream_read_config, qlin_status_string,
 qlin_dispatch_count, qlin_set_path,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
@@ -78,6 +78,7 @@ def lib():
     L.qlin_chain_destroy.argtypes = [vp]
     L.qlin_chain_destroy.restype = None
     L.qlin_stream_read.argtypes = [vp, i64, vp, vp]
+    L.qlin_stream_read_config.argtypes = [vp, i64, vp, i32, i32, i32, vp]
     L.qlin_mlp.argtypes = [vp, i32, i32, W, W, W, Ln, vp, vp, vp, i32, vp]
     L.qlin_sample.argtypes = [vp, i32, i32, vp, ctypes.c_float, i32, vp, vp, i32, i32, i32, vp, vp, vp]
     L.qlin_kvq_decode_workspace.argtypes = [i32, i32, i32]
@@ -92,7 +93,7 @@ def lib():
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
-                 "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
+                 "qlin_stream_read", "qlin_stream_read_config", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -334,6 +335,21 @@ def qlin_stream_read(buf: torch.Tensor, partial: Optional[torch.Tensor] = None, 
     st = lib().qlin_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partial), _stream(stream))
     if st != 0:
         raise QlinError(st, "qlin_stream_read")
+    return partial
+
+
+def qlin_stream_read_config(buf: torch.Tensor, blocks: int, unroll: int, nontemporal: bool,
+                            partial: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """qlin_stream_read with its launch chosen: blocks of 512 threads, unroll loads in flight
+    per thread, non-temporal or ordinary loads."""
+    if partial is None:
+        partial = torch.zeros(STREAM_READ_BLOCKS, dtype=torch.int32, device=buf.device)
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    st = lib().qlin_stream_read_config(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partial), int(blocks),
+                                       int(unroll), 1 if nontemporal else 0, _stream(stream))
+    if st != 0:
+        raise QlinError(st, "qlin_stream_read_config")
     return partial
 
 

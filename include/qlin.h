@@ -95,8 +95,9 @@ typedef struct {
  *   y         (T, N) of y_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16), written with one
  *             round-to-nearest-even from an fp32 value; it must not overlap x or residual.
  *   stream    hipStream_t as void*.
- * Accumulation is fp32; activations enter the contraction with at least 22 significant
- * bits.  Returns QLIN_OK once the work is enqueued. */
+ * Accumulation is fp32.  Each activation enters the contraction with an error of at most
+ * 2^-22 times the largest magnitude among the elements of its row in the same aligned
+ * block of 512 (with LayerNorm, of the values (x - x[t, 0]) * gamma).  Returns QLIN_OK once the work is enqueued. */
 qlin_status qlin_linear(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w,
                         const qlin_ln* ln, qlin_act act, const void* residual, const void* add,
                         void* y, qlin_dtype y_dtype, void* stream);
@@ -284,6 +285,15 @@ qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, in
  * on a launch failure. */
 #define QLIN_STREAM_READ_BLOCKS 1024
 qlin_status qlin_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream);
+
+/* The same read with its launch chosen by the caller, so that a measurement can take the best
+ * of several: `blocks` workgroups of 512 threads (1 .. QLIN_STREAM_READ_BLOCKS; blocks past
+ * it write nothing), `unroll` 16-byte loads in flight per thread (1, 2, 4, 8 or 16), and
+ * non-temporal loads when `nontemporal` is 1 (0: ordinary loads).  qlin_stream_read is
+ * blocks = min(compute units, QLIN_STREAM_READ_BLOCKS), unroll 4, non-temporal.
+ * Errors as qlin_stream_read, plus QLIN_ERR_ARG for an unsupported launch. */
+qlin_status qlin_stream_read_config(const void* buf, int64_t bytes, uint32_t* partial, int32_t blocks,
+                                    int32_t unroll, int32_t nontemporal, void* stream);
 
 /* Number of kernels this library has enqueued in this process, by entry point:
  * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample,

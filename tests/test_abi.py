@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
-                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
+                 "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode",
+                 "qlin_stream_read_config", "qlin_set_path"):
         assert must in names
 
 
@@ -228,6 +229,25 @@ def test_stream_read_validation(q):
     assert f(QKV, 1000, AO, None) == -2       # not a multiple of 16
     assert f(QKV + 8, 1024, AO, None) == -5
     assert f(QKV, 1024, AO + 2, None) == -5
+
+
+def test_stream_read_config_validation(q):
+    f = q.lib().qlin_stream_read_config
+    assert f(None, 1024, AO, 4, 4, 1, None) == -1
+    assert f(QKV, 1000, AO, 4, 4, 1, None) == -2
+    assert f(QKV, 1024, AO, 0, 4, 1, None) == -7       # blocks below 1
+    assert f(QKV, 1024, AO, 1025, 4, 1, None) == -7    # blocks past QLIN_STREAM_READ_BLOCKS
+    assert f(QKV, 1024, AO, 4, 3, 1, None) == -7       # unroll not 1, 2, 4, 8 or 16
+    assert f(QKV, 1024, AO, 4, 4, 2, None) == -7       # nontemporal not 0 or 1
+    assert f(QKV + 8, 1024, AO, 4, 4, 1, None) == -5
+
+
+def test_set_path_validation(q):
+    f = q.lib().qlin_set_path
+    assert f(5) == -1 and f(-1) == -1
+    prev = f(1)
+    assert prev in (0, 1)
+    assert f(prev) == 1
 
 
 def test_mlp_validation(q):
