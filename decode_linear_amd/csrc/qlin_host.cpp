@@ -12,7 +12,7 @@
 
 namespace {
 
-std::atomic<int64_t> g_dispatch[8];
+std::atomic<int64_t> g_dispatch[9];
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
 constexpr int64_t kMaxN = int64_t(1) << 28;
@@ -169,6 +169,7 @@ qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, 
     if (try_s8(x, x_dtype, T, w, up, ln, act, res, add, y, y_dtype, stream, &e)) {
       if (e != hipSuccess) return QLIN_ERR_HIP;
       g_dispatch[up ? 1 : 0].fetch_add(1, std::memory_order_relaxed);
+      g_dispatch[8].fetch_add(1, std::memory_order_relaxed);
       return QLIN_OK;
     }
   }
@@ -551,7 +552,7 @@ int32_t qlin_set_path(int32_t path) {
 }
 
 int64_t qlin_dispatch_count(int32_t which) {
-  if (which < 0 || which > 7) return -1;
+  if (which < 0 || which > 8) return -1;
   return g_dispatch[which].load(std::memory_order_relaxed);
 }
 

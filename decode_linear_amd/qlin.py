@@ -173,11 +173,87 @@ def _check(status: int, where: str):
         raise QlinError(status, where)
 
 
+_ACT_DTYPES = (torch.float16, torch.bfloat16)
+_OUT_DTYPES = (torch.float32, torch.float16, torch.bfloat16)
+
+
+class _Args:
+    """Checks of one call's tensors, raised as ValueError before anything is launched (the C
+    ABI sees only pointers and sizes, so a tensor's shape can only be checked here).  Shapes,
+    contiguity and dtypes first, for every argument; then that all of them sit on one GPU."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.seen = []
+
+    def fail(self, msg: str):
+        raise ValueError(f"{self.where}: {msg}")
+
+    def need(self, name: str, t, shape, dtypes=None, optional=False):
+        """t: a contiguous tensor of `shape` (None entries: any size) and one of `dtypes`."""
+        if t is None:
+            if optional:
+                return
+            self.fail(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            self.fail(f"{name} must be a torch.Tensor")
+        if t.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape)):
+            want = "(" + ", ".join("*" if e is None else str(e) for e in shape) + ")"
+            self.fail(f"{name} must have shape {want}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            self.fail(f"{name} must be contiguous")
+        if dtypes is not None and t.dtype not in dtypes:
+            self.fail(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+        self.seen.append((name, t))
+
+    def weight(self, name: str, w, K: Optional[int] = None):
+        if not isinstance(w, QWeight):
+            self.fail(f"{name} must be a QWeight")
+        if w.bits not in (4, 8, 16):
+            self.fail(f"{name}.bits must be 4, 8 or 16, got {w.bits}")
+        if K is not None and w.K != K:
+            self.fail(f"{name}.K = {w.K} does not match the activation row length {K}")
+        if w.K <= 0 or w.K % 64 or w.N < 0:
+            self.fail(f"{name} must have K a positive multiple of 64 and N >= 0")
+        if w.bits == 16:
+            self.need(f"{name}.data", w.data, (w.N, w.K), _ACT_DTYPES)
+        else:
+            self.need(f"{name}.data", w.data, (w.N, w.K * w.bits // 32), (torch.int32,))
+            self.need(f"{name}.scales", w.scales, (w.N, w.K // 64), (torch.float16,))
+            self.need(f"{name}.biases", w.biases, (w.N, w.K // 64), (torch.float16,))
+
+    def ln(self, ln, K: int, dtype):
+        if ln is None:
+            return
+        if not isinstance(ln, (tuple, list)) or len(ln) != 3:
+            self.fail("ln must be (gamma, beta, eps)")
+        self.need("gamma", ln[0], (K,), (dtype,))
+        self.need("beta", ln[1], (K,), (dtype,))
+
+    def on_one_gpu(self):
+        dev = None
+        for name, t in self.seen:
+            if not t.is_cuda:
+                self.fail(f"{name} must be on a GPU, got {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                self.fail(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
 def qlin_linear(x: torch.Tensor, w: QWeight, ln=None, act: int = QLIN_ACT_NONE,
                 residual: Optional[torch.Tensor] = None, add: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
     """y (T, N) = [add +] [residual +] act(LN?(x) @ W.T).  ln = (gamma, beta, eps) or None."""
+    c = _Args("qlin_linear")
+    c.need("x", x, (None, None), _ACT_DTYPES)
     T = x.shape[0]
+    c.weight("w", w, x.shape[1])
+    c.ln(ln, w.K, x.dtype)
+    c.need("residual", residual, (T, w.N), (x.dtype,), optional=True)
+    c.need("add", add, (w.N,), (x.dtype,), optional=True)
+    c.need("out", out, (T, w.N), _OUT_DTYPES, optional=True)
+    c.on_one_gpu()
     if out is None:
         out = torch.empty((T, w.N), dtype=out_dtype or x.dtype, device=x.device)
     lnc = _ln(ln)
@@ -191,7 +267,16 @@ def qlin_linear(x: torch.Tensor, w: QWeight, ln=None, act: int = QLIN_ACT_NONE,
 def qlin_gateup_swiglu(x: torch.Tensor, gate: QWeight, up: QWeight, ln=None, out: Optional[torch.Tensor] = None,
                        out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
     """y (T, N) = silu(LN?(x) @ Wg.T) * (LN?(x) @ Wu.T)."""
+    c = _Args("qlin_gateup_swiglu")
+    c.need("x", x, (None, None), _ACT_DTYPES)
     T = x.shape[0]
+    c.weight("gate", gate, x.shape[1])
+    c.weight("up", up, x.shape[1])
+    if (gate.bits, gate.N) != (up.bits, up.N):
+        c.fail("gate and up must have the same bits and N")
+    c.ln(ln, gate.K, x.dtype)
+    c.need("out", out, (T, gate.N), _OUT_DTYPES, optional=True)
+    c.on_one_gpu()
     if out is None:
         out = torch.empty((T, gate.N), dtype=out_dtype or x.dtype, device=x.device)
     lnc = _ln(ln)
@@ -207,7 +292,19 @@ def qlin_mlp(x: torch.Tensor, gate: QWeight, up: QWeight, down: QWeight, ln=None
              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, stream=None):
     """(y, h): h (T, I) = silu(LN?(x) @ Wg.T) * (LN?(x) @ Wu.T) in x's dtype, then
     y (T, Hout) = [residual +] h @ Wd.T (two dispatches; h is the caller's workspace)."""
+    c = _Args("qlin_mlp")
+    c.need("x", x, (None, None), _ACT_DTYPES)
     T = x.shape[0]
+    c.weight("gate", gate, x.shape[1])
+    c.weight("up", up, x.shape[1])
+    if (gate.bits, gate.N) != (up.bits, up.N):
+        c.fail("gate and up must have the same bits and N")
+    c.weight("down", down, gate.N)
+    c.ln(ln, gate.K, x.dtype)
+    c.need("residual", residual, (T, down.N), (x.dtype,), optional=True)
+    c.need("h", h, (T, gate.N), (x.dtype,), optional=True)
+    c.need("out", out, (T, down.N), _OUT_DTYPES, optional=True)
+    c.on_one_gpu()
     if h is None:
         h = torch.empty((T, gate.N), dtype=x.dtype, device=x.device)
     if out is None:
@@ -253,8 +350,16 @@ def qlin_attend(qkv: torch.Tensor, kv: Optional[torch.Tensor], heads: int, head_
 
 def qlin_pack_affine(w: torch.Tensor, bits: int, flag: Optional[torch.Tensor] = None, stream=None) -> QWeight:
     """Quantize an fp32 (N, K) device tensor to the affine group-64 format."""
+    c = _Args("qlin_pack_affine")
+    c.need("w", w, (None, None), (torch.float32,))
+    if bits not in (4, 8):
+        c.fail(f"bits must be 4 or 8, got {bits}")
     N, K = w.shape
     dev = w.device
+    if K <= 0 or K % 64:
+        c.fail(f"K must be a positive multiple of 64, got {K}")
+    c.need("flag", flag, (None,), (torch.int32,), optional=True)
+    c.on_one_gpu()
     codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=dev)
     scales = torch.empty((N, K // 64), dtype=torch.float16, device=dev)
     biases = torch.empty((N, K // 64), dtype=torch.float16, device=dev)
@@ -266,6 +371,10 @@ def qlin_pack_affine(w: torch.Tensor, bits: int, flag: Optional[torch.Tensor] = 
 
 def qlin_unpack_affine(w: QWeight, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """fp32 (N, K) = fmaf(q, s, b) (or the widened dense element)."""
+    c = _Args("qlin_unpack_affine")
+    c.weight("w", w)
+    c.need("out", out, (w.N, w.K), (torch.float32,), optional=True)
+    c.on_one_gpu()
     if out is None:
         out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.data.device)
     wc = w.c()
@@ -287,6 +396,21 @@ class QlinChain:
     passes: dicts with keys x, T, w (QWeight), ln (tuple or None), act, residual, add, y."""
 
     def __init__(self, passes: Sequence[dict], x_dtype: torch.dtype, y_dtype: torch.dtype, capture_stream=None):
+        c = _Args("QlinChain")
+        if x_dtype not in _ACT_DTYPES or y_dtype not in _OUT_DTYPES:
+            c.fail("x_dtype must be float16 or bfloat16, y_dtype one of those or float32")
+        for i, ps in enumerate(passes):
+            w, T, x = ps["w"], int(ps["T"]), ps["x"]
+            c.need(f"passes[{i}].x", x, (None, None), (x_dtype,))
+            c.weight(f"passes[{i}].w", w, x.shape[1])
+            c.ln(ps.get("ln"), w.K, x_dtype)
+            c.need(f"passes[{i}].residual", ps.get("residual"), (None, w.N), (x_dtype,), optional=True)
+            c.need(f"passes[{i}].add", ps.get("add"), (w.N,), (x_dtype,), optional=True)
+            c.need(f"passes[{i}].y", ps["y"], (None, w.N), (y_dtype,))
+            for name in ("x", "y", "residual"):
+                if ps.get(name) is not None and ps[name].shape[0] < T:
+                    c.fail(f"passes[{i}].{name} has fewer than T = {T} rows")
+        c.on_one_gpu()
         self._keep = list(passes)
         arr = (_Pass * len(passes))()
         for i, ps in enumerate(passes):
@@ -404,3 +528,4 @@ def qlin_kvq_decode(q: torch.Tensor, k, v, kv_heads: int, group: int, bits: int,
                                _stream(stream))
     _check(st, "qlin_kvq_decode")
     return out
+

@@ -298,7 +298,8 @@ qlin_status qlin_stream_read_config(const void* buf, int64_t bytes, uint32_t* pa
 /* Number of kernels this library has enqueued in this process, by entry point:
  * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample,
  * 7 = quantized-KV decode (a test can assert a kernel ran; qlin_mlp counts one gate/up and
- * one linear). */
+ * one linear); 8 = how many of the linear and gate/up launches ran on the int8 streaming
+ * kernel rather than the general one.  -1 for any other index. */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Selects the kernel family for 4- and 8-bit qlin_linear / qlin_gateup_swiglu / qlin_mlp

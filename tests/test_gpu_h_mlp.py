@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from helpers import TOL, Packed, TORCH_DT, dev_bits, errors, gate_a, gate_b, host_bits
+from helpers import TAU_FRAC, TOL, Packed, TORCH_DT, dev_bits, errors, gate_a, gate_b, host_bits, host_values
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,28 @@ def _run(c):
     # down stage on the library's own hidden activation (teacher forced)
     y_tf = oracle.linear(h_dev, c.x_dtype, c.bits, do[0], wdt, do[1], do[2], res=c.res)
     gate_a(y32, y_tf, what=c.name + " (teacher forced)")
-    # End to end, y differs from the oracle's y64 by exactly the oracle's down projection
-    # of (h - h_oracle): both sides round h once, and near a tie they may round apart.
-    # That difference is a property of the two h, so the gates above carry the parity.
+    # End to end: y_tf - y64 is exactly the down projection of (h_dev - h_orc) (both sides
+    # round h once, and near a tie they may round apart), so
+    #   |y - y64| <= |y - y_tf| + sum_k |Wd[n, k]| |h_dev - h_orc|[t, k].
+    # The first term is under Gate A; the hidden check bounds |h_dev - h64| by
+    # (TOL + u) max(|h64|, tau_h), and rounding bounds |h_orc - h64| by u |h64|.  Checked
+    # twice: with the observed hidden difference (tight), and with its a-priori bound.
     assert np.isfinite(y64).all()
+    if c.bits == 16:
+        Wd = oracle.widen(do[0], c.x_dtype)
+    else:
+        Wd = oracle.dequant_f64(do[0], do[1], do[2], c.Hout, c.I, c.bits)
+    y = host_values(y32)
+    tau_y = TAU_FRAC * float(np.sqrt(np.mean(y_tf ** 2)))
+    slack = TOL * np.maximum(np.abs(y_tf), tau_y) + 1e-9 * (1.0 + np.abs(y64))
+    dh = np.abs(oracle.widen(h_dev, c.x_dtype) - oracle.widen(h_orc, c.x_dtype))
+    gap = np.abs(y - y64)
+    tight = slack + dh @ np.abs(Wd).T
+    assert np.all(gap <= tight), f"{c.name}: end-to-end y exceeds the propagated bound by {float((gap - tight).max()):.3e}"
+    tau_h = TAU_FRAC * float(np.sqrt(np.mean(h64 ** 2)))
+    dh_max = (TOL + 2 * u) * np.maximum(np.abs(h64), tau_h)
+    prior = slack + dh_max @ np.abs(Wd).T
+    assert np.all(gap <= prior), f"{c.name}: end-to-end y exceeds the a-priori bound"
     y16, _ = qlin_mlp(x, G.q, U.q, Dn.q, ln=ln, residual=res, out_dtype=TORCH_DT[c.x_dtype])
     torch.cuda.synchronize()
     gate_b(y16, y32, y_tf, c.x_dtype, what=c.name)
@@ -82,8 +100,8 @@ def test_mlp_rejects_aliasing_and_shape():
     c = synth.random_mlp(522, 2, 128, 64, 32, 8)
     (G, U, Dn), _, _ = _weights(c)
     x = dev_bits(c.x, c.x_dtype)
-    with pytest.raises(QlinError):
-        qlin_mlp(x, G.q, U.q, G.q)          # down->K (=128) != I (=64)
+    with pytest.raises(ValueError, match="down.K"):
+        qlin_mlp(x, G.q, U.q, G.q)          # down->K (=128) != I (=64): refused by the binding
     big = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
     xa = big[:c.T * c.K].view(c.T, c.K)
     xa.copy_(x)

@@ -1,0 +1,99 @@
+"""Both kernel families of the 4- and 8-bit linear, against the oracle.
+
+By default the library sends a quantized call to the int8 streaming kernel wherever that
+kernel's shape rules admit it, else to the general kernel.  This file checks (1) which
+family each kind of call lands on (dispatch counter 8 counts the int8 kernel's launches),
+and (2) the general kernel, forced with qlin_set_path(1), on the shapes the int8 kernel
+otherwise takes: rows with and without LayerNorm, ragged K and N, long K, epilogues and
+gate/up.  The forced path must stay correct: it is what every call falls back to."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import run_gateup_case, run_linear_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from decode_linear_amd import build
+    build.ensure_built()
+
+
+@pytest.fixture
+def general_path():
+    from decode_linear_amd import qlin_dispatch_count, qlin_set_path
+    prev = qlin_set_path(1)
+    before = qlin_dispatch_count(8)
+    yield
+    assert qlin_set_path(prev) == 1
+    assert qlin_dispatch_count(8) == before, "a call ran on the int8 kernel while the general path was forced"
+
+
+def _s8_launches(fn):
+    from decode_linear_amd import qlin_dispatch_count
+    before = qlin_dispatch_count(8)
+    fn()
+    return qlin_dispatch_count(8) - before
+
+
+@pytest.mark.parametrize("kind,expect", [
+    ("q4-T4", True), ("q8-T4-ln", True), ("q4-T32-ln", True), ("q8-K16384", True),
+    ("gateup-q4", True), ("gateup-q4-ln", False), ("dense-f16", False), ("q4-K192", False)])
+def test_family_chosen(kind, expect):
+    cases = {
+        "q4-T4": lambda: run_linear_case(synth.random_case(9100, 4, 1024, 64, 4, x_dtype=synth.BF16)),
+        "q8-T4-ln": lambda: run_linear_case(synth.random_case(9101, 4, 1024, 64, 8, x_dtype=synth.BF16, ln=True)),
+        "q4-T32-ln": lambda: run_linear_case(synth.random_case(9102, 32, 512, 48, 4, x_dtype=synth.BF16, ln=True)),
+        "q8-K16384": lambda: run_linear_case(synth.random_case(9103, 4, 16384, 32, 8, x_dtype=synth.BF16)),
+        "gateup-q4": lambda: run_gateup_case(synth.random_gateup(9104, 4, 1024, 40, 4)),
+        "gateup-q4-ln": lambda: run_gateup_case(synth.random_gateup(9105, 4, 1024, 40, 4, ln=True)),
+        "dense-f16": lambda: run_linear_case(synth.random_case(9106, 4, 512, 48, 16, x_dtype=synth.F16)),
+        "q4-K192": lambda: run_linear_case(synth.random_case(9107, 3, 192, 40, 4, x_dtype=synth.BF16)),
+    }
+    n = _s8_launches(cases[kind])
+    assert (n > 0) == expect, (kind, n)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("T", [1, 4, 5, 9, 17, 32])
+@pytest.mark.parametrize("ln", [False, True])
+def test_general_rows(general_path, bits, T, ln):
+    case = synth.random_case(9200 + 37 * T + bits + ln, T, 512, 72, bits, x_dtype=synth.BF16, ln=ln,
+                             x_mean=3.0 if ln else 0.0)
+    run_linear_case(case, y_dtypes=(synth.BF16,))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("K,N", [(64, 17), (192, 40), (4160, 33), (16384, 48)])
+def test_general_k_and_n(general_path, bits, K, N):
+    case = synth.random_case(9300 + K + N + bits, 3, K, N, bits, x_dtype=synth.F16, ln=True, act=1)
+    run_linear_case(case, y_dtypes=(synth.F16,))
+
+
+@pytest.mark.parametrize("act,res,add", [(1, True, True), (0, True, False)])
+def test_general_epilogues(general_path, act, res, add):
+    case = synth.random_case(9400 + act + 2 * res, 4, 1024, 64, 8, x_dtype=synth.BF16, act=act, res=res, add=add)
+    run_linear_case(case, y_dtypes=(synth.BF16,))
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_general_gateup(general_path, T):
+    run_gateup_case(synth.random_gateup(9500 + T, T, 1024, 72, 4))
+    run_gateup_case(synth.random_gateup(9510 + T, T, 512, 24, 8))
+
+
+def test_paths_agree_within_tolerance():
+    """The same call on both families: each meets the oracle's gate (checked in the helper);
+    their outputs differ only by rounding, never by a structural error."""
+    from decode_linear_amd import qlin_set_path
+    case = synth.random_case(9600, 4, 4096, 256, 4, x_dtype=synth.BF16, ln=True)
+    a, _ = run_linear_case(case)
+    prev = qlin_set_path(1)
+    try:
+        b, _ = run_linear_case(case)
+    finally:
+        qlin_set_path(prev)
+    assert np.isfinite(a) and np.isfinite(b)
