@@ -500,13 +500,17 @@ int64_t qlin_kvq_decode_workspace(int32_t heads, int32_t n_rows, int32_t head_di
   return (int64_t)heads * G * ((int64_t)head_dim + 2) * 4;
 }
 
-qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads, int32_t n_rows,
-                            int32_t head_dim, int32_t group_size, int32_t bits, const uint32_t* k_codes,
-                            const void* k_scales, const void* k_biases, const uint32_t* v_codes,
-                            const void* v_scales, const void* v_biases, qlin_dtype sb_dtype, void* workspace,
-                            int64_t workspace_bytes, void* out, qlin_dtype out_dtype, void* stream) {
-  if (!q || !k_codes || !k_scales || !k_biases || !v_codes || !v_scales || !v_biases || !workspace || !out)
-    return QLIN_ERR_NULL;
+namespace {
+// Checks and launch shared by qlin_kvq_decode and qlin_kvq_decode_noalloc.  ws == null asks
+// for the library's static scratch (the no-allocation entry point); otherwise ws holds
+// ws_bytes bytes of caller workspace.
+qlin_status kvq_run(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads, int32_t n_rows,
+                    int32_t head_dim, int32_t group_size, int32_t bits, const uint32_t* k_codes,
+                    const void* k_scales, const void* k_biases, const uint32_t* v_codes, const void* v_scales,
+                    const void* v_biases, qlin_dtype sb_dtype, void* ws, int64_t ws_bytes, void* out,
+                    qlin_dtype out_dtype, void* stream) {
+  const bool own = ws == nullptr;
+  if (!q || !k_codes || !k_scales || !k_biases || !v_codes || !v_scales || !v_biases || !out) return QLIN_ERR_NULL;
   if ((q_dtype != QLIN_F16 && q_dtype != QLIN_BF16) || (sb_dtype != QLIN_F16 && sb_dtype != QLIN_BF16) ||
       (out_dtype != QLIN_F32 && out_dtype != QLIN_F16 && out_dtype != QLIN_BF16))
     return QLIN_ERR_DTYPE;
@@ -516,34 +520,59 @@ qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, in
   if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return QLIN_ERR_SHAPE;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || group_size > head_dim) return QLIN_ERR_SHAPE;
   if (!aligned(q, 2) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 2) ||
-      !aligned(k_biases, 2) || !aligned(v_scales, 2) || !aligned(v_biases, 2) || !aligned(workspace, 4) ||
+      !aligned(k_biases, 2) || !aligned(v_scales, 2) || !aligned(v_biases, 2) || (!own && !aligned(ws, 4)) ||
       !aligned(out, dtype_size(out_dtype)))
     return QLIN_ERR_ALIGN;
   const int64_t need = qlin_kvq_decode_workspace(heads, n_rows, head_dim);
-  if (workspace_bytes < need) return QLIN_ERR_ARG;
+  if (!own && need > ws_bytes) return QLIN_ERR_ARG;
+  if (own && need > (int64_t)QLIN_KVQ_SCRATCH_BYTES) return QLIN_ERR_SCRATCH;
   const size_t ob = (size_t)heads * head_dim * dtype_size(out_dtype);
   const size_t rows = (size_t)kv_heads * n_rows;
   const size_t cb = rows * head_dim * bits / 8, sbb = rows * (head_dim / group_size) * 2;
-  if (overlaps(out, ob, q, (size_t)heads * head_dim * 2) || overlaps(out, ob, workspace, (size_t)need) ||
+  if (overlaps(out, ob, q, (size_t)heads * head_dim * 2) || (!own && overlaps(out, ob, ws, (size_t)need)) ||
       overlaps(out, ob, k_codes, cb) || overlaps(out, ob, v_codes, cb) || overlaps(out, ob, k_scales, sbb) ||
       overlaps(out, ob, k_biases, sbb) || overlaps(out, ob, v_scales, sbb) || overlaps(out, ob, v_biases, sbb))
     return QLIN_ERR_ARG;
-  for (const void* in : {static_cast<const void*>(q), static_cast<const void*>(k_codes),
-                         static_cast<const void*>(v_codes), k_scales, k_biases, v_scales, v_biases}) {
-    const size_t len = in == q ? (size_t)heads * head_dim * 2 : (in == k_codes || in == v_codes) ? cb : sbb;
-    if (overlaps(workspace, (size_t)need, in, len)) return QLIN_ERR_ARG;
+  if (!own) {
+    for (const void* in : {static_cast<const void*>(q), static_cast<const void*>(k_codes),
+                           static_cast<const void*>(v_codes), k_scales, k_biases, v_scales, v_biases}) {
+      const size_t len = in == q ? (size_t)heads * head_dim * 2 : (in == k_codes || in == v_codes) ? cb : sbb;
+      if (overlaps(ws, (size_t)need, in, len)) return QLIN_ERR_ARG;
+    }
   }
+  float* part = static_cast<float*>(ws);
+  if (own && qlin::kvq_scratch(&part) != hipSuccess) return QLIN_ERR_HIP;
   qlin::KvqParams a{};
   a.q = q; a.q_dtype = q_dtype; a.kc = k_codes; a.ks = k_scales; a.kb = k_biases;
   a.vc = v_codes; a.vs = v_scales; a.vb = v_biases; a.sb_dtype = sb_dtype;
   a.H = heads; a.KV = kv_heads; a.N = n_rows; a.D = head_dim; a.GS = group_size; a.bits = bits;
   a.block = kvq_block(n_rows); a.G = (n_rows + a.block - 1) / a.block;
-  a.opart = static_cast<float*>(workspace);
+  a.opart = part;
   a.stats = a.opart + (size_t)heads * a.G * head_dim;
   a.out = out; a.out_dtype = out_dtype;
   if (qlin::launch_kvq_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return QLIN_ERR_HIP;
   g_dispatch[7].fetch_add(1, std::memory_order_relaxed);
   return QLIN_OK;
+}
+}  // namespace
+
+qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads, int32_t n_rows,
+                            int32_t head_dim, int32_t group_size, int32_t bits, const uint32_t* k_codes,
+                            const void* k_scales, const void* k_biases, const uint32_t* v_codes,
+                            const void* v_scales, const void* v_biases, qlin_dtype sb_dtype, void* workspace,
+                            int64_t workspace_bytes, void* out, qlin_dtype out_dtype, void* stream) {
+  if (!workspace) return QLIN_ERR_NULL;
+  return kvq_run(q, q_dtype, heads, kv_heads, n_rows, head_dim, group_size, bits, k_codes, k_scales, k_biases,
+                 v_codes, v_scales, v_biases, sb_dtype, workspace, workspace_bytes, out, out_dtype, stream);
+}
+
+qlin_status qlin_kvq_decode_noalloc(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads,
+                                    int32_t n_rows, int32_t head_dim, int32_t group_size, int32_t bits,
+                                    const uint32_t* k_codes, const void* k_scales, const void* k_biases,
+                                    const uint32_t* v_codes, const void* v_scales, const void* v_biases,
+                                    qlin_dtype sb_dtype, void* out, qlin_dtype out_dtype, void* stream) {
+  return kvq_run(q, q_dtype, heads, kv_heads, n_rows, head_dim, group_size, bits, k_codes, k_scales, k_biases,
+                 v_codes, v_scales, v_biases, sb_dtype, nullptr, 0, out, out_dtype, stream);
 }
 
 int32_t qlin_set_path(int32_t path) {
@@ -566,6 +595,7 @@ const char* qlin_status_string(qlin_status s) {
     case QLIN_ERR_ALIGN: return "pointer misaligned";
     case QLIN_ERR_HIP: return "HIP runtime error";
     case QLIN_ERR_ARG: return "invalid argument";
+    case QLIN_ERR_SCRATCH: return "the call needs more device scratch than the static buffer holds";
   }
   return "unknown status";
 }

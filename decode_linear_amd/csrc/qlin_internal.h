@@ -116,6 +116,9 @@ struct KvqParams {
   int out_dtype;            // 0 fp32, 1 fp16, 2 bf16
 };
 hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s);
+// Device address, on the current device, of the static scratch array behind
+// qlin_kvq_decode_noalloc (QLIN_KVQ_SCRATCH_BYTES); looked up once per device.
+hipError_t kvq_scratch(float** ptr);
 
 // Plain 16-byte streaming read of `bytes` (a multiple of 16) at buf; block b writes the XOR
 // fold of the words it read to partial[b] (grid blocks of 512 threads, `unroll` loads in

@@ -19,6 +19,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "qlin.h"
 #include "qlin_internal.h"
 
 namespace qlin {
@@ -229,6 +232,31 @@ hipError_t launch_block(const KvqParams& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// The partials of qlin_kvq_decode_noalloc: one copy of this array lives on every GPU the
+// library runs on.  Host code never passes its name to a kernel (on the host the name is a
+// stand-in, not a device address): it passes the address kvq_scratch looked up.
+static __device__ __align__(256) float scratch[QLIN_KVQ_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t kvq_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s) {
   const hipError_t e = a.bits == 4 ? launch_block<4>(a, s) : launch_block<8>(a, s);

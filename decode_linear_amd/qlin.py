@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
-qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_stream_read_config, qlin_status_string,
+qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_kvq_decode_noalloc, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_stream_read_config, qlin_status_string,
 qlin_dispatch_count, qlin_set_path,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlin.so"
 QLIN_F32, QLIN_F16, QLIN_BF16 = 0, 1, 2
 QLIN_ACT_NONE, QLIN_ACT_GELU = 0, 1
 STATUS = {0: "QLIN_OK", -1: "QLIN_ERR_NULL", -2: "QLIN_ERR_SHAPE", -3: "QLIN_ERR_DTYPE", -4: "QLIN_ERR_BITS",
-          -5: "QLIN_ERR_ALIGN", -6: "QLIN_ERR_HIP", -7: "QLIN_ERR_ARG"}
+          -5: "QLIN_ERR_ALIGN", -6: "QLIN_ERR_HIP", -7: "QLIN_ERR_ARG", -8: "QLIN_ERR_SCRATCH"}
+QLIN_KVQ_SCRATCH_BYTES = 8 << 20
 
 _TORCH_TO_QLIN = {torch.float32: QLIN_F32, torch.float16: QLIN_F16, torch.bfloat16: QLIN_BF16}
 _QLIN_TO_TORCH = {v: k for k, v in _TORCH_TO_QLIN.items()}
@@ -85,6 +86,8 @@ def lib():
     L.qlin_kvq_decode_workspace.restype = i64
     L.qlin_kvq_decode.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp,
                                   i32, vp]
+    L.qlin_kvq_decode_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp,
+                                          i32, vp]
     L.qlin_set_path.argtypes = [i32]
     L.qlin_set_path.restype = i32
     L.qlin_dispatch_count.argtypes = [i32]
@@ -93,7 +96,8 @@ def lib():
     L.qlin_status_string.restype = ctypes.c_char_p
     for name in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_attend", "qlin_attend_check", "qlin_chain_create", "qlin_chain_launch", "qlin_chain_passes",
-                 "qlin_stream_read", "qlin_stream_read_config", "qlin_mlp", "qlin_sample", "qlin_kvq_decode"):
+                 "qlin_stream_read", "qlin_stream_read_config", "qlin_mlp", "qlin_sample", "qlin_kvq_decode",
+                 "qlin_kvq_decode_noalloc"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -529,3 +533,20 @@ def qlin_kvq_decode(q: torch.Tensor, k, v, kv_heads: int, group: int, bits: int,
     _check(st, "qlin_kvq_decode")
     return out
 
+
+def qlin_kvq_decode_noalloc(q: torch.Tensor, k, v, kv_heads: int, group: int, bits: int, out: torch.Tensor,
+                            stream=None):
+    """qlin_kvq_decode with the library's static device scratch instead of a workspace: the
+    call allocates nothing (out is the caller's).  Calls that overlap on one GPU race."""
+    H, D = q.shape
+    kc, ks, kb = k
+    vc, vs, vb = v
+    N = kc.shape[1]
+    for t in (q, kc, ks, kb, vc, vs, vb, out):
+        if not t.is_contiguous():
+            raise ValueError("qlin_kvq_decode_noalloc: tensors must be contiguous")
+    st = lib().qlin_kvq_decode_noalloc(_ptr(q), _dtype(q), H, kv_heads, N, D, group, bits, _ptr(kc), _ptr(ks),
+                                       _ptr(kb), _ptr(vc), _ptr(vs), _ptr(vb), _dtype(ks), _ptr(out), _dtype(out),
+                                       _stream(stream))
+    _check(st, "qlin_kvq_decode_noalloc")
+    return out

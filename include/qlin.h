@@ -48,7 +48,8 @@ typedef enum {
   QLIN_ERR_BITS = -4,   /* bits not in {4, 8, 16} or group_size != 64 */
   QLIN_ERR_ALIGN = -5,  /* a pointer does not have the required alignment */
   QLIN_ERR_HIP = -6,    /* the HIP runtime reported an error */
-  QLIN_ERR_ARG = -7     /* any other invalid argument (act code, eps, n_passes, ...) */
+  QLIN_ERR_ARG = -7,    /* any other invalid argument (act code, eps, n_passes, ...) */
+  QLIN_ERR_SCRATCH = -8 /* the call needs more than the library's static device scratch */
 } qlin_status;
 
 typedef enum { QLIN_F32 = 0, QLIN_F16 = 1, QLIN_BF16 = 2 } qlin_dtype;
@@ -97,7 +98,8 @@ typedef struct {
  *   stream    hipStream_t as void*.
  * Accumulation is fp32.  Each activation enters the contraction with an error of at most
  * 2^-22 times the largest magnitude among the elements of its row in the same aligned
- * block of 512 (with LayerNorm, of the values (x - x[t, 0]) * gamma).  Returns QLIN_OK once the work is enqueued. */
+ * block of 512 (with LayerNorm, of the values (x - x[t, 0]) * gamma).  Returns QLIN_OK once
+ * the work is enqueued. */
 qlin_status qlin_linear(const void* x, qlin_dtype x_dtype, int32_t T, const qlin_weight* w,
                         const qlin_ln* ln, qlin_act act, const void* residual, const void* add,
                         void* y, qlin_dtype y_dtype, void* stream);
@@ -269,6 +271,24 @@ qlin_status qlin_kvq_decode(const void* q, qlin_dtype q_dtype, int32_t heads, in
                             const void* k_scales, const void* k_biases, const uint32_t* v_codes,
                             const void* v_scales, const void* v_biases, qlin_dtype sb_dtype, void* workspace,
                             int64_t workspace_bytes, void* out, qlin_dtype out_dtype, void* stream);
+
+/* qlin_kvq_decode without the workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The block partials go to a static device array of QLIN_KVQ_SCRATCH_BYTES bytes that the
+ * library holds on every GPU it runs on until the process ends; the call itself allocates
+ * nothing.  Every call on one GPU shares that GPU's array: calls that may overlap in time
+ * on one GPU (on different streams, or from several host threads) race and must be
+ * serialized by the caller.  Nothing in the array needs to start at zero: each call writes
+ * every partial it reads.  Arguments, layouts and errors as for qlin_kvq_decode, except
+ * QLIN_ERR_SCRATCH (nothing enqueued) when qlin_kvq_decode_workspace(heads, n_rows,
+ * head_dim) exceeds QLIN_KVQ_SCRATCH_BYTES, and QLIN_ERR_HIP when the array's device
+ * address cannot be obtained on the current device (looked up on the first call there). */
+#define QLIN_KVQ_SCRATCH_BYTES (8 << 20)
+qlin_status qlin_kvq_decode_noalloc(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv_heads,
+                                    int32_t n_rows, int32_t head_dim, int32_t group_size, int32_t bits,
+                                    const uint32_t* k_codes, const void* k_scales, const void* k_biases,
+                                    const uint32_t* v_codes, const void* v_scales, const void* v_biases,
+                                    qlin_dtype sb_dtype, void* out, qlin_dtype out_dtype, void* stream);
 
 /* ---- measurement aid ----------------------------------------------------------------
  * qlin_stream_read: the device's streaming-read ceiling for the weight stream's access (the

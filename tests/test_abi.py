@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     for must in ("qlin_linear", "qlin_gateup_swiglu", "qlin_pack_affine", "qlin_unpack_affine", "qlin_check",
                  "qlin_chain_create", "qlin_chain_launch", "qlin_chain_destroy", "qlin_status_string",
                  "qlin_dispatch_count", "qlin_attend", "qlin_attend_check", "qlin_stream_read", "qlin_mlp", "qlin_sample", "qlin_kvq_decode",
-                 "qlin_stream_read_config", "qlin_set_path"):
+                 "qlin_stream_read_config", "qlin_set_path", "qlin_kvq_decode_noalloc"):
         assert must in names
 
 
@@ -41,8 +41,8 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_status_strings(q):
-    for s in range(-7, 1):
-        assert q.qlin_status_string(s)
+    for s in range(-8, 1):
+        assert q.qlin_status_string(s) and q.qlin_status_string(s) != "unknown status"
     assert q.qlin_status_string(0) == "ok"
 
 
@@ -318,3 +318,28 @@ def test_kvq_validation(q):
     assert call(out=O + 1) == -5
     assert call(wsb=ws(16, 8192, 256) - 4) == -7
     assert call(out=WS + 64) == -7 and call(out=KC + 64) == -7
+
+
+def test_kvq_noalloc_validation(q):
+    """The allocation-free decode checks its arguments as qlin_kvq_decode does and refuses a
+    call whose partials would not fit the static scratch, all before any HIP call."""
+    f, ws = q.lib().qlin_kvq_decode_noalloc, q.lib().qlin_kvq_decode_workspace
+    assert q.QLIN_KVQ_SCRATCH_BYTES == 8 << 20
+    Q, KC, KS, KB, VC, VS, VB, O = (0x9000000 + 0x1000000 * i for i in range(8))
+    ok = dict(q=Q, qdt=q.QLIN_BF16, H=16, KV=8, N=8192, D=256, GS=64, bits=4, kc=KC, ks=KS, kb=KB, vc=VC, vs=VS,
+              vb=VB, sbdt=q.QLIN_BF16, out=O, odt=q.QLIN_BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["qdt"], a["H"], a["KV"], a["N"], a["D"], a["GS"], a["bits"], a["kc"], a["ks"], a["kb"],
+                 a["vc"], a["vs"], a["vb"], a["sbdt"], a["out"], a["odt"], None)
+    assert call(q=None) == -1 and call(vb=None) == -1 and call(out=None) == -1
+    assert call(qdt=q.QLIN_F32) == -3 and call(bits=2) == -4 and call(H=12) == -2 and call(D=96) == -2
+    assert call(q=Q + 1) == -5 and call(out=O + 1) == -5
+    assert call(out=KC + 64) == -7
+    # 64 heads x 512 blocks of 128 rows x (128 + 2) floats = 17 MB of partials: too much
+    assert ws(64, 65536, 128) > q.QLIN_KVQ_SCRATCH_BYTES
+    assert call(H=64, KV=8, N=65536, D=128) == -8
+    # the largest heads x rows that still fit, just past it
+    assert ws(32, 64 * 128, 256) <= q.QLIN_KVQ_SCRATCH_BYTES < ws(32, 64 * 128 * 4, 256)
+    assert call(H=32, KV=8, N=64 * 128 * 4, D=256) == -8

@@ -1,6 +1,6 @@
 """A fresh process whose FIRST call of each library entry point happens inside a HIP graph
-capture (torch.cuda.graph): no lazy set-up of the library (device queries, kernel
-loading) may break the capture or be left out of the graph.
+capture (torch.cuda.graph): no lazy set-up of the library (device queries, the static
+scratch's address, kernel loading) may break the capture or be left out of the graph.
 The graph is then replayed three times, with unrelated eager work and a refill of every
 output between replays, and each replay must equal the same calls made eagerly, bit for
 bit.  Inputs are random tensors of the library's formats (no oracle involved: the parity
@@ -67,6 +67,7 @@ def outputs():
         code=torch.empty((1,), dtype=torch.int32, device=dev),
         smp=torch.empty((4, 256), dtype=bf, device=dev),
         kvq=torch.empty((H, D), dtype=torch.float32, device=dev),
+        kvq0=torch.empty((H, D), dtype=bf, device=dev),
     )
 
 def calls(o):
@@ -80,6 +81,7 @@ def calls(o):
     q.qlin_attend(qkv, kv, 4, 64, out=o["att"], kv_out=o["att_kv"])
     q.qlin_sample(logits, gumbel, 0, table, prefix, 1.0, 64, out=o["smp"], code=o["code"])
     q.qlin_kvq_decode((qh), (kc, ks, kb), (vc, vs, vb), KV, 64, 4, out=o["kvq"], workspace=ws)
+    q.qlin_kvq_decode_noalloc(qh, (kc, ks, kb), (vc, vs, vb), KV, 64, 4, o["kvq0"])
 
 for i in range(9):
     assert q.qlin_dispatch_count(i) == 0, "a library kernel ran before the capture"
