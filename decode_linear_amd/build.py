@@ -36,11 +36,16 @@ CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 
 def _compile(src: str) -> str:
+    """Compile one source; the compiler's per-kernel register, scratch and LDS report goes to
+    _build/<source>.resources.txt (a test checks that no kernel spills registers)."""
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    with open(os.path.join(BUILD_DIR, src + ".resources.txt"), "w") as fh:
+        fh.write(r.stderr)
     return obj
 
 

@@ -19,7 +19,8 @@ from typing import Optional, Sequence
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlin.so")
+# QLIN_LIB_PATH names another build of the same library (the sanitizer test loads one).
+LIB_PATH = os.environ.get("QLIN_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlin.so")
 
 QLIN_F32, QLIN_F16, QLIN_BF16 = 0, 1, 2
 QLIN_ACT_NONE, QLIN_ACT_GELU = 0, 1

@@ -40,7 +40,11 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes, dtype codes and activation codes travel as plain 32-bit integers: a caller
+ * may pass any value, and an out-of-range one is rejected with a status (an enum parameter
+ * type would make such a value undefined behaviour in C++ before it could be checked). */
+typedef int32_t qlin_status;
+enum {
   QLIN_OK = 0,
   QLIN_ERR_NULL = -1,   /* a required pointer is NULL */
   QLIN_ERR_SHAPE = -2,  /* T, K or N outside the accepted range */
@@ -50,11 +54,13 @@ typedef enum {
   QLIN_ERR_HIP = -6,    /* the HIP runtime reported an error */
   QLIN_ERR_ARG = -7,    /* any other invalid argument (act code, eps, n_passes, ...) */
   QLIN_ERR_SCRATCH = -8 /* the call needs more than the library's static device scratch */
-} qlin_status;
+};
 
-typedef enum { QLIN_F32 = 0, QLIN_F16 = 1, QLIN_BF16 = 2 } qlin_dtype;
+typedef int32_t qlin_dtype;
+enum { QLIN_F32 = 0, QLIN_F16 = 1, QLIN_BF16 = 2 };
 
-typedef enum { QLIN_ACT_NONE = 0, QLIN_ACT_GELU = 1 } qlin_act;
+typedef int32_t qlin_act;
+enum { QLIN_ACT_NONE = 0, QLIN_ACT_GELU = 1 };
 
 /* A weight matrix W of N output rows and K input columns (y = x . W^T).
  *   bits == 16: dense; `data` holds N*K elements of `dtype` (QLIN_F16 or QLIN_BF16, and it

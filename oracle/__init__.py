@@ -23,7 +23,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+BUILD_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB_PATH names another build of oracle.cpp to load (the sanitizer test uses one).
+LIB_PATH = os.environ.get("ORACLE_LIB_PATH") or BUILD_PATH
 SRC_PATH = os.path.join(_HERE, "oracle.cpp")
 
 F32, F16, BF16 = 0, 1, 2
@@ -33,13 +35,13 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile oracle.cpp into liboracle.so with g++ (-O2, no fast-math, no FP contraction)."""
-    if not force and os.path.exists(LIB_PATH):
-        return LIB_PATH
+    if not force and os.path.exists(BUILD_PATH):
+        return BUILD_PATH
     cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-           SRC_PATH, "-o", LIB_PATH + ".tmp"]
+           SRC_PATH, "-o", BUILD_PATH + ".tmp"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    os.replace(BUILD_PATH + ".tmp", BUILD_PATH)
+    return BUILD_PATH
 
 
 def _p(a):
@@ -50,7 +52,7 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    if LIB_PATH == BUILD_PATH and not os.path.exists(LIB_PATH):
         build()
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
