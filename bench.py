@@ -59,6 +59,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-main", action="store_true", help="time only the headline workload")
+    ap.add_argument("--only", default="", help="comma-separated labels of the secondary workloads to time "
+                    "(swiglu-shard8, linear-config-1..3, chain, mlp, attend, sample, kvq); default all")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="instead: run a plain device copy of this many bytes (counter calibration) and exit")
@@ -491,6 +493,9 @@ def main():
         runs += [("chain", lambda: bench_chain(max(4, a.steps // 10), max(2, a.warmup // 4))),
                  ("mlp", lambda: bench_mlp(a.steps, a.warmup)), ("attend", lambda: bench_attend(a.steps, a.warmup)),
                  ("sample", lambda: bench_sample(a.steps, a.warmup)), ("kvq", lambda: bench_kvq(a.steps, a.warmup))]
+        if a.only:
+            keep = set(a.only.split(","))
+            runs = [r for r in runs if r[0] in keep]
         for label, run in runs:
             try:
                 r = run()

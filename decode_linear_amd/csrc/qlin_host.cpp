@@ -132,11 +132,19 @@ bool try_s8(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const q
   // sharing a SIMD would run ahead of the younger and the workgroup wait for it; up to 8
   // waves otherwise (more loads issue at once, and staging is shorter per wave).
   auto window = [&](int waves) { return pow2_ceil(G <= 2 * waves ? 2 : (G + waves - 1) / waves); };
-  auto usable = [&](int g) { return g <= 32 && G % (g < 8 ? g : 8) == 0 && s8::max_tiles(mt, g) > 0; };
+  const int bits = w->bits;
+  const bool lnb = ln != nullptr;
+  auto usable = [&](int g) { return g <= 32 && G % (g < 8 ? g : 8) == 0 && s8::max_tiles(bits, lnb, mt, g) > 0; };
   int gw = window(ntiles > 3 * cu_count() ? 4 : 8);
   if (!usable(gw)) gw = window(8);
   if (!usable(gw)) return false;
-  const int dm = s8::max_tiles(mt, gw);
+  // One tile per workgroup: up to 16 waves where the shorter windows give more than 8 of
+  // them, so that more of the rows' loads are in flight at once.
+  if (ntiles <= cu_count()) {
+    const int g16 = window(16);
+    if ((G + g16 - 1) / g16 > 8 && s8::wide_ok(bits, lnb, mt, g16) && G % (g16 < 8 ? g16 : 8) == 0) gw = g16;
+  }
+  const int dm = (G + gw - 1) / gw > 8 ? 1 : s8::max_tiles(bits, lnb, mt, gw);
   S8Launch a{};
   a.x = x;
   a.w0 = w->data; a.s0 = w->scales; a.b0 = w->biases;
@@ -543,7 +551,7 @@ qlin_status kvq_run(const void* q, qlin_dtype q_dtype, int32_t heads, int32_t kv
   float* part = static_cast<float*>(ws);
   if (own && qlin::kvq_scratch(&part) != hipSuccess) return QLIN_ERR_HIP;
   qlin::KvqParams a{};
-  a.q = q; a.q_dtype = q_dtype; a.kc = k_codes; a.ks = k_scales; a.kb = k_biases;
+  a.q = q; a.q_dtype = q_dtype; a.q_vec = aligned(q, 16) ? 1 : 0; a.kc = k_codes; a.ks = k_scales; a.kb = k_biases;
   a.vc = v_codes; a.vs = v_scales; a.vb = v_biases; a.sb_dtype = sb_dtype;
   a.H = heads; a.KV = kv_heads; a.N = n_rows; a.D = head_dim; a.GS = group_size; a.bits = bits;
   a.block = kvq_block(n_rows); a.G = (n_rows + a.block - 1) / a.block;

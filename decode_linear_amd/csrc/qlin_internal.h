@@ -101,6 +101,7 @@ hipError_t launch_sample(const SampleParams& a, hipStream_t s);
 struct KvqParams {
   const void* q;            // (H, D), q_dtype
   int q_dtype;              // 1 fp16, 2 bf16
+  int q_vec;                // 1: q is 16-byte aligned (read with 16-byte loads)
   const uint32_t* kc;       // (KV, N, D * bits / 32)
   const void* ks;           // (KV, N, D / GS), sb_dtype
   const void* kb;

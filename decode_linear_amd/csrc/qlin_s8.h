@@ -98,20 +98,25 @@ template <typename T> __device__ __forceinline__ const T* untag(const void* p) {
 //   MT  16-row MFMA blocks (4 operand rows each: RMAX = 4 MT operand rows)
 //   GWM quantization groups in a wave's window (power of two, 2 .. 32)
 //   R   ring slots: tiles whose loads are in flight while the wave computes (1 or 2)
-template <int BITS, bool LN, int MT, int GWM, int R>
+//   W   waves per workgroup at most: 8, or 16 for one-tile workgroups (a long K split over
+//       more waves, so that more of its loads are in flight at once)
+template <int BITS, bool LN, int MT, int GWM, int R, int W>
 struct Cfg {
   static constexpr int RMAX = 4 * MT;
   // The operand fragments of the whole window stay in VGPRs when they are few enough;
   // otherwise (a long window, one tile per workgroup) they are staged chunk by chunk,
   // each chunk right before the groups that use it.
-  static constexpr bool RES = GWM * MT * 4 <= 72;
+  // (16-wave workgroups have half the VGPRs per wave: there only windows of up to 8 groups.)
+  static constexpr bool RES = GWM * MT * 4 <= 72 && (W == 8 || GWM <= 8);
   static constexpr int CG = GWM < 8 ? GWM : 8;        // groups staged at once
   static constexpr int NCH = GWM / CG;                 // staging chunks
   static constexpr int AG = RES ? GWM : CG;            // groups of fragments in VGPRs
   // Streamed fragments: chunks whose loads are in flight ahead of the one being staged.  Two
-  // measured best on the MLP's down projection (K = 14336): 17.1 us, against 18.7 with three;
-  // windows of 64 groups on four waves were slower still (19.1 us with two, 21.8 with four).
-  static constexpr int CA = 2;
+  // measured best on 8-wave workgroups for the MLP's down projection (K = 14336): 17.1 us,
+  // against 18.7 with three; windows of 64 groups on four waves were slower still (19.1 us
+  // with two, 21.8 with four).  16-wave workgroups take one: with two the registers spill,
+  // and the MLP measured 34.2 us against 30.8 with one (32.8 on 8 waves).
+  static constexpr int CA = W > 8 ? 1 : 2;
   static constexpr int W8 = 8 * GWM;                   // 8-element pieces per operand row window
   static constexpr int NPX = MT * GWM / 2;             // pieces per lane (RMAX * W8 / 64)
   static constexpr int UPR = GWM >= 8 ? GWM / 8 : 1;   // piece rounds (u) per operand row
@@ -127,11 +132,12 @@ struct Cfg {
   static constexpr int OFF_ST = OFF_MAX + RMAX * 4;    // LN: S1, S2 [RMAX][GWM][2]
   static constexpr int OFF_IMG = (OFF_ST + (LN ? RMAX * GWM * 8 : 0) + 15) / 16 * 16;
   static constexpr int WAVE_BYTES = OFF_IMG + IMG;
-  static constexpr int PMAX = max_tiles(MT, GWM);        // tiles of one workgroup, at most
-  static constexpr int PART_BYTES = PMAX * kWaves * MT * 256;
-  static constexpr int LDS_BYTES = kWaves * WAVE_BYTES + PART_BYTES;
+  static constexpr int PMAX = W > 8 ? 1 : max_tiles(BITS, LN, MT, GWM);   // tiles of one workgroup, at most
+  static constexpr int PART_BYTES = PMAX * W * MT * 256;
+  static constexpr int LDS_BYTES = W * WAVE_BYTES + PART_BYTES;
   static_assert(GWM >= 2 && (GWM & (GWM - 1)) == 0 && GWM <= 32, "windows of 2..32 groups");
   static_assert(PMAX >= 1, "an instantiated shape");
+  static_assert(W == 8 || (W == 16 && R == 1), "8 waves, or 16 for one tile");
   static_assert(RES || (R == 1 && PMAX == 1), "streamed fragments serve one tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
@@ -225,9 +231,9 @@ __device__ __forceinline__ float elem(uint32_t h, bool bf) {
   return bf ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <int BITS, bool LN, int MT, int GWM, int R>
+template <int BITS, bool LN, int MT, int GWM, int R, int W>
 struct Kern {
-  using C = Cfg<BITS, LN, MT, GWM, R>;
+  using C = Cfg<BITS, LN, MT, GWM, R, W>;
 
   // One tile's loads: the codes of this wave's window and the scales (even lane groups) or
   // biases (odd lane groups) of its groups.
@@ -293,12 +299,12 @@ struct Kern {
 // Inverse of the 4-bit k order: the lane group that feeds 16-code run (k >> 4) of a group.
 __device__ __forceinline__ constexpr int kq4(int run) { return run == 0 ? 0 : (run == 1 ? 2 : (run == 2 ? 1 : 3)); }
 
-template <int BITS, bool LN, int MT, int GWM, int R>
-__global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void* w0t, const void* s0t,
-                                                      const void* b0t, const void* p1t, const void* p2t,
-                                                      const void* p3t, const Tail tail) {
-  using C = Cfg<BITS, LN, MT, GWM, R>;
-  using Kx = Kern<BITS, LN, MT, GWM, R>;
+template <int BITS, bool LN, int MT, int GWM, int R, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kernel(
+    const void* xt, const void* w0t, const void* s0t, const void* b0t, const void* p1t, const void* p2t,
+    const void* p3t, const Tail tail) {
+  using C = Cfg<BITS, LN, MT, GWM, R, W>;
+  using Kx = Kern<BITS, LN, MT, GWM, R, W>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   const uint32_t tx = tag_of(xt), tw = tag_of(w0t);
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
   uint32_t* rowmax = reinterpret_cast<uint32_t*>(wbase + C::OFF_MAX);
   float* sts = reinterpret_cast<float*>(wbase + C::OFF_ST);
   unsigned char* img = wbase + C::OFF_IMG;
-  float* parts = reinterpret_cast<float*>(lds + kWaves * C::WAVE_BYTES);
+  float* parts = reinterpret_cast<float*>(lds + W * C::WAVE_BYTES);
 
   // ---- 1. loads -------------------------------------------------------------------
   // Operand pieces: piece p = lane + 64 u is operand row rho = p / W8, piece kp = p % W8 of
@@ -580,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
   auto put_partial = [&](int i, const float acc[MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      parts[((i * kWaves + wv) * MT + mt) * 64 + lane] = poison[mt] ? __builtin_nanf("") : acc[mt];
+      parts[((i * W + wv) * MT + mt) * 64 + lane] = poison[mt] ? __builtin_nanf("") : acc[mt];
   };
 
   if constexpr (C::RES) {
@@ -627,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void s8_kernel(const void* xt, const void
     if (n >= N) continue;
     auto merged = [&](int rho, int col) __attribute__((always_inline)) {
       float v = 0.0f;
-      for (int w = 0; w < waves; ++w) v += parts[((i * kWaves + w) * MT + (rho >> 2)) * 64 + (rho & 3) * 16 + col];
+      for (int w = 0; w < waves; ++w) v += parts[((i * W + w) * MT + (rho >> 2)) * 64 + (rho & 3) * 16 + col];
       return v;
     };
     float v = merged(t, jj);
@@ -663,22 +669,33 @@ namespace qlin {
 namespace s8 {
 
 // Launch of one instantiation (the caller has checked the shape against it).
-template <int BITS, bool LN, int MT, int GWM, int R>
+template <int BITS, bool LN, int MT, int GWM, int R, int W>
 hipError_t launch_one(const S8Launch& a, hipStream_t s) {
   const Tail tail{a.y, a.res, a.add, a.eps, a.y_dtype, a.act};
   auto tp = [](const void* p, uint32_t v) { return reinterpret_cast<const void*>(tag(p, v)); };
-  hipLaunchKernelGGL((s8_kernel<BITS, LN, MT, GWM, R>), dim3(a.grid), dim3(a.waves * 64), 0, s,
+  hipLaunchKernelGGL((s8_kernel<BITS, LN, MT, GWM, R, W>), dim3(a.grid), dim3(a.waves * 64), 0, s,
                      tp(a.x, (uint32_t)(a.K / 64) | ((uint32_t)a.x_bf16 << 15)),
                      tp(a.w0, (uint32_t)(a.T - 1) | ((uint32_t)a.gateup << 5)), tp(a.s0, (uint32_t)a.N & 0xFFFFu),
                      tp(a.b0, (uint32_t)a.N >> 16), tp(a.p1, (uint32_t)a.grid), a.p2, a.p3, tail);
   return hipGetLastError();
 }
 
-// One tile per workgroup: no ring (a second slot would only carry zeros); more: two slots.
+// One tile per workgroup: no ring (a second slot would only carry zeros), and up to 16
+// waves where the shape has that instantiation; more tiles: two slots, up to 8 waves.
 template <int BITS, bool LN, int MT, int GWM>
 hipError_t launch_d(const S8Launch& a, hipStream_t s) {
-  if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1>(a, s);
-  if constexpr (max_tiles(MT, GWM) >= 2) return launch_one<BITS, LN, MT, GWM, 2>(a, s);
+  if (a.waves > 8) {
+    if constexpr (wide_ok(BITS, LN, MT, GWM)) {
+      if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 16>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if constexpr (max_tiles(BITS, LN, MT, GWM) >= 1) {
+    if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 8>(a, s);
+  }
+  if constexpr (max_tiles(BITS, LN, MT, GWM) >= 2) {
+    if (a.D <= max_tiles(BITS, LN, MT, GWM)) return launch_one<BITS, LN, MT, GWM, 2, 8>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -97,3 +97,21 @@ def test_paths_agree_within_tolerance():
     finally:
         qlin_set_path(prev)
     assert np.isfinite(a) and np.isfinite(b)
+
+
+@pytest.mark.parametrize("bits,T,K,N,ln", [
+    (4, 4, 14336, 256, False),    # windows of 16 groups, 14 waves (the MLP's down projection, cut in N)
+    (8, 4, 8192, 64, False),      # windows of 8 groups, 16 waves
+    (4, 2, 8192, 40, True),       # with LayerNorm (windows of 8 groups)
+    (8, 6, 4096, 100, False),     # two 16-row blocks, windows of 4 groups
+    (4, 1, 2048, 17, True),       # windows of 2 groups stay on 8 waves
+])
+def test_one_tile_workgroups_of_up_to_16_waves(bits, T, K, N, ln):
+    case = synth.random_case(9700 + bits + T + K // 64 + N, T, K, N, bits, x_dtype=synth.BF16, ln=ln)
+    assert _s8_launches(lambda: run_linear_case(case, y_dtypes=(synth.BF16,))) == 2
+
+
+def test_gateup_shard_shape_on_16_waves():
+    """One 8-way shard of the SwiGLU projection (N = 1792 per projection): 224 tiles, one per
+    workgroup, windows of 4 groups over 16 waves."""
+    assert _s8_launches(lambda: run_gateup_case(synth.random_gateup(9800, 4, 4096, 1792, 4))) == 2
