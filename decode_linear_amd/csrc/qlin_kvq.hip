@@ -6,16 +6,18 @@
 //   s[h, n]   = sum_d q[h, d] K[c, n, d]          c = h / (H / KV)
 //   out[h, d] = sum_n softmax_n(s[h, .]) V[c, n, d]
 //
-// The rows are split into G blocks (flash decoding).  block_kernel, one workgroup per
-// (block, head): a wave takes 64 / L rows per step, L = (bytes of a row of codes) / 16
-// lanes per row, each lane one 16-byte slice (32 4-bit or 16 8-bit codes, inside one
-// quantization group), so the dequantization factors out of the dot product like the
-// pages' qdot pattern (s = scale sum q code + bias sum q); the row's score is an xor
-// butterfly over its L lanes, and an online softmax over the step's rows keeps a running
-// maximum, weight sum and per-slice value accumulator, summed over the row slots at the
-// end of the block.  The waves merge in
-// LDS in a fixed order into the block's unnormalized output and (max, sum).  merge_kernel
-// combines the blocks in block order.  No atomics: the result is bitwise reproducible.
+// The rows are split into G blocks (flash decoding).  block_kernel takes one workgroup per
+// (block, KV head, pair of the query heads that share it), so each cache row is read once
+// for both heads (a head count that does not pair up takes one head per workgroup).  A wave
+// takes 64 / L rows per step, L = (bytes of a row of codes) / 16 lanes per row, each lane
+// one 16-byte slice (32 4-bit or 16 8-bit codes, inside one quantization group), so the
+// dequantization factors out of the dot product like the pages' qdot pattern (s = scale
+// sum q code + bias sum q); the row's score is an xor butterfly over its L lanes, and an
+// online softmax per head over the step's rows keeps a running maximum, weight sum and
+// per-slice value accumulator (each value decoded once for both heads), summed over the
+// row slots at the end of the block.  The waves merge in LDS in a fixed order into the
+// block's unnormalized output and (max, sum) per head.  merge_kernel combines the blocks in
+// block order.  No atomics: the result is bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,27 +37,125 @@ __device__ __forceinline__ float half_to_float(uint16_t b, int dtype) {
   if (dtype == 1) return (float)__builtin_bit_cast(_Float16, b);
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
-__device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// Cross-lane combines without LDS: v op v[lane ^ 2^B], the same value on both lanes of each
+// pair.  Bits 0 and 1 are DPP quad permutes, bit 2 two row shifts and a select, bit 3 a row
+// rotation by 8, bits 4 and 5 the gfx950 row swaps (v_permlane16_swap pairs rows 0-1 and
+// 2-3, v_permlane32_swap the two halves; each returns both rows of a pair, so op over the two
+// results combines the pair).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int B, bool MAX> __device__ __forceinline__ float xcomb(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (B == 0) return op(v, dpp_f<0xB1>(v));                 // quad_perm [1, 0, 3, 2]
+  else if constexpr (B == 1) return op(v, dpp_f<0x4E>(v));            // quad_perm [2, 3, 0, 1]
+  else if constexpr (B == 2) {
+    const float dn = dpp_f<0x114>(v), up = dpp_f<0x104>(v);           // row_shr:4, row_shl:4
+    return op(v, (threadIdx.x & 4) ? dn : up);
+  } else if constexpr (B == 3) return op(v, dpp_f<0x128>(v));         // row_ror:8
+  else if constexpr (B == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return op(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return op(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+  }
+}
+// op over the lanes that differ from this one only in bits [LO, HI) of the lane index, in a
+// fixed order (bit LO first); every such lane ends with the same value.
+template <int LO, int HI, bool MAX> __device__ __forceinline__ float lane_reduce(float v) {
+  if constexpr (LO < HI) return lane_reduce<LO + 1, HI, MAX>(xcomb<LO, MAX>(v));
+  else return v;
+}
+constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+
+// The four bytes of w as floats, f[0], f[stride], f[2 stride], f[3 stride] (v_cvt_f32_ubyteN
+// converts byte N directly; the compiler otherwise extracts a narrower field first).
+__device__ __forceinline__ void bytes_to_float(uint32_t w, float* f, int stride) {
+  float b0, b1, b2, b3;
+  asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(b0) : "v"(w));
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(b1) : "v"(w));
+  asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(b2) : "v"(w));
+  asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(b3) : "v"(w));
+  f[0] = b0;
+  f[stride] = b1;
+  f[2 * stride] = b2;
+  f[3 * stride] = b3;
 }
 
-template <int BITS, int D>
+// One level of a reduce-scatter over lane bit B: u holds N values; afterwards the first N / 2
+// hold the sums (this lane + the lane across bit B) of elements [0, N/2) on lanes whose bit B
+// is 0 and of elements [N/2, N) on lanes whose bit B is 1.  Bits 4 and 5 use the row swaps,
+// which hand each lane exactly the pair it needs; bits 0-3 select the half the partner keeps
+// and fetch the partner's selection with a DPP move.
+template <int B, int N> __device__ __forceinline__ void scatter_level(float* u) {
+  constexpr int H = N / 2;
+  if constexpr (B >= 4) {
+#pragma unroll
+    for (int e = 0; e < H; ++e) {
+      const int lo = __builtin_bit_cast(int, u[e]), hi = __builtin_bit_cast(int, u[e + H]);
+      const auto r = B == 5 ? __builtin_amdgcn_permlane32_swap(lo, hi, false, false)
+                            : __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+      u[e] = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+    }
+  } else {
+    const bool up = (threadIdx.x >> B) & 1;
+#pragma unroll
+    for (int e = 0; e < H; ++e) {
+      const float keep = up ? u[e + H] : u[e], give = up ? u[e] : u[e + H];
+      float other;
+      if constexpr (B == 0) other = dpp_f<0xB1>(give);
+      else if constexpr (B == 1) other = dpp_f<0x4E>(give);
+      else if constexpr (B == 2) {
+        const float dn = dpp_f<0x114>(give), upv = dpp_f<0x104>(give);
+        other = up ? dn : upv;
+      } else other = dpp_f<0x128>(give);
+      u[e] = keep + other;
+    }
+  }
+}
+// Reduce-scatter of N values over lane bits [LO, 6), highest bit first: the lane keeps
+// N >> (6 - LO) sums; its k-th is element k + scatter_base<LO>(lane) of the original N.
+template <int LO, int N> __device__ __forceinline__ void reduce_scatter(float* u) {
+  if constexpr (LO < 6) {
+    if constexpr (6 - 1 >= LO) scatter_level<5, N>(u);
+    if constexpr (LO <= 4) scatter_level<4, N / 2>(u);
+    if constexpr (LO <= 3) scatter_level<3, N / 4>(u);
+    if constexpr (LO <= 2) scatter_level<2, N / 8>(u);
+    if constexpr (LO <= 1) scatter_level<1, N / 16>(u);
+    if constexpr (LO <= 0) scatter_level<0, N / 32>(u);
+  }
+}
+template <int LO, int N> __device__ __forceinline__ int scatter_base(int lane) {
+  int base = 0, n = N;
+#pragma unroll
+  for (int b = 5; b >= LO; --b) {
+    n /= 2;
+    if ((lane >> b) & 1) base += n;
+  }
+  return base;
+}
+
+// One workgroup per (block g, KV head c, chunk z of QC query heads sharing c): the block's
+// rows of c are read once for all QC heads (each key slice's dot product is taken against
+// every head's query, and each value is decoded once and added to every head's accumulator).
+template <int BITS, int D, int QC>
 __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
+  constexpr int P = 4;                  // steps whose rows are in flight at once
   constexpr int RB = D * BITS / 8;      // bytes of a row of codes
   constexpr int LPR = RB / 16;          // lanes per row: each takes 16 bytes
+  constexpr int LB = log2i(LPR);        // lane-index bits of the slice (the rest: the row slot)
   constexpr int R = 64 / LPR;           // rows a wave takes per step
   constexpr int EL = 128 / BITS;        // elements per lane (inside one quantization group)
   constexpr int E = D / 64;             // elements per lane in the merge
   constexpr uint32_t mask = (1u << BITS) - 1u;
-  static_assert(LPR >= 2 && LPR <= 32 && EL * LPR == D, "16-byte lane slices");
-  __shared__ float tg_max[kKvqWaves], tg_sum[kKvqWaves];
-  __shared__ float tg_o[kKvqWaves * D];
-  const int g = blockIdx.x, h = blockIdx.y;
+  static_assert(LPR >= 2 && LPR <= 32 && EL * LPR == D && (1 << LB) == LPR, "16-byte lane slices");
+  __shared__ float tg_max[QC][kKvqWaves], tg_sum[QC][kKvqWaves];
+  __shared__ float tg_o[QC][kKvqWaves * D];
+  const int g = blockIdx.x, c = blockIdx.y;
+  const int h0 = c * (a.H / a.KV) + (int)blockIdx.z * QC;   // first query head of this workgroup
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / LPR, j = lane % LPR;   // row slot, slice of the row
-  const int c = h / (a.H / a.KV);
   const int start = g * a.block, end = min(start + a.block, a.N);
   const int groups = D / a.GS, gi = (j * EL) / a.GS;
   const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
@@ -65,89 +165,171 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
   const uint16_t* vb = static_cast<const uint16_t*>(a.vb);
   const u4_t* kc = reinterpret_cast<const u4_t*>(a.kc);
   const u4_t* vc = reinterpret_cast<const u4_t*>(a.vc);
-  float qv[EL], qsum = 0.0f;
+  // this lane's EL query elements of each head: 16-byte loads when q is 16-byte aligned
+  float qv[QC][EL], qsum[QC];
+  if (a.q_vec) {
 #pragma unroll
-  for (int e = 0; e < EL; ++e) {
-    qv[e] = half_to_float(q16[(long)h * D + j * EL + e], a.q_dtype);
-    qsum += qv[e];
+    for (int i = 0; i < QC; ++i)
+#pragma unroll
+      for (int u = 0; u < EL / 8; ++u) {
+        const u4_t w = reinterpret_cast<const u4_t*>(q16 + (long)(h0 + i) * D + j * EL)[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[i][8 * u + e] = half_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, a.q_dtype);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QC; ++i)
+#pragma unroll
+      for (int e = 0; e < EL; ++e) qv[i][e] = half_to_float(q16[(long)(h0 + i) * D + j * EL + e], a.q_dtype);
   }
-  float mx = -__builtin_inff(), lsum = 0.0f, o[EL];
 #pragma unroll
-  for (int e = 0; e < EL; ++e) o[e] = 0.0f;
-  for (int n0 = start + R * wv; n0 < end; n0 += kKvqWaves * R) {
-    const int n = n0 + slot;
-    const bool live = n < end;
-    const long row = (long)c * a.N + (live ? n : end - 1);   // rows past the block: masked below
-    const u4_t kw = kc[row * LPR + j], vw = vc[row * LPR + j];
-    const float ksc = half_to_float(ks[row * groups + gi], a.sb_dtype), kbi = half_to_float(kb[row * groups + gi], a.sb_dtype);
-    const float vsc = half_to_float(vs[row * groups + gi], a.sb_dtype), vbi = half_to_float(vb[row * groups + gi], a.sb_dtype);
-    float dot = 0.0f;
+  for (int i = 0; i < QC; ++i) {
+    qsum[i] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) dot = fmaf(qv[e], (float)((kw[(e * BITS) >> 5] >> ((e * BITS) & 31)) & mask), dot);
-    float s = fmaf(ksc, dot, kbi * qsum);
+    for (int e = 0; e < EL; ++e) qsum[i] += qv[i][e];
+  }
+  // State per head: running max, weight sum, and the value accumulator split as the pages'
+  // qdot pattern splits the dequantization: o[e] = sum_n p_n vs_n code_n[e] and pvb = sum_n
+  // p_n vb_n (the slice lies in one group, so one bias per row), added together at the end.
+  float mx[QC], lsum[QC], pvb[QC], o[QC][EL];
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);   // the row's score on its LPR lanes
-    float smax = live ? s : -__builtin_inff();
+  for (int i = 0; i < QC; ++i) {
+    mx[i] = -__builtin_inff();
+    lsum[i] = 0.0f;
+    pvb[i] = 0.0f;
 #pragma unroll
-    for (int m = LPR; m < 64; m <<= 1) smax = fmaxf(smax, __shfl_xor(smax, m, 64));   // over the step's rows
-    const float mnew = fmaxf(mx, smax);
-    const float f = expf(mx - mnew), p = live ? expf(s - mnew) : 0.0f;
-    lsum = fmaf(lsum, f, j == 0 ? p : 0.0f);   // one lane per row carries its weight
-    mx = mnew;
+    for (int e = 0; e < EL; ++e) o[i][e] = 0.0f;
+  }
+  // The wave's steps run in rounds of P: the rows of P steps are in flight at once (the loads
+  // of the next round are issued as each step is done).  A round first takes the P steps'
+  // scores, then moves the running max once, then adds the P steps' values.  Every slot is
+  // computed (the last round's steps past the block read row end - 1 and are masked), so no
+  // branch separates a load from its use.
+  const int first = start + R * wv;
+  const int nsteps = first < end ? (end - first + kKvqWaves * R - 1) / (kKvqWaves * R) : 0;
+  u4_t kw[P], vw[P];
+  uint32_t sbk[P], sbv[P];   // scale | bias << 16 of the slice's group, keys and values
+  auto issue = [&](int sl, int q) __attribute__((always_inline)) {
+    const int n = first + q * (kKvqWaves * R) + slot;
+    const long row = (long)c * a.N + (n < end ? n : end - 1);
+    kw[sl] = kc[row * LPR + j];
+    vw[sl] = vc[row * LPR + j];
+    sbk[sl] = (uint32_t)ks[row * groups + gi] | ((uint32_t)kb[row * groups + gi] << 16);
+    sbv[sl] = (uint32_t)vs[row * groups + gi] | ((uint32_t)vb[row * groups + gi] << 16);
+  };
+  // the slice's EL codes as floats (4-bit: the even and odd codes of a dword spread to bytes
+  // first); each byte converts in one instruction
+  auto codes = [&](const u4_t& w, float f[EL]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      const float v = fmaf((float)((vw[(e * BITS) >> 5] >> ((e * BITS) & 31)) & mask), vsc, vbi);
-      o[e] = fmaf(o[e], f, p * v);
+    for (int d = 0; d < 4; ++d) {
+      if constexpr (BITS == 8) {
+        bytes_to_float(w[d], f + 4 * d, 1);
+      } else {
+        bytes_to_float(w[d] & 0x0F0F0F0Fu, f + 8 * d, 2);          // even codes
+        bytes_to_float((w[d] >> 4) & 0x0F0F0F0Fu, f + 8 * d + 1, 2);   // odd codes
+      }
+    }
+  };
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) issue(sl, sl);
+  for (int q0 = 0; q0 < nsteps; q0 += P) {
+    float sc[P][QC];
+    bool live[P];
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) {
+      live[sl] = first + (q0 + sl) * (kKvqWaves * R) + slot < end;
+      const float ksc = half_to_float(sbk[sl] & 0xFFFFu, a.sb_dtype), kbi = half_to_float(sbk[sl] >> 16, a.sb_dtype);
+      float kf[EL];
+      codes(kw[sl], kf);
+#pragma unroll
+      for (int i = 0; i < QC; ++i) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) dot = fmaf(qv[i][e], kf[e], dot);
+        sc[sl][i] = lane_reduce<0, LB, false>(fmaf(ksc, dot, kbi * qsum[i]));   // the row's score on its LPR lanes
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) m = fmaxf(m, live[sl] ? sc[sl][i] : -__builtin_inff());
+      const float mnew = fmaxf(mx[i], lane_reduce<LB, 6, true>(m));   // over the round's rows
+      // a round without live rows (mnew may still be -inf) leaves the state as it is
+      const float f = mnew == -__builtin_inff() ? 1.0f : expf(mx[i] - mnew);
+      mx[i] = mnew;
+      lsum[i] *= f;
+      pvb[i] *= f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) o[i][e] *= f;
+    }
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) {
+      const float vsc = half_to_float(sbv[sl] & 0xFFFFu, a.sb_dtype), vbi = half_to_float(sbv[sl] >> 16, a.sb_dtype);
+      float vf[EL];
+      codes(vw[sl], vf);
+#pragma unroll
+      for (int i = 0; i < QC; ++i) {
+        const float p = live[sl] ? expf(sc[sl][i] - mx[i]) : 0.0f;
+        lsum[i] += j == 0 ? p : 0.0f;   // one lane per row carries its weight
+        pvb[i] = fmaf(p, vbi, pvb[i]);
+        const float w = p * vsc;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) o[i][e] = fmaf(w, vf[e], o[i][e]);
+      }
+      issue(sl, q0 + sl + P);
     }
   }
-  // sum over the row slots: lanes of one slice, then the wave's weight sum
 #pragma unroll
-  for (int m = LPR; m < 64; m <<= 1)
+  for (int i = 0; i < QC; ++i)
 #pragma unroll
-    for (int e = 0; e < EL; ++e) o[e] += __shfl_xor(o[e], m, 64);
+    for (int e = 0; e < EL; ++e) o[i][e] += pvb[i];
+  // per head: sum over the row slots (lanes of one slice; a reduce-scatter leaves each lane
+  // EL >> (6 - LB) of the slice's sums), then the wave's weight sum
+  constexpr int KEEP = EL >> (6 - LB);
+  static_assert(KEEP >= 1, "at least one sum per lane");
+  const int sbase = j * EL + scatter_base<LB, EL>(lane);
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m, 64);
-  if (lane == 0) {
-    tg_max[wv] = mx;
-    tg_sum[wv] = lsum;
-  }
-  if (slot == 0) {
+  for (int i = 0; i < QC; ++i) {
+    reduce_scatter<LB, EL>(o[i]);
+    lsum[i] = lane_reduce<0, 6, false>(lsum[i]);
+    if (lane == 0) {
+      tg_max[i][wv] = mx[i];
+      tg_sum[i][wv] = lsum[i];
+    }
 #pragma unroll
-    for (int e = 0; e < EL; ++e) tg_o[wv * D + j * EL + e] = o[e];
+    for (int e = 0; e < KEEP; ++e) tg_o[i][wv * D + sbase + e] = o[i][e];
   }
   __syncthreads();
-  if (wv == 0) {
-    float M = tg_max[0];
-    for (int w = 1; w < kKvqWaves; ++w) M = fmaxf(M, tg_max[w]);
+  if (wv < QC) {   // wave i merges head h0 + i
+    const int i = wv;
+    float M = tg_max[i][0];
+    for (int w = 1; w < kKvqWaves; ++w) M = fmaxf(M, tg_max[i][w]);
     float wgt[kKvqWaves], S = 0.0f;
     for (int w = 0; w < kKvqWaves; ++w) {
-      wgt[w] = tg_max[w] == -__builtin_inff() ? 0.0f : expf(tg_max[w] - M);   // a wave without rows
-      S = fmaf(tg_sum[w], wgt[w], S);
+      wgt[w] = tg_max[i][w] == -__builtin_inff() ? 0.0f : expf(tg_max[i][w] - M);   // a wave without rows
+      S = fmaf(tg_sum[i][w], wgt[w], S);
     }
-    const long base = ((long)h * a.G + g) * D;
+    const long base = ((long)(h0 + i) * a.G + g) * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int d = lane * E + e;
       float v = 0.0f;
-      for (int w = 0; w < kKvqWaves; ++w) v = fmaf(tg_o[w * D + d], wgt[w], v);
+      for (int w = 0; w < kKvqWaves; ++w) v = fmaf(tg_o[i][w * D + d], wgt[w], v);
       a.opart[base + d] = v;
     }
     if (lane == 0) {
-      a.stats[((long)h * a.G + g) * 2 + 0] = M;
-      a.stats[((long)h * a.G + g) * 2 + 1] = S;
+      a.stats[((long)(h0 + i) * a.G + g) * 2 + 0] = M;
+      a.stats[((long)(h0 + i) * a.G + g) * 2 + 1] = S;
     }
   }
 }
 
-// A workgroup-wide reduction of one value per thread in a fixed order: an xor butterfly in
-// each wave, then the four waves' results in wave order, read by every thread.
+// A workgroup-wide reduction of one value per thread in a fixed order: a butterfly over the
+// lane bits in each wave, then the four waves' results in wave order, read by every thread.
 template <bool MAX>
 __device__ __forceinline__ float merge_reduce(float v, float* part) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o = __shfl_xor(v, m, 64);
-    v = MAX ? fmaxf(v, o) : v + o;
-  }
+  v = lane_reduce<0, 6, MAX>(v);
   __syncthreads();   // earlier readers of part are done
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -218,17 +400,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const KvqParams a)
   }
 }
 
-template <int BITS>
-hipError_t launch_block(const KvqParams& a, hipStream_t s) {
-  const dim3 grid(a.G, a.H);
+template <int BITS, int QC>
+hipError_t launch_block_qc(const KvqParams& a, hipStream_t s) {
+  const dim3 grid(a.G, a.KV, (a.H / a.KV) / QC);
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Query heads per workgroup: two where the heads sharing a KV head pair up, else one.
+template <int BITS>
+hipError_t launch_block(const KvqParams& a, hipStream_t s) {
+  return (a.H / a.KV) % 2 == 0 ? launch_block_qc<BITS, 2>(a, s) : launch_block_qc<BITS, 1>(a, s);
 }
 
 }  // namespace

@@ -99,3 +99,21 @@ def test_kvq_merge_statistics_at_256_blocks(N):
 def test_kvq_merge_past_4096_blocks():
     # past 4096 blocks (of 512 rows) the merge takes the block weights in two LDS chunks
     _run(synth.kvq_case(994, 1, 1, 4096 * 512 + 700, 64, 64, 4), out16=False)
+
+
+def test_kvq_unaligned_query_matches_aligned():
+    """A query that is only 2-byte aligned takes the element-wise load path: same result, bit
+    for bit, as the 16-byte aligned query."""
+    from decode_linear_amd import qlin_kvq_decode
+    c = synth.kvq_case(950, 8, 4, 300, 128, 64, 4)
+    q = _dev16(c.q, c.q_dtype)
+    big = torch.empty(q.numel() + 1, dtype=q.dtype, device="cuda")
+    qu = big[1:].view(q.shape)
+    qu.copy_(q)
+    assert qu.data_ptr() % 16 != 0
+    k = (torch.from_numpy(c.k[0].view(np.int32)).cuda(), _dev16(c.k[1], c.sb_dtype), _dev16(c.k[2], c.sb_dtype))
+    v = (torch.from_numpy(c.v[0].view(np.int32)).cuda(), _dev16(c.v[1], c.sb_dtype), _dev16(c.v[2], c.sb_dtype))
+    a = qlin_kvq_decode(q, k, v, c.KV, c.GS, c.bits, out_dtype=torch.float32)
+    b = qlin_kvq_decode(qu, k, v, c.KV, c.GS, c.bits, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
