@@ -447,6 +447,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   // group kq reads them (image row 3 rho + v: v = 0 top bytes, 1 middle, 2 low; 8-bit
   // k = 16 kq + b, 4-bit k = {0, 32, 16, 48}[kq] + 8 (b >> 3) + 2 (b & 3) + ((b >> 2) & 1)).
   // Then the chunk's fragments into slots [base, base + CG), and their group sums of X.
+  // With LayerNorm and several MFMA blocks, pass 1 keeps its values for pass 2 (registers
+  // are free there, and recomputing the shifted, gamma-scaled values is most of the staging).
+  constexpr bool KEEP = LN && MT >= 2;
+  float kept[KEEP ? C::NPX : 1][8];
   auto stage = [&](int ch, int base) __attribute__((always_inline)) {
     uint32_t rmx[C::NPX];
 #pragma unroll
@@ -457,6 +461,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
       if constexpr (LN) {
         float a[8], dsh[8];
         values(u, a, dsh);
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kept[u][e] = a[e];
+        }
         m = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = max(m, __builtin_bit_cast(uint32_t, a[e]) & 0x7FFFFFFFu);
@@ -498,7 +506,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
       const int p = lane + 64 * u, rho = p / C::W8, kp = p % C::W8;
       const int gg = kp >> 3, pp = kp & 7;
       float a[8], dsh[8];
-      values(u, a, dsh);
+      if constexpr (KEEP) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = kept[u][e];
+      } else {
+        values(u, a, dsh);
+      }
       const int ex = 16 + row_exp(rmx[u]);
       int X[8];
 #pragma unroll
