@@ -61,6 +61,12 @@ def _args():
     ap.add_argument("--only-main", action="store_true", help="time only the headline workload")
     ap.add_argument("--only", default="", help="comma-separated labels of the secondary workloads to time "
                     "(swiglu-shard8, linear-config-1..3, chain, mlp, attend, sample, kvq); default all")
+    ap.add_argument("--path", type=int, default=0, choices=(0, 1, 2),
+                    help="kernel family for the quantized calls (qlin_set_path): 0 the library's choice, "
+                    "1 the general kernel, 2 the vector-ALU kernel where it applies (for A/B runs)")
+    ap.add_argument("--path-ab", action="store_true",
+                    help="instead: time the SwiGLU (4-bit, K=4096, N=14336) and LN+GELU (8-bit, K=2048, "
+                    "N=8192) calls at T = 1..4 on each kernel family (qlin_set_path 0, 2, 1) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="instead: run a plain device copy of this many bytes (counter calibration) and exit")
@@ -442,6 +448,50 @@ def cpu_baseline(target_s):
             "us_per_call_full_workload_est_1_thread": round(w1 / c1 * (14336 / Ns) * 1e6, 1)}
 
 
+def path_ab(steps, warmup):
+    """The kernel-family A/B: the SwiGLU projection (4-bit, K=4096, N=14336 per projection) and
+    the LN + GELU linear (8-bit, K=2048, N=8192) at T = 1..4 rows, each timed on the int8
+    matrix-core kernel (path 0), the vector-ALU kernel (path 2) and the general kernel (path
+    1), cold (weights rotated over >= 1 GiB), median over graph replays.  The dispatch
+    counters confirm which family ran."""
+    import synth
+    from decode_linear_amd import qlin_dispatch_count, qlin_gateup_swiglu, qlin_linear, qlin_set_path
+    torch = _torch()
+    c4 = synth.workload(4)
+    g0, u0 = _pack(c4.gate, 4), _pack(c4.up, 4)
+    n4 = max(2, -(-ROTATE_BYTES // (g0.nbytes + u0.nbytes)))
+    w4 = [(g0, u0)] + [(_clone_q(g0), _clone_q(u0)) for _ in range(n4 - 1)]
+    c2 = synth.workload(2)
+    q2 = _pack(c2.w_f32, 8)
+    n2 = max(2, -(-ROTATE_BYTES // q2.nbytes))
+    w2 = [q2] + [_clone_q(q2) for _ in range(n2 - 1)]
+    ln2 = (_dev(c2.gamma, c2.x_dtype), _dev(c2.beta, c2.x_dtype), c2.eps)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    rows = []
+    for T in (1, 2, 3, 4):
+        x4 = torch.randn((T, c4.K), device="cuda", generator=gen).to(torch.bfloat16)
+        y4 = torch.empty((T, c4.N), dtype=torch.bfloat16, device="cuda")
+        x2 = (torch.randn((T, c2.K), device="cuda", generator=gen) + 3.0).to(torch.bfloat16)
+        y2 = torch.empty((T, c2.N), dtype=torch.bfloat16, device="cuda")
+        for path in (0, 2, 1):
+            prev = qlin_set_path(path)
+            try:
+                before = [qlin_dispatch_count(i) for i in (0, 1, 8, 9)]
+                ms = _time_graph(lambda i: qlin_gateup_swiglu(x4, w4[i][0], w4[i][1], out=y4), n4, steps, warmup,
+                                 replays=5)
+                swiglu = float(np.median(ms)) * 1e3 / steps
+                ms = _time_graph(lambda i: qlin_linear(x2, w2[i], ln=ln2, act=1, out=y2), n2, steps, warmup, replays=5)
+                lngelu = float(np.median(ms)) * 1e3 / steps
+                after = [qlin_dispatch_count(i) for i in (0, 1, 8, 9)]
+            finally:
+                qlin_set_path(prev)
+            calls = after[0] + after[1] - before[0] - before[1]
+            fam = ("int8-mfma" if after[2] - before[2] == calls else "valu" if after[3] - before[3] == calls
+                   else "general" if after[2] == before[2] and after[3] == before[3] else "mixed")
+            rows.append(dict(T=T, path=path, family=fam, swiglu_us=round(swiglu, 3), ln_gelu_us=round(lngelu, 3)))
+    print(json.dumps({"path_ab": rows, "swiglu": c4.name, "ln_gelu": c2.name, "steps": steps}))
+
+
 def copy_probe(nbytes):
     torch = _torch()
     a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
@@ -482,6 +532,12 @@ def main():
     if a.copy_probe:
         copy_probe(a.copy_probe)
         return
+    if a.path_ab:
+        path_ab(a.steps, a.warmup)
+        return
+    if a.path:
+        from decode_linear_amd import qlin_set_path
+        qlin_set_path(a.path)
     main_r = bench_swiglu(a.steps, a.warmup)
     ceil_r = read_ceiling(main_r["weight_bytes"], a.steps, a.warmup)
     extra = {}
@@ -520,6 +576,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        "kernel_path": a.path,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": main_r["name"], "rows": main_r["T"], "K": main_r["K"], "N_per_projection": main_r["N"],

@@ -12,7 +12,7 @@
 
 namespace {
 
-std::atomic<int64_t> g_dispatch[9];
+std::atomic<int64_t> g_dispatch[10];
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // keeps every in-kernel row offset within int range
 constexpr int64_t kMaxN = int64_t(1) << 28;
@@ -168,12 +168,56 @@ bool try_s8(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const q
   return true;
 }
 
+// The vector-ALU kernel (qlin_valu.h) for 4- and 8-bit codes and T <= 4, when selected.
+// Returns false when it does not take the call.
+bool try_valu(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up, const qlin_ln* ln,
+              int act, const void* res, const void* add, void* y, int y_dtype, hipStream_t stream, hipError_t* err) {
+  using namespace qlin;
+  if (g_path.load(std::memory_order_relaxed) != 2) return false;
+  if ((w->bits != 4 && w->bits != 8) || T > 4 || (up && ln)) return false;
+  const int tt = T == 1 ? 1 : (T == 2 ? 2 : 4);
+  const int K = (int)w->K;
+  int lpr = 0, waves = 0;
+  for (int l : {16, 32}) {
+    const int maxw = (l == 16 && !ln) ? 16 : 8;
+    const int wv = (K + 16 * l - 1) / (16 * l);
+    if (wv <= maxw && !(l == 32 && ln && tt == 4)) { lpr = l; waves = wv; break; }
+  }
+  if (lpr == 0) return false;
+  const int ntiles = (int)(up ? (w->N + 7) / 8 : (w->N + 15) / 16);
+  int tpw = (ntiles + cu_count() - 1) / cu_count();
+  if (tpw > 8) tpw = 8;
+  S8Launch a{};
+  a.x = x;
+  a.w0 = w->data; a.s0 = w->scales; a.b0 = w->biases;
+  if (up) { a.p1 = up->data; a.p2 = up->scales; a.p3 = up->biases; }
+  else if (ln) { a.p1 = ln->gamma; a.p2 = ln->beta; a.p3 = nullptr; }
+  a.K = K; a.T = T; a.N = (int)w->N; a.x_bf16 = x_dtype == QLIN_BF16 ? 1 : 0;
+  a.gateup = up ? 1 : 0; a.ln = ln ? 1 : 0; a.bits = w->bits;
+  a.y = y; a.res = res; a.add = add; a.eps = ln ? ln->eps : 0.0f; a.y_dtype = y_dtype; a.act = act;
+  a.MT = tt; a.GWM = lpr; a.waves = waves;
+  a.grid = (ntiles + tpw - 1) / tpw;
+  a.D = (ntiles + a.grid - 1) / a.grid;
+  if (a.grid > 0xFFFF) return false;
+  for (const void* q : {a.x, a.w0, a.s0, a.b0, a.p1, a.p2, a.p3}) {
+    if ((reinterpret_cast<uintptr_t>(q) >> s8::kTagShift) != 0) return false;
+  }
+  *err = w->bits == 4 ? launch_valu_q4(a, stream) : launch_valu_q8(a, stream);
+  return true;
+}
+
 qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const qlin_weight* up,
                    const qlin_ln* ln, int act, const void* res, const void* add, void* y, int y_dtype,
                    hipStream_t stream) {
   using namespace qlin;
   {
     hipError_t e = hipSuccess;
+    if (try_valu(x, x_dtype, T, w, up, ln, act, res, add, y, y_dtype, stream, &e)) {
+      if (e != hipSuccess) return QLIN_ERR_HIP;
+      g_dispatch[up ? 1 : 0].fetch_add(1, std::memory_order_relaxed);
+      g_dispatch[9].fetch_add(1, std::memory_order_relaxed);
+      return QLIN_OK;
+    }
     if (try_s8(x, x_dtype, T, w, up, ln, act, res, add, y, y_dtype, stream, &e)) {
       if (e != hipSuccess) return QLIN_ERR_HIP;
       g_dispatch[up ? 1 : 0].fetch_add(1, std::memory_order_relaxed);
@@ -584,12 +628,12 @@ qlin_status qlin_kvq_decode_noalloc(const void* q, qlin_dtype q_dtype, int32_t h
 }
 
 int32_t qlin_set_path(int32_t path) {
-  if (path != 0 && path != 1) return -1;
+  if (path < 0 || path > 2) return -1;
   return g_path.exchange(path, std::memory_order_relaxed);
 }
 
 int64_t qlin_dispatch_count(int32_t which) {
-  if (which < 0 || which > 8) return -1;
+  if (which < 0 || which > 9) return -1;
   return g_dispatch[which].load(std::memory_order_relaxed);
 }
 

@@ -325,16 +325,19 @@ qlin_status qlin_stream_read_config(const void* buf, int64_t bytes, uint32_t* pa
  * 0 = linear, 1 = gate/up, 2 = pack, 3 = unpack, 4 = attend, 5 = stream read, 6 = sample,
  * 7 = quantized-KV decode (a test can assert a kernel ran; qlin_mlp counts one gate/up and
  * one linear); 8 = how many of the linear and gate/up launches ran on the int8 streaming
- * kernel rather than the general one.  -1 for any other index. */
+ * kernel, 9 = how many on the vector-ALU kernel (the rest ran on the general kernel).  -1
+ * for any other index. */
 int64_t qlin_dispatch_count(int32_t which);
 
 /* Selects the kernel family for 4- and 8-bit qlin_linear / qlin_gateup_swiglu / qlin_mlp
  * calls made after it, process-wide: 0 (the default) lets the library pick the int8 streaming
  * kernel wherever its shape rules admit the call and the general kernel elsewhere; 1 sends
- * every call to the general kernel.  Both compute the same operation to the same tolerance;
- * this exists so that tests and measurements can exercise each one.  Returns the previous
- * setting, or -1 (and changes nothing) for any other value.  Not synchronized with calls
- * in flight on other host threads. */
+ * every call to the general kernel; 2 sends calls of at most 4 activation rows to the
+ * vector-ALU kernel where its shape rules admit them (K up to 4096, or 2048 with LayerNorm
+ * and 3-4 rows; no LayerNorm with gate/up), the rest as 0.  All compute the same operation to
+ * the same tolerance; this exists so that tests and measurements can exercise each one.
+ * Returns the previous setting, or -1 (and changes nothing) for any other value.  Not
+ * synchronized with calls in flight on other host threads. */
 int32_t qlin_set_path(int32_t path);
 
 /* Static description of a status code. */

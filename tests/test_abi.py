@@ -165,9 +165,9 @@ def test_chain_argument_errors(q):
 
 
 def test_dispatch_counter_range(q):
-    assert q.qlin_dispatch_count(9) == -1
+    assert q.qlin_dispatch_count(10) == -1
     assert q.qlin_dispatch_count(-1) == -1
-    assert q.qlin_dispatch_count(8) >= 0
+    assert q.qlin_dispatch_count(8) >= 0 and q.qlin_dispatch_count(9) >= 0
     assert q.qlin_dispatch_count(0) >= 0
     assert q.qlin_dispatch_count(7) >= 0
 
@@ -245,9 +245,10 @@ def test_stream_read_config_validation(q):
 
 def test_set_path_validation(q):
     f = q.lib().qlin_set_path
-    assert f(5) == -1 and f(-1) == -1
-    prev = f(1)
-    assert prev in (0, 1)
+    assert f(3) == -1 and f(5) == -1 and f(-1) == -1
+    prev = f(2)
+    assert prev in (0, 1, 2)
+    assert f(1) == 2
     assert f(prev) == 1
 
 

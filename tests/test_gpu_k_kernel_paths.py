@@ -115,3 +115,76 @@ def test_gateup_shard_shape_on_16_waves():
     """One 8-way shard of the SwiGLU projection (N = 1792 per projection): 224 tiles, one per
     workgroup, windows of 4 groups over 16 waves."""
     assert _s8_launches(lambda: run_gateup_case(synth.random_gateup(9800, 4, 4096, 1792, 4))) == 2
+
+
+# ---- the vector-ALU kernel (qlin_set_path(2)): T <= 4 -----------------------------------------
+
+@pytest.fixture
+def valu_path():
+    from decode_linear_amd import qlin_dispatch_count, qlin_set_path
+    prev = qlin_set_path(2)
+    before = qlin_dispatch_count(9)
+    yield lambda: qlin_dispatch_count(9) - before
+    assert qlin_set_path(prev) == 2
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("ln", [False, True])
+def test_valu_rows(valu_path, bits, T, ln):
+    case = synth.random_case(9900 + 10 * T + bits + ln, T, 1024, 72, bits, x_dtype=synth.BF16, ln=ln,
+                             x_mean=3.0 if ln else 0.0)
+    run_linear_case(case, y_dtypes=(synth.BF16,))
+    assert valu_path() == 2
+
+
+@pytest.mark.parametrize("bits,T,K,N,ln", [(4, 4, 64, 17, False), (8, 3, 192, 40, True), (4, 2, 320, 33, False),
+                                           (8, 4, 2048, 100, True), (4, 4, 4096, 48, False), (8, 1, 4096, 20, True),
+                                           (4, 2, 4096, 24, True), (8, 4, 4032, 16, False)])
+def test_valu_k_and_n(valu_path, bits, T, K, N, ln):
+    case = synth.random_case(9950 + K + N + bits, T, K, N, bits, x_dtype=synth.F16 if K % 128 else synth.BF16,
+                             ln=ln, act=1)
+    run_linear_case(case, y_dtypes=(case.x_dtype,))
+    assert valu_path() == 2
+
+
+@pytest.mark.parametrize("act,res,add", [(1, True, True), (0, True, False)])
+def test_valu_epilogues(valu_path, act, res, add):
+    case = synth.random_case(9970 + act + 2 * res, 4, 1024, 64, 8, x_dtype=synth.BF16, act=act, res=res, add=add)
+    run_linear_case(case, y_dtypes=(synth.BF16,))
+    assert valu_path() == 2
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_valu_gateup(valu_path, T):
+    run_gateup_case(synth.random_gateup(9980 + T, T, 1024, 72, 4))
+    run_gateup_case(synth.random_gateup(9990 + T, T, 512, 24, 8))
+    assert valu_path() == 4
+
+
+def test_valu_falls_back_outside_its_shapes(valu_path):
+    # K past 4096, and LayerNorm with gate/up, go to the other kernels
+    run_linear_case(synth.random_case(9995, 2, 8192, 32, 4, x_dtype=synth.BF16))
+    run_gateup_case(synth.random_gateup(9996, 4, 512, 24, 4, ln=True))
+    assert valu_path() == 0
+
+
+def test_valu_full_size_workloads(valu_path):
+    """The LN + GELU workload (T=4, K=2048, N=8192, 8-bit) and the SwiGLU projection (T=4,
+    K=4096, N=14336 per projection, 4-bit) on the vector-ALU kernel."""
+    run_linear_case(synth.workload(2))
+    run_gateup_case(synth.workload(4))
+    assert valu_path() == 4
+
+
+def test_valu_deterministic(valu_path):
+    from decode_linear_amd import qlin_linear
+    from helpers import Packed, dev_bits
+    case = synth.random_case(9997, 4, 2048, 256, 4, x_dtype=synth.BF16, ln=True)
+    W = Packed(case.w_f32, 4)
+    x = dev_bits(case.x, case.x_dtype)
+    ln = (dev_bits(case.gamma, case.x_dtype), dev_bits(case.beta, case.x_dtype), case.eps)
+    a = qlin_linear(x, W.q, ln=ln, out_dtype=torch.float32)
+    b = qlin_linear(x, W.q, ln=ln, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
