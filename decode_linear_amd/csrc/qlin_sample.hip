@@ -1,22 +1,25 @@
-// sample for gfx950: one sampling step of the depth decoder ([p1] maya-mac
-// src/maya_mac/mlx_kernels.py, `_SAMPLE` and `sample()`).
+// One sampling step of the depth decoder for gfx950 ([p1] maya-mac src/maya_mac/mlx_kernels.py,
+// the sampling kernel and `sample()`): keep the top_k largest logits (every logit equal to the
+// top_k-th stays), pick one of them by Gumbel-max, and append the picked code's embedding row.
 //
-//   key(f)  = order-preserving 32-bit key of the fp32 logit f (bits u; ~u when negative,
-//             u | 2^31 otherwise), so larger logits have larger keys and -0 < +0
-//   kth     = the top_k-th largest key, found exactly by a radix select (4 passes of 8 bits)
-//   code    = argmax over the codes with key >= kth (ties with the k-th all kept) of
-//             fl32(fl32(f * inv_temp) + gumbel), the smaller index on equal scores; a NaN
-//             score never wins, and no number among the kept scores gives -1
-//   out     = the prefix rows, then (with a table) the table row of the code (zeros for -1)
+//   rank(f)   order-preserving 32-bit image of the fp32 logit f (larger logit, larger rank;
+//             -0 ranks below +0): the bits of f with the sign flipped, all bits flipped for
+//             negative f
+//   theta     the top_k-th largest rank: exact, by a most-significant-digit-first radix
+//             select over 8-bit digits
+//   code      among the codes with rank >= theta, the one with the largest score
+//             fl32(fl32(f * inv_temp) + gumbel), the smaller index among equal scores (+0
+//             and -0 are equal); NaN scores never win; -1 when no kept score is a number
+//   out       the prefix rows, then (with a table) the code's row of the table (zeros for -1)
 //
-// Mapping: one workgroup of 256 threads (4 waves); thread t holds the keys of codes
-// t, t + 256, ... in registers (n <= 8192).  A radix pass counts digits of the keys that
-// still match the selected prefix into a 256-bin LDS histogram (integer LDS atomics: the
-// counts do not depend on their order), and wave 0 scans the bins from the top with a lane
-// prefix sum to find the digit that holds the need-th largest key.  The argmax is a
-// per-thread scan, an xor butterfly over each wave (a total order on (score, index)) and a
-// fixed-order pass over the four waves.  The rows are copied with 16-byte accesses, the
-// prefix first of all (it does not depend on the code).
+// Mapping: one workgroup of 256 threads; thread t keeps the ranks of codes t, t + 256, ... in
+// registers (n <= 8192).  Radix pass: each wave counts the digits of its matching ranks into
+// its own 256-bin LDS histogram (LDS integer atomics, private to the wave), then all 256
+// threads take one digit each, highest digit first, add the four waves' counts and run one
+// prefix sum over the workgroup; the thread whose digit holds the wanted rank publishes it.
+// Gumbel-max: every candidate becomes one 64-bit word, (rank of the score) << 32 | ~index, so
+// the winner is the plain maximum of the words (an exact, order-free reduction: the result
+// does not depend on the order of the combines).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,165 +29,161 @@ namespace qlin {
 namespace {
 
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-constexpr int kSampleThreads = 256;
-constexpr int kSamplePerThread = kSampleMaxCodes / kSampleThreads;
+constexpr int kThr = 256;                     // threads of the workgroup
+constexpr int kWv = kThr / 64;                // its waves
+constexpr int kPer = kSampleMaxCodes / kThr;  // ranks per thread
 
-__device__ __forceinline__ uint32_t order_key(float f) {
+__device__ __forceinline__ uint32_t rank_of(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (u >> 31) ? ~u : (u ^ 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+__device__ __forceinline__ float logit_of(uint32_t r) {
+  return __builtin_bit_cast(float, (r >> 31) ? (r ^ 0x80000000u) : ~r);
 }
-__device__ __forceinline__ float logit_at(const SampleParams& a, int i) {
+__device__ __forceinline__ float read_logit(const SampleParams& a, int i) {
   if (a.logit_dtype == 0) return static_cast<const float*>(a.logits)[i];
-  const uint16_t b = static_cast<const uint16_t*>(a.logits)[i];
-  if (a.logit_dtype == 1) return (float)__builtin_bit_cast(_Float16, b);
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
+  const uint32_t h = static_cast<const uint16_t*>(a.logits)[i];
+  return a.logit_dtype == 1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h) : __builtin_bit_cast(float, h << 16);
 }
-// (s, i) beats (bs, bi): a larger score, or an equal score at a smaller index.  Scores are
-// never NaN on the winning side (a NaN compares false both ways and is never taken).
-__device__ __forceinline__ bool beats(float s, uint32_t i, float bs, uint32_t bi) {
-  return s > bs || (s == bs && i < bi);
+// Candidate word of code i with score s: 0 (never wins) for a NaN score; otherwise the rank of
+// s (with -0 taken as +0) above the complement of i, so that a larger score, then a smaller
+// index, gives a larger word.
+__device__ __forceinline__ uint64_t candidate(float s, uint32_t i) {
+  if (s != s) return 0ull;
+  const uint32_t r = rank_of(s == 0.0f ? 0.0f : s);
+  return ((uint64_t)r << 32) | (uint64_t)(~i);
 }
 
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const SampleParams a) {
+// Inclusive prefix sum over the 64 lanes (lane l: sum of lanes 0..l).
+__device__ __forceinline__ uint32_t wave_prefix(uint32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)v, d, 64);
+    v += lane >= d ? o : 0u;
+  }
+  return v;
+}
+// Maximum of a 64-bit word over the wave (every lane ends with it).
+__device__ __forceinline__ uint64_t wave_max64(uint64_t w) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(w >> 32), d, 64);
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)w, d, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    w = o > w ? o : w;
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
 #pragma clang fp contract(off)
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_need;
-  __shared__ float best_s[kSampleThreads / 64];
-  __shared__ uint32_t best_i[kSampleThreads / 64];
-  __shared__ int32_t sh_code;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ uint32_t counts[kWv][256];   // one digit histogram per wave
+  __shared__ uint32_t wave_total[kWv];
+  __shared__ uint32_t sel_digits, sel_left;   // the selected high digits, and ranks still wanted
+  __shared__ uint64_t wave_best[kWv];
+  __shared__ int32_t picked;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int n = a.n;
-  // the prefix rows do not depend on the code: they are copied first, their loads in
-  // flight together, while the keys load and the selection runs
-  const long W = (long)a.D * a.es / 16;   // 16-byte pieces per row
+  const long pieces = (long)a.D * a.es / 16;   // 16-byte pieces of one row
   u4_t* out = static_cast<u4_t*>(a.out);
+
+  // The prefix rows do not depend on the code: their copy goes out first, eight pieces in
+  // flight per thread, under the selection.
   if (a.copy_prefix) {
-    const u4_t* pre = static_cast<const u4_t*>(a.prefix);
-    const long total = (long)a.n_prev * W;
-    long v = tid;
-    for (; v + 7 * kSampleThreads < total; v += 8 * kSampleThreads) {
-      u4_t t[8];
+    const u4_t* src = static_cast<const u4_t*>(a.prefix);
+    const long total = (long)a.n_prev * pieces;
+    long p = t;
+    for (; p + 7L * kThr < total; p += 8L * kThr) {
+      u4_t buf[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = pre[v + u * kSampleThreads];
+      for (int u = 0; u < 8; ++u) buf[u] = src[p + (long)u * kThr];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) out[v + u * kSampleThreads] = t[u];
+      for (int u = 0; u < 8; ++u) out[p + (long)u * kThr] = buf[u];
     }
-    for (; v < total; v += kSampleThreads) out[v] = pre[v];
+    for (; p < total; p += kThr) out[p] = src[p];
   }
 
-  uint32_t key[kSamplePerThread];
+  uint32_t rk[kPer];
 #pragma unroll
-  for (int e = 0; e < kSamplePerThread; ++e) {
-    const int i = tid + kSampleThreads * e;
-    key[e] = i < n ? order_key(logit_at(a, i)) : 0u;
+  for (int e = 0; e < kPer; ++e) {
+    const int i = t + kThr * e;
+    rk[e] = i < n ? rank_of(read_logit(a, i)) : 0u;
   }
-  if (tid == 0) {
-    sh_prefix = 0u;
-    sh_need = (uint32_t)a.top_k;
-  }
-  // radix select of the top_k-th largest key, 8 bits per pass from the top
+
+  // ---- theta: four 8-bit digits, most significant first ----------------------------------
+  uint32_t digits = 0u, left = (uint32_t)a.top_k;   // chosen so far (uniform), ranks wanted
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0u;   // 256 threads, 256 bins
-    __syncthreads();  // also publishes sh_prefix / sh_need of the previous pass
-    const uint32_t prefix = sh_prefix;
+    const int sh = 24 - 8 * pass;
 #pragma unroll
-    for (int e = 0; e < kSamplePerThread; ++e) {
-      const int i = tid + kSampleThreads * e;
-      const bool match = pass == 0 ? true : (key[e] >> (shift + 8)) == prefix;
-      if (i < n && match) atomicAdd(&hist[(key[e] >> shift) & 0xFFu], 1u);
+    for (int w = 0; w < kWv; ++w) counts[w][t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = t + kThr * e;
+      const bool on_path = pass == 0 || (rk[e] >> (sh + 8)) == digits;
+      if (i < n && on_path) atomicAdd(&counts[wv][(rk[e] >> sh) & 0xFFu], 1u);
     }
     __syncthreads();
-    if (wv == 0) {
-      // lane l holds bins 255 - 4l .. 252 - 4l, in descending order
-      uint32_t c[4], tot = 0u;
+    // thread t owns digit 255 - t: how many matching ranks carry it, and how many carry a
+    // higher digit (a prefix sum over the threads in order)
+    const uint32_t dgt = 255u - (uint32_t)t;
+    uint32_t mine = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - (4 * lane + j)];
-        tot += c[j];
-      }
-      uint32_t incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
-        if (lane >= off) incl += t;
-      }
-      const uint32_t before = incl - tot, need = sh_need;
-      if (before < need && need <= before + tot) {   // exactly one lane: need <= the candidates
-        uint32_t run = before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (need <= run + c[j]) {
-            sh_prefix = (prefix << 8) | (uint32_t)(255 - (4 * lane + j));
-            sh_need = need - run;
-            break;
-          }
-          run += c[j];
-        }
-      }
+    for (int w = 0; w < kWv; ++w) mine += counts[w][dgt];
+    const uint32_t incl = wave_prefix(mine, lane);
+    if (lane == 63) wave_total[wv] = incl;
+    __syncthreads();
+    uint32_t above = incl - mine;
+    for (int w = 0; w < wv; ++w) above += wave_total[w];
+    if (above < left && left <= above + mine) {   // exactly one thread: its digit holds the rank
+      sel_digits = (digits << 8) | dgt;
+      sel_left = left - above;
     }
     __syncthreads();
+    digits = sel_digits;
+    left = sel_left;
   }
-  const uint32_t kth = sh_prefix;
-  // Gumbel-max over the kept codes
-  float bs = -__builtin_inff();
-  uint32_t bi = 0xFFFFFFFFu;
+  const uint32_t theta = digits;
+
+  // ---- Gumbel-max over the kept codes ------------------------------------------------------
+  uint64_t best = 0ull;
 #pragma unroll
-  for (int e = 0; e < kSamplePerThread; ++e) {
-    const int i = tid + kSampleThreads * e;
-    if (i < n && key[e] >= kth) {
-      const float scaled = key_value(key[e]) * a.inv_temp;   // one fp32 rounding
-      const float s = scaled + a.gumbel[i];                  // and another (no contraction)
-      if (beats(s, (uint32_t)i, bs, bi)) {
-        bs = s;
-        bi = (uint32_t)i;
-      }
+  for (int e = 0; e < kPer; ++e) {
+    const int i = t + kThr * e;
+    if (i < n && rk[e] >= theta) {
+      const float scaled = logit_of(rk[e]) * a.inv_temp;   // one fp32 rounding
+      const float s = scaled + a.gumbel[i];                // and another (no contraction)
+      const uint64_t c = candidate(s, (uint32_t)i);
+      best = c > best ? c : best;
     }
   }
+  best = wave_max64(best);
+  if (lane == 0) wave_best[wv] = best;
+  __syncthreads();
+  if (t == 0) {
+    uint64_t b = wave_best[0];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float os = __shfl_xor(bs, m, 64);
-    const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
-    if (beats(os, oi, bs, bi)) {
-      bs = os;
-      bi = oi;
-    }
-  }
-  if (lane == 0) {
-    best_s[wv] = bs;
-    best_i[wv] = bi;
+    for (int w = 1; w < kWv; ++w) b = wave_best[w] > b ? wave_best[w] : b;
+    const int32_t code = b == 0ull ? -1 : (int32_t)(~(uint32_t)b);
+    picked = code;
+    *a.code = code;
   }
   __syncthreads();
-  if (tid == 0) {
-    float s = best_s[0];
-    uint32_t i = best_i[0];
-    for (int w = 1; w < kSampleThreads / 64; ++w)
-      if (beats(best_s[w], best_i[w], s, i)) {
-        s = best_s[w];
-        i = best_i[w];
-      }
-    const int32_t c = i == 0xFFFFFFFFu ? -1 : (int32_t)i;
-    sh_code = c;
-    *a.code = c;
-  }
-  __syncthreads();
-  // the code's table row after the prefix
+
+  // ---- the picked code's embedding row after the prefix --------------------------------------
   if (a.table) {
-    const int32_t c = sh_code;
-    const u4_t* row = static_cast<const u4_t*>(a.table) + (long)(c < 0 ? 0 : c) * W;
-    for (long v = tid; v < W; v += kSampleThreads)
-      out[(long)a.n_prev * W + v] = c < 0 ? (u4_t){0u, 0u, 0u, 0u} : row[v];
+    const int32_t code = picked;
+    const u4_t* row = static_cast<const u4_t*>(a.table) + (long)(code < 0 ? 0 : code) * pieces;
+    for (long p = t; p < pieces; p += kThr)
+      out[(long)a.n_prev * pieces + p] = code < 0 ? (u4_t){0u, 0u, 0u, 0u} : row[p];
   }
 }
 
 }  // namespace
 
 hipError_t launch_sample(const SampleParams& a, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(kSampleThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 
