@@ -174,7 +174,8 @@ bool try_valu(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const
               int act, const void* res, const void* add, void* y, int y_dtype, hipStream_t stream, hipError_t* err) {
   using namespace qlin;
   if (g_path.load(std::memory_order_relaxed) != 2) return false;
-  if ((w->bits != 4 && w->bits != 8) || T > 4 || (up && ln)) return false;
+  const bool dense16 = w->bits == 16 && w->dtype == QLIN_F16 && x_dtype == QLIN_F16;
+  if ((w->bits != 4 && w->bits != 8 && !dense16) || T > 4 || (up && ln)) return false;
   const int tt = T == 1 ? 1 : (T == 2 ? 2 : 4);
   const int K = (int)w->K;
   int lpr = 0, waves = 0;
@@ -202,7 +203,7 @@ bool try_valu(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const
   for (const void* q : {a.x, a.w0, a.s0, a.b0, a.p1, a.p2, a.p3}) {
     if ((reinterpret_cast<uintptr_t>(q) >> s8::kTagShift) != 0) return false;
   }
-  *err = w->bits == 4 ? launch_valu_q4(a, stream) : launch_valu_q8(a, stream);
+  *err = w->bits == 4 ? launch_valu_q4(a, stream) : w->bits == 8 ? launch_valu_q8(a, stream) : launch_valu_f16(a, stream);
   return true;
 }
 

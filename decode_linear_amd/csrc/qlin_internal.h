@@ -60,9 +60,10 @@ hipError_t launch_s8_q4_ln1(const S8Launch& a, hipStream_t s);
 hipError_t launch_s8_q8_ln0(const S8Launch& a, hipStream_t s);
 hipError_t launch_s8_q8_ln1(const S8Launch& a, hipStream_t s);
 // The vector-ALU streaming kernel for T <= 4 (qlin_valu.h): S8Launch with MT = activation
-// rows held (1, 2 or 4) and GWM = lanes per weight row (16, 32 or 64).
+// rows held (1, 2 or 4) and GWM = lanes per weight row (16 or 32).
 hipError_t launch_valu_q4(const S8Launch& a, hipStream_t s);
 hipError_t launch_valu_q8(const S8Launch& a, hipStream_t s);
+hipError_t launch_valu_f16(const S8Launch& a, hipStream_t s);   // dense fp16 weights and activations
 
 // Arguments of one attend launch (cache append + causal attention, <= 32 positions).
 struct AttendParams {

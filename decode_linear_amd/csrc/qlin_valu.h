@@ -1,6 +1,7 @@
 // The streaming fused linear on the vector ALUs, for a few activation rows (T <= 4): the
 // plain-FMA counterpart of the int8 matrix-core kernel (qlin_s8.h), built to measure where
-// the matrix cores pay.  Shared by qlin_valu_q4.hip and qlin_valu_q8.hip.
+// the matrix cores pay.  Shared by qlin_valu_q4.hip, qlin_valu_q8.hip and qlin_valu_f16.hip
+// (dense fp16 weights and activations: the weight pairs go to v_dot2 as they are).
 //
 // Same operation and conventions as qlin_s8.h ([p1] maya-mac `_linear_kernel`: LayerNorm
 // folded into the weight stream with statistics shifted by x[t, 0]; [p3] mlx-bun 0.0.10 ->
@@ -45,7 +46,7 @@ constexpr int log2c(int v) { return v <= 1 ? 0 : 1 + log2c(v / 2); }
 template <int BITS, bool LN, int TT, int LPR>
 struct VCfg {
   static constexpr int CPL = 16;                   // codes per lane and load
-  static constexpr int CB = CPL * BITS / 8;        // their bytes (8 or 16)
+  static constexpr int CB = CPL * BITS / 8;        // their bytes (8, 16, or 32 for dense fp16)
   static constexpr int LB = log2c(LPR);
   static constexpr int KW = LPR * CPL;             // k of one wave's window
   static constexpr int RPL = 64 / LPR;             // weight rows per load
@@ -71,10 +72,13 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask) {
   return h2_bits(bits_h2((w & mask) | 0x64006400u) - (h2_t){(_Float16)1024.0f, (_Float16)1024.0f});
 }
 
-// The slice's codes as PAIRS fp16 pairs; pair order below matches the activation pairs
-// built in staging (pair_k).
+// The slice's codes as PAIRS fp16 pairs (dense fp16 weights: the elements as they are); pair
+// order below matches the activation pairs built in staging (pair_k).
 template <int BITS> __device__ __forceinline__ void decode(const uint32_t* w, uint32_t* cp) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cp[i] = w[i];   // elements 2i, 2i+1
+  } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -89,7 +93,7 @@ template <int BITS> __device__ __forceinline__ void decode(const uint32_t* w, ui
 }
 // Slice positions of the two elements of pair i.
 template <int BITS> __device__ __forceinline__ constexpr int pair_k(int i, int h) {
-  return BITS == 4 ? 8 * (i >> 2) + (i & 3) + 4 * h : 4 * (i >> 1) + (i & 1) + 2 * h;
+  return BITS == 16 ? 2 * i + h : BITS == 4 ? 8 * (i >> 2) + (i & 3) + 4 * h : 4 * (i >> 1) + (i & 1) + 2 * h;
 }
 
 // Sum over lane bits [0, LB) in a fixed order (xor 1, 2, 4, 8, 16, 32), the same value on
@@ -172,7 +176,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, VCfg<BITS, LN, TT, LPR>
       const bool ok = kin && tile < ntiles && n < N;
       const void* wb = proj ? p1 : (const void*)w0;
       const long off = (long)n * row_bytes + (long)k0 * BITS / 8;
-      if constexpr (C::CB == 16) {
+      if constexpr (C::CB == 32) {
+        const u4_t v0 = *(ok ? gaddr<u4_t>(wb, off) : zaddr<u4_t>(0));
+        const u4_t v1 = *(ok ? gaddr<u4_t>(wb, off + 16) : zaddr<u4_t>(0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r.code[l][i] = v0[i];
+          r.code[l][4 + i] = v1[i];
+        }
+      } else if constexpr (C::CB == 16) {
         const u4_t v = *(ok ? gaddr<u4_t>(wb, off) : zaddr<u4_t>(0));
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.code[l][i] = v[i];
@@ -181,12 +193,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, VCfg<BITS, LN, TT, LPR>
         r.code[l][0] = v[0];
         r.code[l][1] = v[1];
       }
-      const void* sp = proj ? p2 : (const void*)s0;
-      const void* bp = proj ? p3 : (const void*)b0;
-      const long so = ((long)n * G + grp) * 2;
-      const uint32_t sv = *(ok ? gaddr<uint16_t>(sp, so) : zaddr<uint16_t>(0));
-      const uint32_t bv = *(ok ? gaddr<uint16_t>(bp, so) : zaddr<uint16_t>(0));
-      r.sb[l] = sv | (bv << 16);
+      if constexpr (BITS == 16) {
+        r.sb[l] = 0x3C00u;   // dense: scale 1, bias 0
+      } else {
+        const void* sp = proj ? p2 : (const void*)s0;
+        const void* bp = proj ? p3 : (const void*)b0;
+        const long so = ((long)n * G + grp) * 2;
+        const uint32_t sv = *(ok ? gaddr<uint16_t>(sp, so) : zaddr<uint16_t>(0));
+        const uint32_t bv = *(ok ? gaddr<uint16_t>(bp, so) : zaddr<uint16_t>(0));
+        r.sb[l] = sv | (bv << 16);
+      }
     }
   };
   Slot ring[2];

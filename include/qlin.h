@@ -333,8 +333,9 @@ int64_t qlin_dispatch_count(int32_t which);
  * calls made after it, process-wide: 0 (the default) lets the library pick the int8 streaming
  * kernel wherever its shape rules admit the call and the general kernel elsewhere; 1 sends
  * every call to the general kernel; 2 sends calls of at most 4 activation rows to the
- * vector-ALU kernel where its shape rules admit them (K up to 4096, or 2048 with LayerNorm
- * and 3-4 rows; no LayerNorm with gate/up), the rest as 0.  All compute the same operation to
+ * vector-ALU kernel where its shape rules admit them (4- and 8-bit codes, or dense fp16
+ * weights with fp16 activations; K up to 4096, or 2048 with LayerNorm and 3-4 rows; no
+ * LayerNorm with gate/up), the rest as 0.  All compute the same operation to
  * the same tolerance; this exists so that tests and measurements can exercise each one.
  * Returns the previous setting, or -1 (and changes nothing) for any other value.  Not
  * synchronized with calls in flight on other host threads. */

@@ -188,3 +188,16 @@ def test_valu_deterministic(valu_path):
     b = qlin_linear(x, W.q, ln=ln, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("T,K,N,ln", [(1, 1024, 1024, False), (2, 512, 72, True), (4, 4096, 40, False),
+                                      (3, 2048, 33, True), (4, 64, 17, False)])
+def test_valu_dense_fp16(valu_path, T, K, N, ln):
+    case = synth.random_case(9800 + T + K // 64 + N, T, K, N, 16, x_dtype=synth.F16, ln=ln, act=int(ln))
+    run_linear_case(case, y_dtypes=(synth.F16,))
+    assert valu_path() == 2
+
+
+def test_valu_dense_bf16_stays_off(valu_path):
+    run_linear_case(synth.random_case(9810, 2, 512, 40, 16, x_dtype=synth.BF16))
+    assert valu_path() == 0
