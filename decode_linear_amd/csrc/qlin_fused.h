@@ -1324,13 +1324,35 @@ __device__ __forceinline__ void finalize_tile3(const LinParams& p, float* part, 
   }
 }
 
-// Bounded wait until an LDS word equals v (all lanes read the same word).
-__device__ __forceinline__ void lds_wait_eq(const int* a, int v) {
+// Bounded wait until an LDS word equals v (all lanes read the same word): at most `limit`
+// polls.  Returns whether the word reached v (uniform over the wave); a wait that gives up
+// is reported by the caller (device counter, NaN outputs), never ignored.
+__device__ __forceinline__ bool lds_wait_eq(const int* a, int v, int limit) {
 #pragma nounroll
-  for (int it = 0; it < kSpinMax; ++it) {
+  for (int it = 0; it < limit; ++it) {
     const int cur = __builtin_amdgcn_readfirstlane(__hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-    if (cur == v) break;
+    if (cur == v) return true;
     __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// The outputs a finishing wave owns for block b of a tile (or, with three-term rows, the
+// whole tile), stored as NaN: its merge wait gave up, so its partial sums are not known.
+template <int MT, int NT>
+__device__ __forceinline__ void finalize_failed(const LinParams& p, int b, int tile, int lane, bool whole) {
+  const int c = lane >> 4, li = lane & 15;
+  const float nan = __builtin_nanf("");
+  for (int t0 = whole ? 0 : (16 * b + 4 * c) / NT; t0 < (whole ? p.T : (16 * b + 4 * c) / NT + 4 / NT);
+       t0 += whole ? 4 : 1) {
+    const int t = whole ? t0 + c : t0;
+    if (p.gateup) {
+      const int n = tile * 8 + li;
+      if (t < p.T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, nan);
+    } else {
+      const int n = tile * 16 + li;
+      if (t < p.T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, nan);
+    }
   }
 }
 
@@ -1478,21 +1500,31 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     // block of tile rot this wave finishes (none when >= nfin)
     auto my_block = [&](int rot) __attribute__((always_inline)) { return (wv - rot) & 7; };
     // Put this wave's partials of tile rot into its buffer once the buffer is open for it.
+    // A put whose wait gives up writes nothing and does not count itself in: the tile's
+    // finishing waves then give up too and store NaN (each give-up counts in p.timeouts).
     auto put = [&](const f4_t acc[MT], int rot) __attribute__((always_inline)) {
       const int q = rot & (NB - 1);
-      lds_wait_eq(pgen + q, rot);
-      write_partials(acc, 0, red + q * kWaves * MT * 256);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the writes are done
-      if (lane == 0) __hip_atomic_fetch_add(pcnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lds_wait_eq(pgen + q, rot, p.spin)) {
+        write_partials(acc, 0, red + q * kWaves * MT * 256);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the writes are done
+        if (lane == 0) __hip_atomic_fetch_add(pcnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else if (lane == 0) {
+        atomicAdd(p.timeouts, 1u);
+      }
     };
     // Finish tile `tl` (index rot) if this wave owns one of its blocks.
     auto finish_tile = [&](int tl, int rot, const typename S::EpW& e) __attribute__((always_inline)) {
       const int b = my_block(rot);
       if (b < nfin) {   // uniform
         const int q = rot & (NB - 1);
-        lds_wait_eq(pcnt + q, kWaves);
+        const bool all_in = lds_wait_eq(pcnt + q, kWaves, p.spin);
         float* part = red + q * kWaves * MT * 256;
-        if (three) {
+        if (!all_in) {
+          if (lane == 0) atomicAdd(p.timeouts, 1u);
+          if (three) finalize_failed<MT, 3>(p, 0, tl, lane, true);
+          else if (p.terms == 1) finalize_failed<MT, 1>(p, b, tl, lane, false);
+          else finalize_failed<MT, 2>(p, b, tl, lane, false);
+        } else if (three) {
           finalize_tile3<MT>(p, part, mr, tl, lane);
         } else {
           float res[4], add = __builtin_bit_cast(float, 0u);

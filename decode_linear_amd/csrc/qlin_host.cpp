@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "qlin_fused.h"
@@ -103,8 +104,34 @@ int cu_count() {
 }
 
 // Which kernel family serves quantized calls: 0 the int8 streaming kernel where its shape
-// rules admit the call (else the general kernel), 1 always the general kernel.
+// rules admit the call (else the general kernel), 1 always the general kernel, 2 the
+// vector-ALU kernel where it applies.
 std::atomic<int> g_path{0};
+
+// Polls a merge wait of the general kernel makes before it gives up, and the device counter
+// of the waits that gave up (one per GPU; its address looked up once per device).
+std::atomic<int> g_merge_spin{qlin::kSpinMax};
+static __device__ unsigned int g_merge_timeouts;
+
+hipError_t merge_timeouts_ptr(unsigned int** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static unsigned int* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_merge_timeouts));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<unsigned int*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 int pow2_ceil(int v) {
   int p = 1;
@@ -246,6 +273,8 @@ qlin_status launch(const void* x, int x_dtype, int32_t T, const qlin_weight* w, 
     p.scale_gb = (p.ln && x_dtype == QLIN_BF16) ? 1 : 0;
   }
   p.act = act; p.res = res; p.add = add; p.y = y; p.y_dtype = y_dtype;
+  p.spin = g_merge_spin.load(std::memory_order_relaxed);
+  if (merge_timeouts_ptr(&p.timeouts) != hipSuccess) return QLIN_ERR_HIP;
   p.rows = act_rows(T, p.terms, p.ln);
   const int mt = (p.rows + 15) / 16;
   const int64_t row_bytes = w->K * w->bits / 8;
@@ -631,6 +660,21 @@ qlin_status qlin_kvq_decode_noalloc(const void* q, qlin_dtype q_dtype, int32_t h
 int32_t qlin_set_path(int32_t path) {
   if (path < 0 || path > 2) return -1;
   return g_path.exchange(path, std::memory_order_relaxed);
+}
+
+int32_t qlin_set_merge_spin_limit(int32_t limit) {
+  if (limit < 0) return -1;
+  return g_merge_spin.exchange(limit, std::memory_order_relaxed);
+}
+
+int64_t qlin_merge_timeouts(int32_t reset) {
+  if (reset != 0 && reset != 1) return -1;
+  unsigned int* p = nullptr;
+  if (merge_timeouts_ptr(&p) != hipSuccess) return -1;
+  unsigned int v = 0;
+  if (hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  if (reset && hipMemset(p, 0, sizeof(v)) != hipSuccess) return -1;
+  return (int64_t)v;
 }
 
 int64_t qlin_dispatch_count(int32_t which) {

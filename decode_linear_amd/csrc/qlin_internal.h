@@ -38,6 +38,8 @@ struct LinParams {
   int ntiles;             // 16-column output tiles (linear) or 8-column tiles (gate/up)
   int steps;              // 64-byte steps per weight row
   int chunk_steps;        // steps staged at once (all of them unless K is long)
+  int spin;               // polls a merge wait makes before it gives up
+  unsigned int* timeouts; // device counter of merge waits that gave up
 };
 
 // Rows of the activation operand: terms*T activation terms, then gamma and beta (LN).

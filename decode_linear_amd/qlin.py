@@ -4,7 +4,7 @@ Every computation runs in the library's HIP kernels; PyTorch supplies device
 memory and the current HIP stream.  The names follow the C ABI:
 qlin_linear, qlin_gateup_swiglu, qlin_pack_affine, qlin_unpack_affine,
 qlin_mlp, qlin_sample, qlin_kvq_decode, qlin_kvq_decode_noalloc, qlin_attend, qlin_check, qlin_attend_check, qlin_stream_read, qlin_stream_read_config, qlin_status_string,
-qlin_dispatch_count, qlin_set_path,
+qlin_dispatch_count, qlin_set_path, qlin_merge_timeouts, qlin_set_merge_spin_limit,
 and the chain calls
 (QlinChain wraps qlin_chain_create / launch / destroy).
 
@@ -91,6 +91,10 @@ def lib():
                                           i32, vp]
     L.qlin_set_path.argtypes = [i32]
     L.qlin_set_path.restype = i32
+    L.qlin_merge_timeouts.argtypes = [i32]
+    L.qlin_merge_timeouts.restype = i64
+    L.qlin_set_merge_spin_limit.argtypes = [i32]
+    L.qlin_set_merge_spin_limit.restype = i32
     L.qlin_dispatch_count.argtypes = [i32]
     L.qlin_dispatch_count.restype = i64
     L.qlin_status_string.argtypes = [i32]
@@ -110,6 +114,15 @@ def qlin_status_string(status: int) -> str:
 
 def qlin_dispatch_count(which: int) -> int:
     return int(lib().qlin_dispatch_count(int(which)))
+
+
+def qlin_merge_timeouts(reset: bool = False) -> int:
+    """Merge waits of the general kernel that gave up on the current device (see qlin.h)."""
+    return int(lib().qlin_merge_timeouts(1 if reset else 0))
+
+
+def qlin_set_merge_spin_limit(limit: int) -> int:
+    return int(lib().qlin_set_merge_spin_limit(int(limit)))
 
 
 def qlin_set_path(path: int) -> int:

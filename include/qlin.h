@@ -341,6 +341,21 @@ int64_t qlin_dispatch_count(int32_t which);
  * synchronized with calls in flight on other host threads. */
 int32_t qlin_set_path(int32_t path);
 
+/* The general kernel (dense weights, and the calls the int8 kernel does not take) merges its
+ * waves' partial sums through LDS handshakes whose waits are bounded.  A wait that gives up
+ * (which only a fault of the device could cause) is never silent: the outputs that depended
+ * on it are stored as NaN, and a per-GPU device counter is incremented.
+ *   qlin_merge_timeouts(reset): the current device's counter (call it after the launches
+ *     have completed, e.g. once their stream is synchronized; it copies from the device);
+ *     reset = 1 also clears it.  -1 on a HIP error or a reset other than 0 or 1.
+ *   qlin_set_merge_spin_limit(limit): polls a wait makes before it gives up, for launches
+ *     made after the call (default 4194304, each poll sleeping about 64 clocks); limit >= 0.
+ *     A limit of 0 makes every wait give up at once, so that a test can see the report
+ *     without any wait actually failing.  Returns the previous limit, or -1 (and changes
+ *     nothing) for a negative limit.  Process-wide, not synchronized with other threads. */
+int64_t qlin_merge_timeouts(int32_t reset);
+int32_t qlin_set_merge_spin_limit(int32_t limit);
+
 /* Static description of a status code. */
 const char* qlin_status_string(qlin_status s);
 

@@ -344,3 +344,12 @@ def test_kvq_noalloc_validation(q):
     # the largest heads x rows that still fit, just past it
     assert ws(32, 64 * 128, 256) <= q.QLIN_KVQ_SCRATCH_BYTES < ws(32, 64 * 128 * 4, 256)
     assert call(H=32, KV=8, N=64 * 128 * 4, D=256) == -8
+
+
+def test_merge_report_entry_points_validate(q):
+    lib = q.lib()
+    assert lib.qlin_set_merge_spin_limit(-1) == -1
+    prev = lib.qlin_set_merge_spin_limit(1000)
+    assert prev >= 0
+    assert lib.qlin_set_merge_spin_limit(prev) == 1000
+    assert lib.qlin_merge_timeouts(2) == -1 and lib.qlin_merge_timeouts(-1) == -1
