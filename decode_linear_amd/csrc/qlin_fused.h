@@ -1205,9 +1205,11 @@ __device__ __forceinline__ void finalize(const LinParams& p, const float* red, c
 // 16-lane row.  part: the tile's partials, [wave][MT][256].  res / add: the lane's residual
 // values (one per output row) and constant.  Epilogue order as [p1] `_linear_kernel`: GELU,
 // then residual, then constant; one rounding to the output type.
+// bad: the tile's merge wait gave up; its outputs are stored as NaN (a select, not a branch,
+// so that the stores and their wait counts are the same on both paths).
 template <int MT, int NT>
 __device__ __forceinline__ void finalize_block(const LinParams& p, const float* part, const float* mr, int b, int tile,
-                                               int lane, const float res[4 / NT], float add) {
+                                               int lane, const float res[4 / NT], float add, bool bad = false) {
   const int c = lane >> 4, li = lane & 15;
   const int T = p.T;
   // all eight reads in flight before the first add (one LDS round trip)
@@ -1246,13 +1248,13 @@ __device__ __forceinline__ void finalize_block(const LinParams& p, const float* 
       const float u = dpp_f<0x128>(v);   // row_ror:8
       v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
       const int n = tile * 8 + li;
-      if (t < T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      if (t < T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, bad ? __builtin_nanf("") : v);
     } else {
       if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
       if (p.res) v += res[o];
       if (p.add) v += add;
       const int n = tile * 16 + li;
-      if (t < T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      if (t < T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, bad ? __builtin_nanf("") : v);
     }
   }
 }
@@ -1282,7 +1284,8 @@ __device__ __forceinline__ void finalize_rows(const LinParams& p, const float* r
 // positions), then lane (q, n) finishes outputs (4 i + q, n) from the merged rows.  The
 // residual and constant are read from global memory here (a rare path).
 template <int MT>
-__device__ __forceinline__ void finalize_tile3(const LinParams& p, float* part, const float* mr, int tile, int lane) {
+__device__ __forceinline__ void finalize_tile3(const LinParams& p, float* part, const float* mr, int tile, int lane,
+                                               bool bad = false) {
   constexpr int NT = 3;
   const int T = p.T;
 #pragma unroll
@@ -1312,14 +1315,14 @@ __device__ __forceinline__ void finalize_tile3(const LinParams& p, float* part, 
       const float u = dpp_f<0x128>(v);   // row_ror:8
       v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
       const int n = tile * 8 + col;
-      if (t < T && col < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      if (t < T && col < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, bad ? __builtin_nanf("") : v);
     } else {
       const int n = tile * 16 + col;
       const bool ok = t < T && n < p.N;
       if (p.act == 1) v = 0.5f * v * erfcf(-v * 0.70710678118654752f);
       if (p.res && ok) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.res)[(long)t * p.N + n], p.x_dtype);
       if (p.add && ok) v += elem_to_float(reinterpret_cast<const uint16_t*>(p.add)[n], p.x_dtype);
-      if (ok) store_out(p.y, p.y_dtype, (long)t * p.N + n, v);
+      if (ok) store_out(p.y, p.y_dtype, (long)t * p.N + n, bad ? __builtin_nanf("") : v);
     }
   }
 }
@@ -1335,25 +1338,6 @@ __device__ __forceinline__ bool lds_wait_eq(const int* a, int v, int limit) {
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
-}
-
-// The outputs a finishing wave owns for block b of a tile (or, with three-term rows, the
-// whole tile), stored as NaN: its merge wait gave up, so its partial sums are not known.
-template <int MT, int NT>
-__device__ __forceinline__ void finalize_failed(const LinParams& p, int b, int tile, int lane, bool whole) {
-  const int c = lane >> 4, li = lane & 15;
-  const float nan = __builtin_nanf("");
-  for (int t0 = whole ? 0 : (16 * b + 4 * c) / NT; t0 < (whole ? p.T : (16 * b + 4 * c) / NT + 4 / NT);
-       t0 += whole ? 4 : 1) {
-    const int t = whole ? t0 + c : t0;
-    if (p.gateup) {
-      const int n = tile * 8 + li;
-      if (t < p.T && li < 8 && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, nan);
-    } else {
-      const int n = tile * 16 + li;
-      if (t < p.T && n < p.N) store_out(p.y, p.y_dtype, (long)t * p.N + n, nan);
-    }
-  }
 }
 
 // EPI (streaming variant): the call is a linear with residual or constant inputs.
@@ -1500,17 +1484,18 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     // block of tile rot this wave finishes (none when >= nfin)
     auto my_block = [&](int rot) __attribute__((always_inline)) { return (wv - rot) & 7; };
     // Put this wave's partials of tile rot into its buffer once the buffer is open for it.
-    // A put whose wait gives up writes nothing and does not count itself in: the tile's
-    // finishing waves then give up too and store NaN (each give-up counts in p.timeouts).
+    // Give-ups of the bounded waits are counted in a register and added to p.timeouts once,
+    // at the end of the kernel (a global atomic inside a branch here would make the compiler
+    // wait for every load in flight at the join).  A put writes after its wait either way, so
+    // that no branch separates the compute from the next tile; a finishing wave that gives up
+    // stores NaN.  Any give-up is therefore reported, by the counter and/or NaN outputs.
+    int gave_up = 0;
     auto put = [&](const f4_t acc[MT], int rot) __attribute__((always_inline)) {
       const int q = rot & (NB - 1);
-      if (lds_wait_eq(pgen + q, rot, p.spin)) {
-        write_partials(acc, 0, red + q * kWaves * MT * 256);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the writes are done
-        if (lane == 0) __hip_atomic_fetch_add(pcnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else if (lane == 0) {
-        atomicAdd(p.timeouts, 1u);
-      }
+      gave_up += lds_wait_eq(pgen + q, rot, p.spin) ? 0 : 1;
+      write_partials(acc, 0, red + q * kWaves * MT * 256);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the writes are done
+      if (lane == 0) __hip_atomic_fetch_add(pcnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
     // Finish tile `tl` (index rot) if this wave owns one of its blocks.
     auto finish_tile = [&](int tl, int rot, const typename S::EpW& e) __attribute__((always_inline)) {
@@ -1518,21 +1503,17 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
       if (b < nfin) {   // uniform
         const int q = rot & (NB - 1);
         const bool all_in = lds_wait_eq(pcnt + q, kWaves, p.spin);
+        gave_up += all_in ? 0 : 1;
         float* part = red + q * kWaves * MT * 256;
-        if (!all_in) {
-          if (lane == 0) atomicAdd(p.timeouts, 1u);
-          if (three) finalize_failed<MT, 3>(p, 0, tl, lane, true);
-          else if (p.terms == 1) finalize_failed<MT, 1>(p, b, tl, lane, false);
-          else finalize_failed<MT, 2>(p, b, tl, lane, false);
-        } else if (three) {
-          finalize_tile3<MT>(p, part, mr, tl, lane);
+        if (three) {
+          finalize_tile3<MT>(p, part, mr, tl, lane, !all_in);
         } else {
           float res[4], add = __builtin_bit_cast(float, 0u);
 #pragma unroll
           for (int o = 0; o < 4; ++o) res[o] = elem_to_float(e.v[o], p.x_dtype);
           add = elem_to_float(e.v[4], p.x_dtype);
-          if (p.terms == 1) finalize_block<MT, 1>(p, part, mr, b, tl, lane, res, add);
-          else finalize_block<MT, 2>(p, part, mr, b, tl, lane, res, add);
+          if (p.terms == 1) finalize_block<MT, 1>(p, part, mr, b, tl, lane, res, add, !all_in);
+          else finalize_block<MT, 2>(p, part, mr, b, tl, lane, res, add, !all_in);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the reads are done
         if (lane == 0) {
@@ -1592,6 +1573,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const LinParams p) {
     } else {       // the last tile (index n - 1) is tile - G
       finish_tile(tile - G, n - 1, ea);
     }
+    if (gave_up != 0 && lane == 0) atomicAdd(p.timeouts, (unsigned int)gave_up);   // all tiles are done
   } else {
     // Long K: rebuild the fragments per chunk.  acc stays in the current chunk's scaled
     // units; switching chunks multiplies by a ratio of powers of two (exact).

@@ -343,8 +343,9 @@ int32_t qlin_set_path(int32_t path);
 
 /* The general kernel (dense weights, and the calls the int8 kernel does not take) merges its
  * waves' partial sums through LDS handshakes whose waits are bounded.  A wait that gives up
- * (which only a fault of the device could cause) is never silent: the outputs that depended
- * on it are stored as NaN, and a per-GPU device counter is incremented.
+ * (which only a fault of the device could cause) is never silent: every give-up increments
+ * a per-GPU device counter, and the outputs of a tile whose final wait gave up are stored
+ * as NaN.
  *   qlin_merge_timeouts(reset): the current device's counter (call it after the launches
  *     have completed, e.g. once their stream is synchronized; it copies from the device);
  *     reset = 1 also clears it.  -1 on a HIP error or a reset other than 0 or 1.
