@@ -198,11 +198,15 @@ _OUT_DTYPES = (torch.float32, torch.float16, torch.bfloat16)
 class _Args:
     """Checks of one call's tensors, raised as ValueError before anything is launched (the C
     ABI sees only pointers and sizes, so a tensor's shape can only be checked here).  Shapes,
-    contiguity and dtypes first, for every argument; then that all of them sit on one GPU."""
+    contiguity and dtypes first, for every argument; then that all of them sit on one GPU.
+    The passing path is a few attribute reads per tensor; messages are built on failure."""
+
+    __slots__ = ("where", "devs", "names")
 
     def __init__(self, where: str):
         self.where = where
-        self.seen = []
+        self.devs = []
+        self.names = []
 
     def fail(self, msg: str):
         raise ValueError(f"{self.where}: {msg}")
@@ -215,30 +219,37 @@ class _Args:
             self.fail(f"{name} is required")
         if not isinstance(t, torch.Tensor):
             self.fail(f"{name} must be a torch.Tensor")
-        if t.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape)):
+        sh = t.shape
+        if None in shape:
+            ok = len(sh) == len(shape) and all(e is None or a == e for a, e in zip(sh, shape))
+        else:
+            ok = sh == shape
+        if not ok:
             want = "(" + ", ".join("*" if e is None else str(e) for e in shape) + ")"
-            self.fail(f"{name} must have shape {want}, got {tuple(t.shape)}")
+            self.fail(f"{name} must have shape {want}, got {tuple(sh)}")
         if not t.is_contiguous():
             self.fail(f"{name} must be contiguous")
         if dtypes is not None and t.dtype not in dtypes:
             self.fail(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
-        self.seen.append((name, t))
+        self.devs.append(t.get_device())   # -1 on the CPU
+        self.names.append(name)
 
     def weight(self, name: str, w, K: Optional[int] = None):
         if not isinstance(w, QWeight):
             self.fail(f"{name} must be a QWeight")
-        if w.bits not in (4, 8, 16):
-            self.fail(f"{name}.bits must be 4, 8 or 16, got {w.bits}")
+        bits = w.bits
+        if bits not in (4, 8, 16):
+            self.fail(f"{name}.bits must be 4, 8 or 16, got {bits}")
         if K is not None and w.K != K:
             self.fail(f"{name}.K = {w.K} does not match the activation row length {K}")
         if w.K <= 0 or w.K % 64 or w.N < 0:
             self.fail(f"{name} must have K a positive multiple of 64 and N >= 0")
-        if w.bits == 16:
+        if bits == 16:
             self.need(f"{name}.data", w.data, (w.N, w.K), _ACT_DTYPES)
         else:
-            self.need(f"{name}.data", w.data, (w.N, w.K * w.bits // 32), (torch.int32,))
-            self.need(f"{name}.scales", w.scales, (w.N, w.K // 64), (torch.float16,))
-            self.need(f"{name}.biases", w.biases, (w.N, w.K // 64), (torch.float16,))
+            self.need(f"{name}.data", w.data, (w.N, w.K * bits // 32), _I32)
+            self.need(f"{name}.scales", w.scales, (w.N, w.K // 64), _F16)
+            self.need(f"{name}.biases", w.biases, (w.N, w.K // 64), _F16)
 
     def ln(self, ln, K: int, dtype):
         if ln is None:
@@ -249,14 +260,22 @@ class _Args:
         self.need("beta", ln[1], (K,), (dtype,))
 
     def on_one_gpu(self):
-        dev = None
-        for name, t in self.seen:
-            if not t.is_cuda:
-                self.fail(f"{name} must be on a GPU, got {t.device}")
-            if dev is None:
-                dev = t.device
-            elif t.device != dev:
-                self.fail(f"{name} is on {t.device}, the other arguments on {dev}")
+        devs = self.devs
+        if not devs:
+            return
+        d0 = devs[0]
+        if d0 >= 0 and devs.count(d0) == len(devs):
+            return
+        for name, d in zip(self.names, devs):
+            if d < 0:
+                self.fail(f"{name} must be on a GPU, got cpu")
+        for name, d in zip(self.names, devs):
+            if d != d0:
+                self.fail(f"{name} is on cuda:{d}, the other arguments on cuda:{d0}")
+
+
+_I32 = (torch.int32,)
+_F16 = (torch.float16,)
 
 
 def qlin_linear(x: torch.Tensor, w: QWeight, ln=None, act: int = QLIN_ACT_NONE,
