@@ -17,7 +17,8 @@
 // per-slice value accumulator (each value decoded once for both heads), summed over the
 // row slots at the end of the block.  The waves merge in LDS in a fixed order into the
 // block's unnormalized output and (max, sum) per head.  merge_kernel combines the blocks in
-// block order.  No atomics: the result is bitwise reproducible.
+// a fixed order (four quarters of the block range, each in block order, then the quarters in
+// order).  No atomics: the result is bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -139,9 +140,9 @@ template <int LO, int N> __device__ __forceinline__ int scatter_base(int lane) {
 // One workgroup per (block g, KV head c, chunk z of QC query heads sharing c): the block's
 // rows of c are read once for all QC heads (each key slice's dot product is taken against
 // every head's query, and each value is decoded once and added to every head's accumulator).
-template <int BITS, int D, int QC>
+template <int BITS, int D, int QC, int SBT>
 __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
-  constexpr int P = 4;                  // steps whose rows are in flight at once
+  constexpr int P = 2;                  // steps whose rows are in flight at once
   constexpr int RB = D * BITS / 8;      // bytes of a row of codes
   constexpr int LPR = RB / 16;          // lanes per row: each takes 16 bytes
   constexpr int LB = log2i(LPR);        // lane-index bits of the slice (the rest: the row slot)
@@ -159,12 +160,15 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
   const int start = g * a.block, end = min(start + a.block, a.N);
   const int groups = D / a.GS, gi = (j * EL) / a.GS;
   const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
-  const uint16_t* ks = static_cast<const uint16_t*>(a.ks);
-  const uint16_t* kb = static_cast<const uint16_t*>(a.kb);
-  const uint16_t* vs = static_cast<const uint16_t*>(a.vs);
-  const uint16_t* vb = static_cast<const uint16_t*>(a.vb);
-  const u4_t* kc = reinterpret_cast<const u4_t*>(a.kc);
-  const u4_t* vc = reinterpret_cast<const u4_t*>(a.vc);
+  // the block's rows of KV head c: bases shared by the workgroup, 32-bit offsets per lane
+  const long rbase = (long)c * a.N + start;
+  const uint16_t* ks = static_cast<const uint16_t*>(a.ks) + rbase * groups;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.kb) + rbase * groups;
+  const uint16_t* vs = static_cast<const uint16_t*>(a.vs) + rbase * groups;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.vb) + rbase * groups;
+  const u4_t* kc = reinterpret_cast<const u4_t*>(a.kc) + rbase * LPR;
+  const u4_t* vc = reinterpret_cast<const u4_t*>(a.vc) + rbase * LPR;
+  const int nloc = end - start;   // rows of the block (>= 1)
   // this lane's EL query elements of each head: 16-byte loads when q is 16-byte aligned
   float qv[QC][EL], qsum[QC];
   if (a.q_vec) {
@@ -200,22 +204,34 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
 #pragma unroll
     for (int e = 0; e < EL; ++e) o[i][e] = 0.0f;
   }
-  // The wave's steps run in rounds of P: the rows of P steps are in flight at once (the loads
-  // of the next round are issued as each step is done).  A round first takes the P steps'
-  // scores, then moves the running max once, then adds the P steps' values.  Every slot is
-  // computed (the last round's steps past the block read row end - 1 and are masked), so no
-  // branch separates a load from its use.
-  const int first = start + R * wv;
-  const int nsteps = first < end ? (end - first + kKvqWaves * R - 1) / (kKvqWaves * R) : 0;
+  // The wave's steps run in rounds of P: the rows of P steps are in flight at once.  A round
+  // first takes the P steps' scores, then moves the running max once, then adds the P steps'
+  // values; the next round's keys are issued once the scores are taken and its values once
+  // the values are added (only when there is a next round: a uniform branch).  Every slot
+  // is computed (steps past the block read its last row and are masked).  Nothing combines
+  // a loaded value at issue, so no load is waited for before its round uses it.
+  const int first = R * wv;   // the wave's first row in the block
+  const int nsteps = first < nloc ? (nloc - first + kKvqWaves * R - 1) / (kKvqWaves * R) : 0;
   u4_t kw[P], vw[P];
-  uint32_t sbk[P], sbv[P];   // scale | bias << 16 of the slice's group, keys and values
-  auto issue = [&](int sl, int q) __attribute__((always_inline)) {
+  uint32_t ksr[P], kbr[P], vsr[P], vbr[P];   // the slice group's scale and bias bits
+  auto row_of = [&](int q) __attribute__((always_inline)) {
     const int n = first + q * (kKvqWaves * R) + slot;
-    const long row = (long)c * a.N + (n < end ? n : end - 1);
-    kw[sl] = kc[row * LPR + j];
-    vw[sl] = vc[row * LPR + j];
-    sbk[sl] = (uint32_t)ks[row * groups + gi] | ((uint32_t)kb[row * groups + gi] << 16);
-    sbv[sl] = (uint32_t)vs[row * groups + gi] | ((uint32_t)vb[row * groups + gi] << 16);
+    return (uint32_t)(n < nloc ? n : nloc - 1);
+  };
+  auto issue_k = [&](int sl, int q) __attribute__((always_inline)) {
+    const uint32_t r = row_of(q);
+    kw[sl] = kc[r * LPR + j];
+    ksr[sl] = ks[r * groups + gi];
+    kbr[sl] = kb[r * groups + gi];
+  };
+  auto issue_v = [&](int sl, int q) __attribute__((always_inline)) {
+    const uint32_t r = row_of(q);
+    vw[sl] = vc[r * LPR + j];
+    vsr[sl] = vs[r * groups + gi];
+    vbr[sl] = vb[r * groups + gi];
+  };
+  auto sbf = [](uint32_t h) __attribute__((always_inline)) {
+    return SBT == 1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h) : __builtin_bit_cast(float, h << 16);
   };
   // the slice's EL codes as floats (4-bit: the even and odd codes of a dword spread to bytes
   // first); each byte converts in one instruction
@@ -231,14 +247,18 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
     }
   };
 #pragma unroll
-  for (int sl = 0; sl < P; ++sl) issue(sl, sl);
+  for (int sl = 0; sl < P; ++sl) issue_k(sl, sl);
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) issue_v(sl, sl);
+  __builtin_amdgcn_sched_barrier(0);
   for (int q0 = 0; q0 < nsteps; q0 += P) {
+    const bool more = q0 + P < nsteps;
     float sc[P][QC];
     bool live[P];
 #pragma unroll
     for (int sl = 0; sl < P; ++sl) {
-      live[sl] = first + (q0 + sl) * (kKvqWaves * R) + slot < end;
-      const float ksc = half_to_float(sbk[sl] & 0xFFFFu, a.sb_dtype), kbi = half_to_float(sbk[sl] >> 16, a.sb_dtype);
+      live[sl] = first + (q0 + sl) * (kKvqWaves * R) + slot < nloc;
+      const float ksc = sbf(ksr[sl]), kbi = sbf(kbr[sl]);
       float kf[EL];
       codes(kw[sl], kf);
 #pragma unroll
@@ -249,23 +269,29 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
         sc[sl][i] = lane_reduce<0, LB, false>(fmaf(ksc, dot, kbi * qsum[i]));   // the row's score on its LPR lanes
       }
     }
+    if (more) {
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) issue_k(sl, q0 + P + sl);
+    }
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
       float m = -__builtin_inff();
 #pragma unroll
       for (int sl = 0; sl < P; ++sl) m = fmaxf(m, live[sl] ? sc[sl][i] : -__builtin_inff());
       const float mnew = fmaxf(mx[i], lane_reduce<LB, 6, true>(m));   // over the round's rows
-      // a round without live rows (mnew may still be -inf) leaves the state as it is
-      const float f = mnew == -__builtin_inff() ? 1.0f : expf(mx[i] - mnew);
-      mx[i] = mnew;
-      lsum[i] *= f;
-      pvb[i] *= f;
+      if (q0 != 0) {   // the first round's state is still zero: nothing to rescale
+        // a round without live rows (mnew may still be -inf) leaves the state as it is
+        const float f = mnew == -__builtin_inff() ? 1.0f : expf(mx[i] - mnew);
+        lsum[i] *= f;
+        pvb[i] *= f;
 #pragma unroll
-      for (int e = 0; e < EL; ++e) o[i][e] *= f;
+        for (int e = 0; e < EL; ++e) o[i][e] *= f;
+      }
+      mx[i] = mnew;
     }
 #pragma unroll
     for (int sl = 0; sl < P; ++sl) {
-      const float vsc = half_to_float(sbv[sl] & 0xFFFFu, a.sb_dtype), vbi = half_to_float(sbv[sl] >> 16, a.sb_dtype);
+      const float vsc = sbf(vsr[sl]), vbi = sbf(vbr[sl]);
       float vf[EL];
       codes(vw[sl], vf);
 #pragma unroll
@@ -277,7 +303,10 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) o[i][e] = fmaf(w, vf[e], o[i][e]);
       }
-      issue(sl, q0 + sl + P);
+    }
+    if (more) {
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) issue_v(sl, q0 + P + sl);
     }
   }
 #pragma unroll
@@ -339,75 +368,64 @@ __device__ __forceinline__ float merge_reduce(float v, float* part) {
   return r;
 }
 
-// out[h, d] = sum_g opart[h, g, d] e^(M_g - M) / sum_g S_g e^(M_g - M), one workgroup per
-// head.  M and the denominator are fixed-order reductions (thread t takes blocks t, t + 256,
-// ... in order, then merge_reduce: a butterfly per wave and the waves in order; one thread
-// walking 256 LDS partials cost about 2.5 us); the block weights e^(M_g - M) go to LDS in
-// chunks, and each thread sums its columns over the blocks in block order with the loads of
-// a chunk independent of each other.
+// out[h, d] = sum_g opart[h, g, d] e^(M_g - M) / sum_g S_g e^(M_g - M).  One workgroup per
+// (head, 64 columns); wave k of it sums its columns over the k-th quarter of the blocks
+// (contiguous, in block order) and the quarters are added in order, so the result is the
+// same on every run.  A thread's first kPrefetch partials and their block maxima are loaded
+// before the statistics are reduced (M and the denominator: every thread takes blocks t,
+// t + 256, ... in order, then merge_reduce), so the partials and the statistics arrive in
+// one round of loads; the block weights e^(M_g - M) are formed in registers.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 4096;
+constexpr int kMergeCols = 64;
+constexpr int kPrefetch = 16;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const KvqParams a) {
   __shared__ float part[kMergeThreads];
-  __shared__ float wgt[kMergeChunk];
+  __shared__ float quarter[kMergeThreads / 64][kMergeCols];
   const int h = blockIdx.x, t = threadIdx.x, D = a.D, G = a.G;
+  const int col = (int)blockIdx.y * kMergeCols + (t & 63), k = t >> 6;
+  const int g_lo = (int)((long)G * k / 4), g_hi = (int)((long)G * (k + 1) / 4);   // this wave's blocks
   const float* st = a.stats + (long)h * G * 2;
-  // up to 256 blocks (every head with at most 32768 rows): each thread reads its block's
-  // statistics once and keeps them for the weights
-  const bool one = G <= kMergeThreads;
-  float m_t = -__builtin_inff(), s_t = 0.0f;
-  if (one && t < G) {
-    m_t = st[2 * t];
-    s_t = st[2 * t + 1];
+  const float* op = a.opart + (long)h * G * D + col;
+  float pre[kPrefetch], pm[kPrefetch];
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) {
+    const int g = min(g_lo + i, G - 1);
+    pre[i] = op[(long)g * D];
+    pm[i] = st[2 * g];
   }
-  float m = m_t;
-  if (!one)
-    for (int g = t; g < G; g += kMergeThreads) m = fmaxf(m, st[2 * g]);
+  float m = -__builtin_inff();
+  for (int g = t; g < G; g += kMergeThreads) m = fmaxf(m, st[2 * g]);
   const float M = merge_reduce<true>(m, part);
-  const float w_t = expf(m_t - M);
-  float den = one ? fmaf(s_t, w_t, 0.0f) : 0.0f;
-  if (!one)
-    for (int g = t; g < G; g += kMergeThreads) den = fmaf(st[2 * g + 1], expf(st[2 * g] - M), den);
+  float den = 0.0f;
+  for (int g = t; g < G; g += kMergeThreads) den = fmaf(st[2 * g + 1], expf(st[2 * g] - M), den);
   const float den_all = merge_reduce<false>(den, part);
-  float o0 = 0.0f, o1 = 0.0f;   // columns t and t + 256 (D <= 512)
-  const float* op = a.opart + (long)h * G * D;
-  for (int g0 = 0; g0 < G; g0 += kMergeChunk) {
-    const int gn = min(kMergeChunk, G - g0);
-    __syncthreads();   // the previous chunk's weights are read
-    if (one) {
-      if (t < G) wgt[t] = w_t;
-    } else {
-      for (int i = t; i < gn; i += kMergeThreads) wgt[i] = expf(st[2 * (g0 + i)] - M);
-    }
-    __syncthreads();
-    if (t < D) {
-#pragma unroll 16
-      for (int i = 0; i < gn; ++i) o0 = fmaf(op[(long)(g0 + i) * D + t], wgt[i], o0);
-    }
-    if (t + kMergeThreads < D) {
-#pragma unroll 16
-      for (int i = 0; i < gn; ++i) o1 = fmaf(op[(long)(g0 + i) * D + t + kMergeThreads], wgt[i], o1);
-    }
-  }
-  for (int k = 0; k < 2; ++k) {
-    const int d = t + k * kMergeThreads;
-    if (d >= D) continue;
-    const float v = (k == 0 ? o0 : o1) / den_all;
-    const long idx = (long)h * D + d;
+  float o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) o = g_lo + i < g_hi ? fmaf(pre[i], expf(pm[i] - M), o) : o;
+#pragma unroll 8
+  for (int g = g_lo + kPrefetch; g < g_hi; ++g) o = fmaf(op[(long)g * D], expf(st[2 * g] - M), o);
+  quarter[k][t & 63] = o;
+  __syncthreads();
+  if (t < kMergeCols) {
+    float v = quarter[0][t];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; ++w) v += quarter[w][t];
+    v /= den_all;
+    const long idx = (long)h * D + col;
     if (a.out_dtype == 0) static_cast<float*>(a.out)[idx] = v;
     else if (a.out_dtype == 1) static_cast<_Float16*>(a.out)[idx] = (_Float16)v;
     else static_cast<__bf16*>(a.out)[idx] = (__bf16)v;
   }
 }
 
-template <int BITS, int QC>
+template <int BITS, int QC, int SBT>
 hipError_t launch_block_qc(const KvqParams& a, hipStream_t s) {
   const dim3 grid(a.G, a.KV, (a.H / a.KV) / QC);
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512, QC>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -416,7 +434,9 @@ hipError_t launch_block_qc(const KvqParams& a, hipStream_t s) {
 // Query heads per workgroup: two where the heads sharing a KV head pair up, else one.
 template <int BITS>
 hipError_t launch_block(const KvqParams& a, hipStream_t s) {
-  return (a.H / a.KV) % 2 == 0 ? launch_block_qc<BITS, 2>(a, s) : launch_block_qc<BITS, 1>(a, s);
+  const bool pair = (a.H / a.KV) % 2 == 0;
+  if (a.sb_dtype == 1) return pair ? launch_block_qc<BITS, 2, 1>(a, s) : launch_block_qc<BITS, 1, 1>(a, s);
+  return pair ? launch_block_qc<BITS, 2, 2>(a, s) : launch_block_qc<BITS, 1, 2>(a, s);
 }
 
 }  // namespace
@@ -449,7 +469,7 @@ hipError_t kvq_scratch(float** ptr) {
 hipError_t launch_kvq_decode(const KvqParams& a, hipStream_t s) {
   const hipError_t e = a.bits == 4 ? launch_block<4>(a, s) : launch_block<8>(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.H), dim3(kMergeThreads), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.H, a.D / kMergeCols), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
