@@ -15,7 +15,8 @@
 // butterflies over the wave; the weighted value sum runs with lanes over head dimensions
 // (coalesced rows of v) and the weights broadcast from their key lanes.  The cache copy is
 // spread over the T waves of a head.  Nothing is staged in LDS: every row is read once per
-// wave from L2.
+// wave from L2, and each phase issues its loads together (clamped to valid rows, the extra
+// ones masked) so that a wave waits for one round of loads per phase, not one per row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +26,7 @@ namespace qlin {
 namespace {
 
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+constexpr int kAttendKeys = 32;   // visible keys at most (cached + new positions)
 
 __device__ __forceinline__ float bits_to_float(uint32_t h, int dtype) {
   if (dtype == 2) return __builtin_bit_cast(float, h << 16);
@@ -77,33 +79,52 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
   uint16_t* kv_out = static_cast<uint16_t*>(a.kv_out);
 
   // The cache: this wave's new rows (position P + t), and the cached rows j = t, t + T, ...
+  // Four pieces per lane are loaded before any is stored.
   const int mine = P > t ? (P - t + T - 1) / T : 0;
-  for (int i = lane; i < (1 + mine) * 2 * pieces; i += 64) {
-    const int r = i / (2 * pieces), kvsel = (i / pieces) & 1, pc = i % pieces;
-    const u4_t* src;
-    long j;
-    if (r == 0) {
-      j = P + t;
-      src = reinterpret_cast<const u4_t*>(qkv + (long)t * 3 * D + (1 + kvsel) * D + (long)h * HD) + pc;
-    } else {
-      j = t + (long)(r - 1) * T;
-      src = reinterpret_cast<const u4_t*>(kv + (((long)kvsel * H + h) * P + j) * HD) + pc;
+  const int items = (1 + mine) * 2 * pieces;
+  for (int i0 = lane; i0 < items; i0 += 4 * 64) {
+    u4_t buf[4];
+    long dst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + 64 * u, items - 1);
+      const int r = i / (2 * pieces), kvsel = (i / pieces) & 1, pc = i % pieces;
+      const long j = r == 0 ? (long)(P + t) : t + (long)(r - 1) * T;
+      const u4_t* src = r == 0 ? reinterpret_cast<const u4_t*>(qkv + (long)t * 3 * D + (1 + kvsel) * D + (long)h * HD) + pc
+                               : reinterpret_cast<const u4_t*>(kv + (((long)kvsel * H + h) * P + j) * HD) + pc;
+      buf[u] = *src;
+      dst[u] = (((long)kvsel * H + h) * L + j) * HD / 8 + pc;
     }
-    reinterpret_cast<u4_t*>(kv_out + (((long)kvsel * H + h) * L + j) * HD)[pc] = *src;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + 64 * u < items) reinterpret_cast<u4_t*>(kv_out)[dst[u]] = buf[u];
   }
   if (a.last && t != T - 1) return;
 
+  // Scores: lane (j, half) takes key j over half of the head dimensions; the pieces of a
+  // batch of four are loaded before their products (keys past pos read key pos, masked).
   const int pos = P + t;   // keys 0 .. pos are visible
   const int j = lane & 31, half = lane >> 5;
+  const int jk = min(j, pos);
+  const uint16_t* krow = jk < P ? kv + ((long)h * P + jk) * HD : qkv + (long)(jk - P) * 3 * D + D + (long)h * HD;
+  const u4_t* q4 = reinterpret_cast<const u4_t*>(qkv + (long)t * 3 * D + (long)h * HD);
+  const u4_t* k4 = reinterpret_cast<const u4_t*>(krow);
+  const int hp = pieces / 2, pc_lo = half * hp;
   float dot = 0.0f;
-  if (j <= pos) {
-    const uint16_t* krow = j < P ? kv + ((long)h * P + j) * HD : qkv + (long)(j - P) * 3 * D + D + (long)h * HD;
-    const u4_t* q4 = reinterpret_cast<const u4_t*>(qkv + (long)t * 3 * D + (long)h * HD);
-    const u4_t* k4 = reinterpret_cast<const u4_t*>(krow);
-    for (int pc = half * (pieces / 2); pc < (half + 1) * (pieces / 2); ++pc) {
+  for (int b = 0; b < hp; b += 4) {
+    u4_t qw[4], kw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = pc_lo + min(b + u, hp - 1);
+      qw[u] = q4[pc];
+      kw[u] = k4[pc];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (b + u >= hp) break;
       float qf[8], kf[8];
-      widen8(q4[pc], a.dtype, qf);
-      widen8(k4[pc], a.dtype, kf);
+      widen8(qw[u], a.dtype, qf);
+      widen8(kw[u], a.dtype, kf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
     }
@@ -117,14 +138,23 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
   const float z = wave_sum(half == 0 ? e : 0.0f);
   const float p = e / z;
 
+  // Values: lanes over head dimensions; every visible row's element is loaded before the
+  // sum, which runs over the keys in order with each weight read from its key's lane.
   const long row = a.last ? 0 : t;
   for (int d = lane; d < HD; d += 64) {
+    uint32_t vv[kAttendKeys];   // bit patterns, widened at their use
+#pragma unroll
+    for (int jj = 0; jj < kAttendKeys; ++jj) {
+      const int jc = min(jj, pos);
+      const uint16_t* vrow = jc < P ? kv + (((long)H + h) * P + jc) * HD : qkv + (long)(jc - P) * 3 * D + 2 * D + (long)h * HD;
+      vv[jj] = vrow[d];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float o = 0.0f;
-    for (int jj = 0; jj <= pos; ++jj) {
-      const float pj = __shfl(p, jj);
-      const uint16_t* vrow = jj < P ? kv + (((long)H + h) * P + jj) * HD
-                                    : qkv + (long)(jj - P) * 3 * D + 2 * D + (long)h * HD;
-      o = fmaf(pj, bits_to_float(vrow[d], a.dtype), o);
+#pragma unroll
+    for (int jj = 0; jj < kAttendKeys; ++jj) {
+      const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), jj));
+      o = jj <= pos ? fmaf(pj, bits_to_float(vv[jj], a.dtype), o) : o;
     }
     store_elem(a.out, a.out_dtype, row * D + (long)h * HD + d, o);
   }

@@ -40,10 +40,15 @@ __device__ __forceinline__ uint32_t rank_of(float f) {
 __device__ __forceinline__ float logit_of(uint32_t r) {
   return __builtin_bit_cast(float, (r >> 31) ? (r ^ 0x80000000u) : ~r);
 }
-__device__ __forceinline__ float read_logit(const SampleParams& a, int i) {
-  if (a.logit_dtype == 0) return static_cast<const float*>(a.logits)[i];
-  const uint32_t h = static_cast<const uint16_t*>(a.logits)[i];
-  return a.logit_dtype == 1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h) : __builtin_bit_cast(float, h << 16);
+// The bits of logit i (LD: 0 fp32, 1 fp16, 2 bf16) and their exact fp32 value.
+template <int LD> __device__ __forceinline__ uint32_t logit_bits(const void* logits, int i) {
+  if constexpr (LD == 0) return static_cast<const uint32_t*>(logits)[i];
+  else return static_cast<const uint16_t*>(logits)[i];
+}
+template <int LD> __device__ __forceinline__ float logit_value(uint32_t b) {
+  if constexpr (LD == 0) return __builtin_bit_cast(float, b);
+  else if constexpr (LD == 1) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  else return __builtin_bit_cast(float, b << 16);
 }
 // Candidate word of code i with score s: 0 (never wins) for a NaN score; otherwise the rank of
 // s (with -0 taken as +0) above the complement of i, so that a larger score, then a smaller
@@ -75,6 +80,7 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t w) {
   return w;
 }
 
+template <int LD>
 __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
 #pragma clang fp contract(off)
   __shared__ uint32_t counts[kWv][256];   // one digit histogram per wave
@@ -103,12 +109,18 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
     for (; p < total; p += kThr) out[p] = src[p];
   }
 
+  // Every logit and noise value of this thread is loaded before any is used (indices past n
+  // read element n - 1 and are masked), so the selection waits for one round of loads.
   uint32_t rk[kPer];
+  float gm[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int i = t + kThr * e;
-    rk[e] = i < n ? rank_of(read_logit(a, i)) : 0u;
+    const int i = min(t + kThr * e, n - 1);
+    rk[e] = logit_bits<LD>(a.logits, i);
+    gm[e] = a.gumbel[i];
   }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) rk[e] = t + kThr * e < n ? rank_of(logit_value<LD>(rk[e])) : 0u;
 
   // ---- theta: four 8-bit digits, most significant first ----------------------------------
   uint32_t digits = 0u, left = (uint32_t)a.top_k;   // chosen so far (uniform), ranks wanted
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
     const int i = t + kThr * e;
     if (i < n && rk[e] >= theta) {
       const float scaled = logit_of(rk[e]) * a.inv_temp;   // one fp32 rounding
-      const float s = scaled + a.gumbel[i];                // and another (no contraction)
+      const float s = scaled + gm[e];                      // and another (no contraction)
       const uint64_t c = candidate(s, (uint32_t)i);
       best = c > best ? c : best;
     }
@@ -183,7 +195,9 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
 }  // namespace
 
 hipError_t launch_sample(const SampleParams& a, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(kThr), 0, s, a);
+  if (a.logit_dtype == 0) hipLaunchKernelGGL(sample_kernel<0>, dim3(1), dim3(kThr), 0, s, a);
+  else if (a.logit_dtype == 1) hipLaunchKernelGGL(sample_kernel<1>, dim3(1), dim3(kThr), 0, s, a);
+  else hipLaunchKernelGGL(sample_kernel<2>, dim3(1), dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 
