@@ -19,9 +19,10 @@
 //   * Short windows (the activation fragments of the whole window fit in VGPRs): the wave
 //     issues every activation piece and then the loads of a ring of R tiles at entry, stages
 //     the activations under those loads, and computes the ring slot by slot, issuing the
-//     next tile's loads into the slot it has just finished.  Every slot is computed, with
-//     leading all-zero tiles where the tile count is not a multiple of R, so no branch joins
-//     the paths (a join would wait for every load in flight).
+//     next tile's loads into the slot it has just finished.  Where the tile count is not a
+//     multiple of R, the ring starts with all-zero steps: their loads are issued like the
+//     others (every path issues the same loads, so a join never waits for loads in flight),
+//     and only their arithmetic, which holds no memory operation, is skipped.
 //   * Long windows (one tile per workgroup): the window is staged and consumed in chunks of
 //     8 groups; the loads of CA chunks are in flight ahead of the chunk being staged.
 //   * Exact products on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  Each operand row
@@ -365,9 +366,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   if constexpr (LN) x0v = *(lane < T ? gaddr<uint16_t>(x, (long)lane * K * 2) : zaddr<uint16_t>(0));
 
   // Tiles: a ring of R slots.  Step q of the workgroup's sequence carries its tile q - z; the
-  // z = (R - ntw mod R) mod R leading steps carry zeros (they are computed, while the real
-  // tiles are in flight, and discarded), so that every step is computed: no branch separates
-  // the steps (the compiler would join the paths and wait for every load in flight).
+  // z = (R - ntw mod R) mod R leading steps carry zeros: their loads (of zeros) are issued
+  // like every other step's, so the loads in flight are the same on every path, and only
+  // their arithmetic is skipped (a branch around memory operations would make the compiler
+  // wait for every load in flight where the paths join).  Skipping it lets the first real
+  // tile start as soon as the staging is done: C4 16.4-16.5 -> 16.2-16.4 us.
   typename Kx::TileRegs tr[R];
   const int nq = (ntw + R - 1) / R * R;   // steps
   const int z = nq - ntw;
@@ -608,13 +611,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
     for (int q0 = 0; q0 < nq; q0 += R) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        float acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
-#pragma unroll
-        for (int ch = 0; ch < C::NCH; ++ch) chunk_step(tr[r], ch, ch * C::CG, acc);
         const int q = q0 + r;
-        if (q >= z) put_partial(q - z, acc);
+        if (q >= z) {   // a leading zero step is not computed (no memory operation in the branch)
+          float acc[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = 0.0f;
+#pragma unroll
+          for (int ch = 0; ch < C::NCH; ++ch) chunk_step(tr[r], ch, ch * C::CG, acc);
+          put_partial(q - z, acc);
+        }
         issue_tile(tr[r], tile_of(q + R));
       }
     }
