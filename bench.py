@@ -514,7 +514,10 @@ def measured_traffic():
     rec = json.load(open(path))
     h = hashlib.sha256()
     for f in rec["source_files"]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):   # a source the counters were taken on is gone: stale
+            return None
+        with open(fp, "rb") as fh:
             h.update(fh.read())
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 

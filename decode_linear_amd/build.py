@@ -25,8 +25,9 @@ LIB_PATH = os.path.join(PKG, "libqlin.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qlin_host.cpp", "qlin_pack.hip", "qlin_attend.hip", "qlin_stream.hip", "qlin_sample.hip", "qlin_kvq.hip", "qlin_fused_q4.hip", "qlin_fused_q8.hip",
-           "qlin_fused_f16.hip", "qlin_fused_bf16.hip", "qlin_s8_q4_ln0.hip", "qlin_s8_q4_ln1.hip",
-           "qlin_s8_q8_ln0.hip", "qlin_s8_q8_ln1.hip", "qlin_valu_q4.hip", "qlin_valu_q8.hip",
+           "qlin_fused_f16.hip", "qlin_fused_bf16.hip", "qlin_s8_q4_ln0_bf16.hip", "qlin_s8_q4_ln0_f16.hip",
+           "qlin_s8_q4_ln1_bf16.hip", "qlin_s8_q4_ln1_f16.hip", "qlin_s8_q8_ln0_bf16.hip", "qlin_s8_q8_ln0_f16.hip",
+           "qlin_s8_q8_ln1_bf16.hip", "qlin_s8_q8_ln1_f16.hip", "qlin_valu_q4.hip", "qlin_valu_q8.hip",
            "qlin_valu_f16.hip"]
 
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -190,8 +190,11 @@ bool try_s8(const void* x, int x_dtype, int32_t T, const qlin_weight* w, const q
   for (const void* q : {a.x, a.w0, a.s0, a.b0, a.p1, a.p2, a.p3}) {
     if ((reinterpret_cast<uintptr_t>(q) >> s8::kTagShift) != 0) return false;
   }
-  if (w->bits == 4) *err = ln ? launch_s8_q4_ln1(a, stream) : launch_s8_q4_ln0(a, stream);
-  else *err = ln ? launch_s8_q8_ln1(a, stream) : launch_s8_q8_ln0(a, stream);
+  using L = hipError_t (*)(const S8Launch&, hipStream_t);
+  static const L table[2][2][2] = {   // [8-bit][LayerNorm][bf16 activations]
+      {{launch_s8_q4_ln0_f16, launch_s8_q4_ln0_bf16}, {launch_s8_q4_ln1_f16, launch_s8_q4_ln1_bf16}},
+      {{launch_s8_q8_ln0_f16, launch_s8_q8_ln0_bf16}, {launch_s8_q8_ln1_f16, launch_s8_q8_ln1_bf16}}};
+  *err = table[w->bits == 8][ln ? 1 : 0][a.x_bf16 ? 1 : 0](a, stream);
   return true;
 }
 

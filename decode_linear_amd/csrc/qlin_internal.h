@@ -57,10 +57,14 @@ int fused_chunk_steps(int bits, int mt, int T, int ln, int rows, long K);
 size_t fused_lds_bytes(int bits, int rows, int chunk_steps, long K, int mt);
 
 // One launcher per code width and prologue (qlin_s8_q{4,8}_ln{0,1}.hip).
-hipError_t launch_s8_q4_ln0(const S8Launch& a, hipStream_t s);
-hipError_t launch_s8_q4_ln1(const S8Launch& a, hipStream_t s);
-hipError_t launch_s8_q8_ln0(const S8Launch& a, hipStream_t s);
-hipError_t launch_s8_q8_ln1(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q4_ln0_bf16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q4_ln0_f16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q4_ln1_bf16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q4_ln1_f16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q8_ln0_bf16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q8_ln0_f16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q8_ln1_bf16(const S8Launch& a, hipStream_t s);
+hipError_t launch_s8_q8_ln1_f16(const S8Launch& a, hipStream_t s);
 // The vector-ALU streaming kernel for T <= 4 (qlin_valu.h): S8Launch with MT = activation
 // rows held (1, 2 or 4) and GWM = lanes per weight row (16 or 32).
 hipError_t launch_valu_q4(const S8Launch& a, hipStream_t s);

@@ -46,6 +46,8 @@
 //     so results are bitwise reproducible and no wait can stall.
 #pragma once
 
+#include <type_traits>
+
 #include "qlin_internal.h"
 
 namespace qlin {
@@ -187,6 +189,23 @@ __device__ __forceinline__ uint32_t max8u(uint32_t v) {
 // Max over aligned groups of N lanes (N a power of two, 8..64): DPP moves within 16-lane
 // rows (xor 1, xor 2, the mirrored half-row, the mirrored row), then the gfx950 row swaps
 // (v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two halves).
+// Level L of group_max alone (levels 0-2: max8u's moves; 3: the mirrored row; 4, 5: the row
+// swaps), so that several values can be reduced level by level with independent moves.
+template <int N, int L> __device__ __forceinline__ uint32_t group_max_level(uint32_t v) {
+  if constexpr (L == 0) return max(v, (uint32_t)dpp_i<0xB1>((int)v));
+  else if constexpr (L == 1) return max(v, (uint32_t)dpp_i<0x4E>((int)v));
+  else if constexpr (L == 2) return max(v, (uint32_t)dpp_i<0x141>((int)v));
+  else if constexpr (L == 3) return N >= 16 ? max(v, (uint32_t)dpp_i<0x140>((int)v)) : v;
+  else if constexpr (L == 4) {
+    if constexpr (N < 32) return v;
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+  } else {
+    if constexpr (N < 64) return v;
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+}
 template <int N> __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   static_assert(N >= 8 && N <= 64, "groups of 8..64 lanes");
   v = max8u(v);
@@ -300,7 +319,7 @@ struct Kern {
 // Inverse of the 4-bit k order: the lane group that feeds 16-code run (k >> 4) of a group.
 __device__ __forceinline__ constexpr int kq4(int run) { return run == 0 ? 0 : (run == 1 ? 2 : (run == 2 ? 1 : 3)); }
 
-template <int BITS, bool LN, int MT, int GWM, int R, int W>
+template <int BITS, bool LN, int MT, int GWM, int R, int W, bool XBF>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kernel(
     const void* xt, const void* w0t, const void* s0t, const void* b0t, const void* p1t, const void* p2t,
     const void* p3t, const Tail tail) {
@@ -310,7 +329,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
 
   const uint32_t tx = tag_of(xt), tw = tag_of(w0t);
   const int G = (int)(tx & 0x7FFFu), K = G << 6;
-  const bool xbf = (tx >> 15) != 0;
+  constexpr bool xbf = XBF;   // the activations' dtype (bf16, else fp16) is part of the instantiation
   const int T = (int)(tw & 31u) + 1;
   const int gateup = (int)((tw >> 5) & 1u);
   const int N = (int)(tag_of(s0t) | (tag_of(b0t) << 16));
@@ -491,8 +510,38 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
         const uint32_t h = max((uint32_t)hm[0], (uint32_t)hm[1]);
         m = xbf ? h << 16 : __builtin_bit_cast(uint32_t, f16_lo(h));
       }
-      rmx[u] = group_max<(C::W8 < 64 ? C::W8 : 64)>(m);
-      if ((p % (C::W8 < 64 ? C::W8 : 64)) == 0) rowmax[rho] = rmx[u];
+      if constexpr (W == 8) {
+        rmx[u] = m;
+      } else {
+        rmx[u] = group_max<(C::W8 < 64 ? C::W8 : 64)>(m);
+        rowmax[rho] = rmx[u];
+      }
+    }
+    // the max over each group of min(W8, 64) lanes, level by level over the chunk's pieces (the
+    // moves of one level are independent; 16-wave workgroups, at 128 VGPRs, reduce each piece
+    // as it is formed instead); every lane of a group then holds the group's max, so all of
+    // them store it
+    constexpr int GM = C::W8 < 64 ? C::W8 : 64;
+    auto level = [&](auto L) __attribute__((always_inline)) {
+      if constexpr (W != 8) return;
+#pragma unroll
+      for (int u = 0; u < C::NPX; ++u) {
+        if (C::NCH > 1 && (u % C::UPR) != ch) continue;
+        rmx[u] = group_max_level<GM, decltype(L)::value>(rmx[u]);
+      }
+    };
+    level(std::integral_constant<int, 0>{});
+    level(std::integral_constant<int, 1>{});
+    level(std::integral_constant<int, 2>{});
+    level(std::integral_constant<int, 3>{});
+    level(std::integral_constant<int, 4>{});
+    level(std::integral_constant<int, 5>{});
+    if constexpr (W == 8) {
+#pragma unroll
+      for (int u = 0; u < C::NPX; ++u) {
+        if (C::NCH > 1 && (u % C::UPR) != ch) continue;
+        rowmax[(lane + 64 * u) / C::W8] = rmx[u];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
@@ -687,11 +736,11 @@ namespace qlin {
 namespace s8 {
 
 // Launch of one instantiation (the caller has checked the shape against it).
-template <int BITS, bool LN, int MT, int GWM, int R, int W>
+template <int BITS, bool LN, int MT, int GWM, int R, int W, bool XBF>
 hipError_t launch_one(const S8Launch& a, hipStream_t s) {
   const Tail tail{a.y, a.res, a.add, a.eps, a.y_dtype, a.act};
   auto tp = [](const void* p, uint32_t v) { return reinterpret_cast<const void*>(tag(p, v)); };
-  hipLaunchKernelGGL((s8_kernel<BITS, LN, MT, GWM, R, W>), dim3(a.grid), dim3(a.waves * 64), 0, s,
+  hipLaunchKernelGGL((s8_kernel<BITS, LN, MT, GWM, R, W, XBF>), dim3(a.grid), dim3(a.waves * 64), 0, s,
                      tp(a.x, (uint32_t)(a.K / 64) | ((uint32_t)a.x_bf16 << 15)),
                      tp(a.w0, (uint32_t)(a.T - 1) | ((uint32_t)a.gateup << 5)), tp(a.s0, (uint32_t)a.N & 0xFFFFu),
                      tp(a.b0, (uint32_t)a.N >> 16), tp(a.p1, (uint32_t)a.grid), a.p2, a.p3, tail);
@@ -700,37 +749,40 @@ hipError_t launch_one(const S8Launch& a, hipStream_t s) {
 
 // One tile per workgroup: no ring (a second slot would only carry zeros), and up to 16
 // waves where the shape has that instantiation; more tiles: two slots, up to 8 waves.
-template <int BITS, bool LN, int MT, int GWM>
+template <int BITS, bool LN, int MT, int GWM, bool XBF>
 hipError_t launch_d(const S8Launch& a, hipStream_t s) {
   if (a.waves > 8) {
     if constexpr (wide_ok(BITS, LN, MT, GWM)) {
-      if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 16>(a, s);
+      if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 16, XBF>(a, s);
     }
     return hipErrorInvalidValue;
   }
   if constexpr (max_tiles(BITS, LN, MT, GWM) >= 1) {
-    if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 8>(a, s);
+    if (a.D == 1) return launch_one<BITS, LN, MT, GWM, 1, 8, XBF>(a, s);
   }
   if constexpr (max_tiles(BITS, LN, MT, GWM) >= 2) {
-    if (a.D <= max_tiles(BITS, LN, MT, GWM)) return launch_one<BITS, LN, MT, GWM, 2, 8>(a, s);
+    if (a.D <= max_tiles(BITS, LN, MT, GWM)) return launch_one<BITS, LN, MT, GWM, 2, 8, XBF>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BITS, bool LN>
+// One instantiation unit per (code width, LayerNorm, activation dtype), so that they compile
+// in parallel; a launch whose x_bf16 does not match XBF is refused.
+template <int BITS, bool LN, bool XBF>
 hipError_t launch_bits_ln(const S8Launch& a, hipStream_t s) {
+  if ((a.x_bf16 != 0) != XBF) return hipErrorInvalidValue;
   switch (a.MT * 100 + a.GWM) {
-    case 102: return launch_d<BITS, LN, 1, 2>(a, s);
-    case 104: return launch_d<BITS, LN, 1, 4>(a, s);
-    case 108: return launch_d<BITS, LN, 1, 8>(a, s);
-    case 116: return launch_d<BITS, LN, 1, 16>(a, s);
-    case 132: return launch_d<BITS, LN, 1, 32>(a, s);
-    case 202: return launch_d<BITS, LN, 2, 2>(a, s);
-    case 204: return launch_d<BITS, LN, 2, 4>(a, s);
-    case 208: return launch_d<BITS, LN, 2, 8>(a, s);
-    case 302: return launch_d<BITS, LN, 3, 2>(a, s);
-    case 304: return launch_d<BITS, LN, 3, 4>(a, s);
-    case 902: return launch_d<BITS, LN, 9, 2>(a, s);
+    case 102: return launch_d<BITS, LN, 1, 2, XBF>(a, s);
+    case 104: return launch_d<BITS, LN, 1, 4, XBF>(a, s);
+    case 108: return launch_d<BITS, LN, 1, 8, XBF>(a, s);
+    case 116: return launch_d<BITS, LN, 1, 16, XBF>(a, s);
+    case 132: return launch_d<BITS, LN, 1, 32, XBF>(a, s);
+    case 202: return launch_d<BITS, LN, 2, 2, XBF>(a, s);
+    case 204: return launch_d<BITS, LN, 2, 4, XBF>(a, s);
+    case 208: return launch_d<BITS, LN, 2, 8, XBF>(a, s);
+    case 302: return launch_d<BITS, LN, 3, 2, XBF>(a, s);
+    case 304: return launch_d<BITS, LN, 3, 4, XBF>(a, s);
+    case 902: return launch_d<BITS, LN, 9, 2, XBF>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
