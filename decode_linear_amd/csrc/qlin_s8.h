@@ -363,8 +363,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   // the window (elements 64 g_lo + 8 kp .. + 7), in staging chunk (u mod UPR) when the window
   // has several chunks.  Pieces past the rows in use or past K read zeros.
   u4_t raw[C::NPX];
-  u4_t graw[LN ? C::NPX : 1];
+  // LayerNorm: gamma at each piece's k, and x[rho, 0] (the shift of each piece's row).  When
+  // a row's pieces divide the wave (W8 | 64), every piece of a lane covers the same k: gamma
+  // is loaded and widened once per lane.
+  constexpr bool GSH = LN && (64 % C::W8 == 0);
+  u4_t graw[LN ? (GSH ? 1 : C::NPX) : 1];
+  uint32_t x0r[LN ? C::NPX : 1];
   auto load_pieces = [&](int ch) __attribute__((always_inline)) {
+    if constexpr (GSH) {
+      const int kp = lane % C::W8;
+      graw[0] = *(g_lo + (kp >> 3) < G ? gaddr<u4_t>(gam, (64L * g_lo + 8 * kp) * 2) : zaddr<u4_t>(0));
+    }
 #pragma unroll
     for (int u = 0; u < C::NPX; ++u) {
       if (C::NCH > 1 && (u % C::UPR) != ch) continue;
@@ -378,11 +387,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
         if (rho >= T) { src = rho == T ? (const void*)gam : (const void*)bet; off = k * 2; }
       }
       raw[u] = *(real ? gaddr<u4_t>(src, off) : zaddr<u4_t>(0));
-      if constexpr (LN) graw[u] = *(real ? gaddr<u4_t>(gam, k * 2) : zaddr<u4_t>(0));
+      if constexpr (LN) {
+        if constexpr (!GSH) graw[u] = *(real ? gaddr<u4_t>(gam, k * 2) : zaddr<u4_t>(0));
+        x0r[u] = *(rho < T ? gaddr<uint16_t>(x, (long)rho * K * 2) : zaddr<uint16_t>(0));
+      }
     }
   };
-  uint32_t x0v = 0u;   // LN: x[lane, 0] for lanes < T (the shift of the row's statistics)
-  if constexpr (LN) x0v = *(lane < T ? gaddr<uint16_t>(x, (long)lane * K * 2) : zaddr<uint16_t>(0));
 
   // Tiles: a ring of R slots.  Step q of the workgroup's sequence carries its tile q - z; the
   // z = (R - ntw mod R) mod R leading steps carry zeros: their loads (of zeros) are issued
@@ -438,14 +448,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   // [64, 128).  The lane's partial sums are kept in absolute units: a group's scale and bias
   // are multiplied by 2^-(16 + e) of the lane's operand row in that chunk (an exact power of
   // two) before they scale the group's exact integer dot product.
+  float gms[GSH ? 8 : 1];   // the lane's gamma values (shared by its pieces), widened at the first staging
   auto values = [&](int u, float a[8], float dsh[8]) __attribute__((always_inline)) {
     const int p = lane + 64 * u, rho = p / C::W8;
     widen8(raw[u], xbf, a);
     if constexpr (LN) {
       float gm[8];
-      widen8(graw[u], xbf, gm);
-      const uint32_t x0b = (uint32_t)__shfl((int)x0v, rho < 32 ? rho : 0);
-      const float x0 = elem(x0b & 0xFFFFu, xbf);
+      if constexpr (GSH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[e] = gms[e];
+      } else {
+        widen8(graw[u], xbf, gm);
+      }
+      const float x0 = elem(x0r[u] & 0xFFFFu, xbf);
       const bool xr = rho < T;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -474,6 +489,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   constexpr bool KEEP = LN && MT >= 2;
   float kept[KEEP ? C::NPX : 1][8];
   auto stage = [&](int ch, int base) __attribute__((always_inline)) {
+    if constexpr (GSH) widen8(graw[0], xbf, gms);
     uint32_t rmx[C::NPX];
 #pragma unroll
     for (int u = 0; u < C::NPX; ++u) {
