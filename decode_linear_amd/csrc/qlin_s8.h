@@ -35,7 +35,8 @@
 //       sum_k X_k q_k = 65536 C_hi + 256 C_mid + C_lo + 32896 C_ones    (4-bit),
 //     with 128 * sum_k X_k added for 8-bit codes.  Every product and every sum inside the
 //     MFMA is an exact integer; fp32 rounding enters only per group, where the exact group
-//     dot product is scaled by its fp16 scale times 2^-(16+e), and in the final sums.
+//     dot product is converted and scaled by its fp16 scale, and in the sums (a chunk's sum
+//     is scaled by 2^-(16+e), exactly, before it joins the lane's partial).
 //   * A 16-row MFMA block holds four operand rows: C rows 4r .. 4r + 3 are the three bytes
 //     of operand row r and the ones row, so a lane holds all parts of one (row, column)
 //     and combines them in registers.
@@ -445,9 +446,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
 
   // ---- 2. staging, per chunk ----------------------------------------------------------
   // Each (operand row, chunk) takes its own exponent e: the chunk's max |a| * 2^e lies in
-  // [64, 128).  The lane's partial sums are kept in absolute units: a group's scale and bias
-  // are multiplied by 2^-(16 + e) of the lane's operand row in that chunk (an exact power of
-  // two) before they scale the group's exact integer dot product.
+  // [64, 128).  Within a chunk the lane sums the groups' scaled exact integer dot products
+  // in units of 2^-(16 + e) of its operand row; the chunk's sum is then multiplied by
+  // 2^-(16 + e) (an exact power of two) into the lane's partial in absolute units.
   float gms[GSH ? 8 : 1];   // the lane's gamma values (shared by its pieces), widened at the first staging
   auto values = [&](int u, float a[8], float dsh[8]) __attribute__((always_inline)) {
     const int p = lane + 64 * u, rho = p / C::W8;
@@ -625,8 +626,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
 
   // ---- 3. the tiles --------------------------------------------------------------
   // acc (per block): this lane's partial of (operand row 4 mt + c, column j), absolute units.
-  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot, const float un[MT],
-                        float acc[MT]) __attribute__((always_inline)) {
+  // accc: the chunk's sums in units of 2^-(16 + e) (the chunk's exponent); chunk_step scales
+  // them to absolute units once (an exact power of two).
+  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot,
+                        float accc[MT]) __attribute__((always_inline)) {
     const i4_t bop = Kx::operand_b(d, gg);
     // scale and bias of group gg for column j: dword gg/2 of the lane's scales (biases), half gg&1
     const uint32_t sw = r.sb[gg >> 1];
@@ -638,9 +641,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const i4_t cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[slot][mt], bop, (i4_t){0, 0, 0, 0}, 0, 0, 0);
-      const float cf = fmaf((float)cc[0], 65536.0f, fmaf((float)cc[1], 256.0f, fmaf((float)cc[3], 32896.0f, (float)cc[2])));
-      acc[mt] = fmaf(s * un[mt], cf, acc[mt]);
-      acc[mt] = fmaf(bb * un[mt], gxf[slot][mt], acc[mt]);
+      // sum X q = 65536 C_hi + 256 C_mid + C_lo + 32896 C_ones: two exact integer parts
+      // (|C| < 2^21 for every part), one rounding each, one fma
+      const int t1 = cc[0] * 256 + cc[1];
+      const int t2 = cc[2] + 32896 * cc[3];
+      const float cf = fmaf((float)t1, 256.0f, (float)t2);
+      accc[mt] = fmaf(s, cf, accc[mt]);
+      accc[mt] = fmaf(bb, gxf[slot][mt], accc[mt]);
     }
   };
   // the code dword set of group gg (4-bit: exchange lane halves once per step)
@@ -656,13 +663,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   };
   // the groups of chunk ch of one tile, fragments from slots [base, base + CG)
   auto chunk_step = [&](const typename Kx::TileRegs& r, int ch, int base, float acc[MT]) __attribute__((always_inline)) {
+    float accc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) accc[mt] = 0.0f;
 #pragma unroll
     for (int q = 0; q < C::CG; q += (BITS == 4 ? 2 : 1)) {
       const int gg = ch * C::CG + q;
       const u4_t dd = codes_of(r, gg);
-      group_step(r, dd, gg, base + q, unit[ch], acc);
-      if constexpr (BITS == 4) group_step(r, dd, gg + 1, base + q + 1, unit[ch], acc);
+      group_step(r, dd, gg, base + q, accc);
+      if constexpr (BITS == 4) group_step(r, dd, gg + 1, base + q + 1, accc);
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = fmaf(unit[ch][mt], accc[mt], acc[mt]);
   };
   auto put_partial = [&](int i, const float acc[MT]) __attribute__((always_inline)) {
 #pragma unroll
