@@ -627,10 +627,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
   // ---- 3. the tiles --------------------------------------------------------------
   // acc (per block): this lane's partial of (operand row 4 mt + c, column j), absolute units.
   // accc: the chunk's sums in units of 2^-(16 + e) (the chunk's exponent); chunk_step scales
-  // them to absolute units once (an exact power of two).
-  auto group_step = [&](const typename Kx::TileRegs& r, const u4_t& d, int gg, int slot,
-                        float accc[MT]) __attribute__((always_inline)) {
+  // them to absolute units once (an exact power of two).  A group's products come from
+  // group_mfma; group_sum folds them in (split so that a pair of groups issues its MFMAs
+  // before either result is read, which hides the MFMA latency).
+  auto group_mfma = [&](const u4_t& d, int gg, int slot, i4_t cc[MT]) __attribute__((always_inline)) {
     const i4_t bop = Kx::operand_b(d, gg);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      cc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[slot][mt], bop, (i4_t){0, 0, 0, 0}, 0, 0, 0);
+  };
+  auto group_sum = [&](const typename Kx::TileRegs& r, int gg, int slot, const i4_t cc[MT],
+                       float accc[MT]) __attribute__((always_inline)) {
     // scale and bias of group gg for column j: dword gg/2 of the lane's scales (biases), half gg&1
     const uint32_t sw = r.sb[gg >> 1];
     const auto sbp = __builtin_amdgcn_permlane16_swap(sw, sw, false, false);
@@ -640,11 +647,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
     const float bb = BITS == 8 ? fmaf(128.0f, s, b) : b;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const i4_t cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[slot][mt], bop, (i4_t){0, 0, 0, 0}, 0, 0, 0);
       // sum X q = 65536 C_hi + 256 C_mid + C_lo + 32896 C_ones: two exact integer parts
-      // (|C| < 2^21 for every part), one rounding each, one fma
-      const int t1 = cc[0] * 256 + cc[1];
-      const int t2 = cc[2] + 32896 * cc[3];
+      // (|C| < 2^21 for every part, |C_ones| <= 8192), one rounding each, one fma
+      const int t1 = cc[mt][0] * 256 + cc[mt][1];
+      const int t2 = cc[mt][2] + __mul24(cc[mt][3], 32896);
       const float cf = fmaf((float)t1, 256.0f, (float)t2);
       accc[mt] = fmaf(s, cf, accc[mt]);
       accc[mt] = fmaf(bb, gxf[slot][mt], accc[mt]);
@@ -667,11 +673,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) accc[mt] = 0.0f;
 #pragma unroll
-    for (int q = 0; q < C::CG; q += (BITS == 4 ? 2 : 1)) {
+    for (int q = 0; q < C::CG; q += 2) {   // CG is even (2 .. 8)
       const int gg = ch * C::CG + q;
-      const u4_t dd = codes_of(r, gg);
-      group_step(r, dd, gg, base + q, accc);
-      if constexpr (BITS == 4) group_step(r, dd, gg + 1, base + q + 1, accc);
+      i4_t c0[MT], c1[MT];
+      if constexpr (BITS == 4) {   // one step holds both groups
+        const u4_t dd = codes_of(r, gg);
+        group_mfma(dd, gg, base + q, c0);
+        group_mfma(dd, gg + 1, base + q + 1, c1);
+      } else {
+        group_mfma(codes_of(r, gg), gg, base + q, c0);
+        group_mfma(codes_of(r, gg + 1), gg + 1, base + q + 1, c1);
+      }
+      group_sum(r, gg, base + q, c0, accc);
+      group_sum(r, gg + 1, base + q + 1, c1, accc);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = fmaf(unit[ch][mt], accc[mt], acc[mt]);
