@@ -712,6 +712,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
           put_partial(q - z, acc);
         }
         issue_tile(tr[r], tile_of(q + R));
+        // Two waves share each SIMD and the older one wins issue: left alone it runs ahead,
+        // its loads go out earlier, and at the end it waits for the younger at the merge
+        // (about 2 us on the SwiGLU shape).  A workgroup barrier per step (no memory wait;
+        // every wave runs the same steps) keeps the waves in step where there are many steps.
+        if constexpr (W == 8) {
+          if (nq >= 4) __builtin_amdgcn_s_barrier();
+        }
       }
     }
   } else {
