@@ -59,25 +59,46 @@ __device__ __forceinline__ uint64_t candidate(float s, uint32_t i) {
   return ((uint64_t)r << 32) | (uint64_t)(~i);
 }
 
-// Inclusive prefix sum over the 64 lanes (lane l: sum of lanes 0..l).
-__device__ __forceinline__ uint32_t wave_prefix(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_up((int)v, d, 64);
-    v += lane >= d ? o : 0u;
-  }
-  return v;
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  // lanes whose source is outside the row read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-// Maximum of a 64-bit word over the wave (every lane ends with it).
-__device__ __forceinline__ uint64_t wave_max64(uint64_t w) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(w >> 32), d, 64);
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)w, d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    w = o > w ? o : w;
+__device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+// Inclusive prefix sum over the 64 lanes (lane l: sum of lanes 0..l): a scan within each
+// 16-lane row by DPP row shifts (1, 2, 4, 8), then each row adds the totals of the rows
+// before it, read from their last lanes (no LDS round trip).
+__device__ __forceinline__ uint32_t wave_prefix(uint32_t v, int lane) {
+  v += dpp_u<0x111>(v);   // row_shr:1
+  v += dpp_u<0x112>(v);   // row_shr:2
+  v += dpp_u<0x114>(v);   // row_shr:4
+  v += dpp_u<0x118>(v);   // row_shr:8
+  const uint32_t r0 = lane_u(v, 15), r1 = lane_u(v, 31), r2 = lane_u(v, 47);
+  return v + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+}
+// Maximum of a 64-bit word over the wave (every lane ends with it): butterflies within each
+// 16-lane row (xor 1, 2, 4, 8 by DPP), then the four rows' maxima read from lanes 0, 16, 32
+// and 48.  A maximum is exact in any order.
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t w) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(w >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)w, CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max64(uint64_t w, int lane) {
+  w = max64(w, dpp64<0xB1>(w));   // quad_perm [1, 0, 3, 2]: xor 1
+  w = max64(w, dpp64<0x4E>(w));   // quad_perm [2, 3, 0, 1]: xor 2
+  {
+    const uint64_t dn = dpp64<0x114>(w), up = dpp64<0x104>(w);   // row_shr:4, row_shl:4
+    w = max64(w, (lane & 4) ? dn : up);                          // xor 4
   }
-  return w;
+  w = max64(w, dpp64<0x128>(w));  // row_ror:8: xor 8
+  const uint32_t hi = (uint32_t)(w >> 32), lo = (uint32_t)w;
+  uint64_t m = ((uint64_t)lane_u(hi, 0) << 32) | lane_u(lo, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) m = max64(m, ((uint64_t)lane_u(hi, 16 * r) << 32) | lane_u(lo, 16 * r));
+  return m;
 }
 
 template <int LD>
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
       best = c > best ? c : best;
     }
   }
-  best = wave_max64(best);
+  best = wave_max64(best, lane);
   if (lane == 0) wave_best[wv] = best;
   __syncthreads();
   if (t == 0) {
