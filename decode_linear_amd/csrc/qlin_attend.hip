@@ -42,16 +42,37 @@ __device__ __forceinline__ void widen8(const u4_t v, int dtype, float f[8]) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+// Butterflies over the wave without LDS: v op v[lane ^ 2^B] for B = 0 .. 5 (DPP quad
+// permutes, a row shift pair, a row rotation, then the gfx950 row swaps, which return both
+// rows of a pair); op is commutative, so both lanes of every pair get the same value.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX> __device__ __forceinline__ float wave_all(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f<0xB1>(v));                                     // xor 1
+  v = op(v, dpp_f<0x4E>(v));                                     // xor 2
+  {
+    const float dn = dpp_f<0x114>(v), up = dpp_f<0x104>(v);      // row_shr:4, row_shl:4
+    v = op(v, (threadIdx.x & 4) ? dn : up);                      // xor 4
+  }
+  v = op(v, dpp_f<0x128>(v));                                    // row_ror:8: xor 8
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = op(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));   // xor 16
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = op(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));   // xor 32
+  }
   return v;
 }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+__device__ __forceinline__ float wave_max(float v) { return wave_all<true>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_all<false>(v); }
+// The value of the lane across the halves (lane ^ 32).
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, (int)((threadIdx.x & 32) ? r[0] : r[1]));
 }
 
 // One RNE rounding of an fp32 value to the output dtype.
@@ -130,7 +151,7 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
     }
   }
   // lanes j and j + 32 swap halves: both hold the key's whole dot product, in one order
-  const float other = __shfl_xor(dot, 32);
+  const float other = other_half(dot);
   const float full = half == 0 ? dot + other : other + dot;
   const float s = j <= pos ? full * a.scale : -__builtin_inff();
   const float m = wave_max(s);
