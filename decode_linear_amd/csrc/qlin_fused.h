@@ -269,18 +269,6 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return e > 126 ? 126 : (e < -126 ? -126 : e);
 }
 
-// Wave-wide fixed-order reductions (xor butterfly over all 64 lanes).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-
 // Unpack a 16-byte piece of 8 16-bit elements.
 __device__ __forceinline__ void unpack8(const u4_t raw, int dtype, float v[8]) {
 #pragma unroll
