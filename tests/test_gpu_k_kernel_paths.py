@@ -39,6 +39,17 @@ def _s8_launches(fn):
     return qlin_dispatch_count(8) - before
 
 
+@pytest.mark.parametrize("x_dtype,K,N", [(synth.F16, 4096, 14336), (synth.F16, 4096, 7176), (synth.BF16, 512, 14336)])
+def test_many_tile_ring(x_dtype, K, N):
+    """Workgroups of several tiles on the int8 kernel's ring.  N = 14336 gives 1792 gate/up
+    tiles, 7 per workgroup: an odd count, so the ring starts with a zero step whose
+    arithmetic is skipped.  N = 7176 gives 897 tiles, 4 per workgroup and 1 in the last
+    (which alone takes a zero step).  K = 4096 runs 8 waves, which meet at a barrier per
+    step in workgroups of four or more steps; K = 512 runs 4 waves, without the barrier."""
+    case = synth.random_gateup(9500 + K + N + x_dtype, 4, K, N, 4, x_dtype=x_dtype)
+    assert _s8_launches(lambda: run_gateup_case(case)) == 2   # fp32 and narrow outputs
+
+
 @pytest.mark.parametrize("kind,expect", [
     ("q4-T4", True), ("q8-T4-ln", True), ("q4-T32-ln", True), ("q8-K16384", True),
     ("gateup-q4", True), ("gateup-q4-ln", False), ("dense-f16", False), ("q4-K192", False)])
