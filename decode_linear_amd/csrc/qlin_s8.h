@@ -318,7 +318,8 @@ struct Kern {
 };
 
 // Inverse of the 4-bit k order: the lane group that feeds 16-code run (k >> 4) of a group.
-__device__ __forceinline__ constexpr int kq4(int run) { return run == 0 ? 0 : (run == 1 ? 2 : (run == 2 ? 1 : 3)); }
+// (0, 1, 2, 3 -> 0, 2, 1, 3: the two bits swapped, in arithmetic so that no branch is made of it)
+__device__ __forceinline__ constexpr int kq4(int run) { return ((run & 1) << 1) | ((run >> 1) & 1); }
 
 template <int BITS, bool LN, int MT, int GWM, int R, int W, bool XBF>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kernel(
@@ -581,7 +582,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
       } else {
         values(u, a, dsh);
       }
-      const int ex = 16 + row_exp(rmx[u]);
+      // a row max reduced over the whole wave is uniform: its exponent is scalar work
+      const uint32_t rm = (C::W8 >= 64) ? (uint32_t)__builtin_amdgcn_readfirstlane((int)rmx[u]) : rmx[u];
+      const int ex = 16 + row_exp(rm);
       int X[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) X[e] = (int)__builtin_amdgcn_ldexpf(a[e], ex);
@@ -747,13 +750,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, W * 64))) void s8_kerne
     const int tile = (int)blockIdx.x + i * grid;
     const int n = gateup ? tile * 8 + jj : tile * 16 + jj;
     if (n >= N) continue;
-    auto merged = [&](int rho, int col) __attribute__((always_inline)) {
+    // the waves' partials in wave order; the loops run over the instantiation's W waves (the
+    // reads are all in the partials' LDS), and a wave past the launch's adds zero
+    auto read_parts = [&](int rho, int col, float pw[W]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) pw[w] = parts[((i * W + w) * MT + (rho >> 2)) * 64 + (rho & 3) * 16 + col];
+    };
+    auto sum_parts = [&](const float pw[W]) __attribute__((always_inline)) {
       float v = 0.0f;
-      for (int w = 0; w < waves; ++w) v += parts[((i * W + w) * MT + (rho >> 2)) * 64 + (rho & 3) * 16 + col];
+#pragma unroll
+      for (int w = 0; w < W; ++w) v += w < waves ? pw[w] : 0.0f;
       return v;
     };
-    float v = merged(t, jj);
-    float u = gateup ? merged(t, jj + 8) : 0.0f;
+    auto merged = [&](int rho, int col) __attribute__((always_inline)) {
+      float pw[W];
+      read_parts(rho, col, pw);
+      return sum_parts(pw);
+    };
+    // the gate and up rows' partials are read together, on every path (the empty asm takes
+    // the up values, so that the compiler cannot sink their reads into the gate/up branch)
+    float pv[W], pu[W];
+    read_parts(t, jj, pv);
+    read_parts(t, gateup ? jj + 8 : jj, pu);
+#pragma unroll
+    for (int w = 0; w < W; ++w) asm volatile("" ::"v"(pu[w]));
+    float v = sum_parts(pv);
+    float u = gateup ? sum_parts(pu) : 0.0f;
     if constexpr (LN) {
       float s1 = 0.0f, s2 = 0.0f;
       for (int w = 0; w < waves; ++w) {
