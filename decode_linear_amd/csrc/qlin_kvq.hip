@@ -140,7 +140,7 @@ template <int LO, int N> __device__ __forceinline__ int scatter_base(int lane) {
 // One workgroup per (block g, KV head c, chunk z of QC query heads sharing c): the block's
 // rows of c are read once for all QC heads (each key slice's dot product is taken against
 // every head's query, and each value is decoded once and added to every head's accumulator).
-template <int BITS, int D, int QC, int SBT>
+template <int BITS, int D, int QC, int SBT, int QT>
 __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
   constexpr int P = 2;                  // steps whose rows are in flight at once
   constexpr int RB = D * BITS / 8;      // bytes of a row of codes
@@ -178,13 +178,13 @@ __global__ __launch_bounds__(kKvqThreads) void block_kernel(const KvqParams a) {
       for (int u = 0; u < EL / 8; ++u) {
         const u4_t w = reinterpret_cast<const u4_t*>(q16 + (long)(h0 + i) * D + j * EL)[u];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[i][8 * u + e] = half_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, a.q_dtype);
+        for (int e = 0; e < 8; ++e) qv[i][8 * u + e] = half_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, QT);
       }
   } else {
 #pragma unroll
     for (int i = 0; i < QC; ++i)
 #pragma unroll
-      for (int e = 0; e < EL; ++e) qv[i][e] = half_to_float(q16[(long)(h0 + i) * D + j * EL + e], a.q_dtype);
+      for (int e = 0; e < EL; ++e) qv[i][e] = half_to_float(q16[(long)(h0 + i) * D + j * EL + e], QT);
   }
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
@@ -418,25 +418,32 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const KvqParams a)
   }
 }
 
-template <int BITS, int QC, int SBT>
+template <int BITS, int QC, int SBT, int QT>
 hipError_t launch_block_qc(const KvqParams& a, hipStream_t s) {
   const dim3 grid(a.G, a.KV, (a.H / a.KV) / QC);
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512, QC, SBT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((block_kernel<BITS, 64, QC, SBT, QT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((block_kernel<BITS, 128, QC, SBT, QT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((block_kernel<BITS, 256, QC, SBT, QT>), grid, dim3(kKvqThreads), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((block_kernel<BITS, 512, QC, SBT, QT>), grid, dim3(kKvqThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Query heads per workgroup: two where the heads sharing a KV head pair up, else one.
+// Query heads per workgroup: two where the heads sharing a KV head pair up, else one.  The
+// query's dtype is part of the instantiation (with it a runtime flag, every query element
+// was widened both ways and one result selected: about 260 of a wave's 1,740 vector
+// instructions; 13.75 -> 13.56 us on the 16-head, 8192-row call).
+template <int BITS, int SBT>
+hipError_t launch_block_sb(const KvqParams& a, hipStream_t s) {
+  const bool pair = (a.H / a.KV) % 2 == 0;
+  if (a.q_dtype == 1) return pair ? launch_block_qc<BITS, 2, SBT, 1>(a, s) : launch_block_qc<BITS, 1, SBT, 1>(a, s);
+  return pair ? launch_block_qc<BITS, 2, SBT, 2>(a, s) : launch_block_qc<BITS, 1, SBT, 2>(a, s);
+}
 template <int BITS>
 hipError_t launch_block(const KvqParams& a, hipStream_t s) {
-  const bool pair = (a.H / a.KV) % 2 == 0;
-  if (a.sb_dtype == 1) return pair ? launch_block_qc<BITS, 2, 1>(a, s) : launch_block_qc<BITS, 1, 1>(a, s);
-  return pair ? launch_block_qc<BITS, 2, 2>(a, s) : launch_block_qc<BITS, 1, 2>(a, s);
+  return a.sb_dtype == 1 ? launch_block_sb<BITS, 1>(a, s) : launch_block_sb<BITS, 2>(a, s);
 }
 
 }  // namespace
