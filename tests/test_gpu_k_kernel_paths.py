@@ -50,6 +50,21 @@ def test_many_tile_ring(x_dtype, K, N):
     assert _s8_launches(lambda: run_gateup_case(case)) == 2   # fp32 and narrow outputs
 
 
+@pytest.mark.parametrize("bits,ln", [(4, False), (8, True)])
+def test_many_tile_ring_ragged_n(bits, ln):
+    """Several tiles per workgroup with a partial last tile: N = 8197 makes 513 tiles of 16
+    rows (3 per workgroup on a ring of two), the last holding 5 rows; the ring clamps the
+    missing rows' loads to the matrix's last row and never stores them."""
+    case = synth.random_case(9600 + bits + ln, 4, 256, 8197, bits, x_dtype=synth.BF16, ln=ln, add=True)
+    assert _s8_launches(lambda: run_linear_case(case, y_dtypes=(synth.BF16,))) == 2
+
+
+def test_many_tile_ring_ragged_gateup():
+    """The gate/up form of the same: N = 4099 per projection makes 513 tiles of 8 + 8 rows."""
+    case = synth.random_gateup(9610, 4, 512, 4099, 4)
+    assert _s8_launches(lambda: run_gateup_case(case)) == 2
+
+
 @pytest.mark.parametrize("kind,expect", [
     ("q4-T4", True), ("q8-T4-ln", True), ("q4-T32-ln", True), ("q8-K16384", True),
     ("gateup-q4", True), ("gateup-q4-ln", False), ("dense-f16", False), ("q4-K192", False)])
