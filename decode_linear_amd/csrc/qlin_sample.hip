@@ -13,10 +13,11 @@
 //   out       the prefix rows, then (with a table) the code's row of the table (zeros for -1)
 //
 // Mapping: one workgroup of 256 threads; thread t keeps the ranks of codes t, t + 256, ... in
-// registers (n <= 8192).  Radix pass: each wave counts the digits of its matching ranks into
-// its own 256-bin LDS histogram (LDS integer atomics, private to the wave), then all 256
-// threads take one digit each, highest digit first, add the four waves' counts and run one
-// prefix sum over the workgroup; the thread whose digit holds the wanted rank publishes it.
+// registers (PER of them: 8, 16 or 32, the fewest that hold n <= 8192).  Radix pass: each
+// wave counts the digits of its matching ranks into its own 256-bin LDS histogram (LDS
+// integer atomics, private to the wave), then all 256 threads take one digit each, highest
+// digit first, add the four waves' counts and run one prefix sum over the workgroup; the
+// thread whose digit holds the wanted rank publishes it.
 // Gumbel-max: every candidate becomes one 64-bit word, (rank of the score) << 32 | ~index, so
 // the winner is the plain maximum of the words (an exact, order-free reduction: the result
 // does not depend on the order of the combines).
@@ -31,7 +32,7 @@ namespace {
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 constexpr int kThr = 256;                     // threads of the workgroup
 constexpr int kWv = kThr / 64;                // its waves
-constexpr int kPer = kSampleMaxCodes / kThr;  // ranks per thread
+constexpr int kPerMax = kSampleMaxCodes / kThr;  // ranks per thread, at most
 
 __device__ __forceinline__ uint32_t rank_of(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -101,9 +102,10 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t w, int lane) {
   return m;
 }
 
-template <int LD>
+template <int LD, int PER>
 __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
 #pragma clang fp contract(off)
+  static_assert(PER >= 1 && PER <= kPerMax, "ranks per thread");
   __shared__ uint32_t counts[kWv][256];   // one digit histogram per wave
   __shared__ uint32_t wave_total[kWv];
   __shared__ uint32_t sel_digits, sel_left;   // the selected high digits, and ranks still wanted
@@ -132,16 +134,16 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
 
   // Every logit and noise value of this thread is loaded before any is used (indices past n
   // read element n - 1 and are masked), so the selection waits for one round of loads.
-  uint32_t rk[kPer];
-  float gm[kPer];
+  uint32_t rk[PER];
+  float gm[PER];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int i = min(t + kThr * e, n - 1);
     rk[e] = logit_bits<LD>(a.logits, i);
     gm[e] = a.gumbel[i];
   }
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) rk[e] = t + kThr * e < n ? rank_of(logit_value<LD>(rk[e])) : 0u;
+  for (int e = 0; e < PER; ++e) rk[e] = t + kThr * e < n ? rank_of(logit_value<LD>(rk[e])) : 0u;
 
   // ---- theta: four 8-bit digits, most significant first ----------------------------------
   uint32_t digits = 0u, left = (uint32_t)a.top_k;   // chosen so far (uniform), ranks wanted
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
     for (int w = 0; w < kWv; ++w) counts[w][t] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
+    for (int e = 0; e < PER; ++e) {
       const int i = t + kThr * e;
       const bool on_path = pass == 0 || (rk[e] >> (sh + 8)) == digits;
       if (i < n && on_path) atomicAdd(&counts[wv][(rk[e] >> sh) & 0xFFu], 1u);
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
   // ---- Gumbel-max over the kept codes ------------------------------------------------------
   uint64_t best = 0ull;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int i = t + kThr * e;
     if (i < n && rk[e] >= theta) {
       const float scaled = logit_of(rk[e]) * a.inv_temp;   // one fp32 rounding
@@ -213,12 +215,21 @@ __global__ __launch_bounds__(kThr) void sample_kernel(const SampleParams a) {
   }
 }
 
+// Ranks per thread: the fewest of 8, 16 and 32 that hold n (with 32 for every n, a call of
+// 2048 codes ran 4 x the loads and loop trips it needed: 10.16 -> 6.65 us).
+template <int LD>
+void launch_ld(const SampleParams& a, hipStream_t s) {
+  if (a.n <= 8 * kThr) hipLaunchKernelGGL((sample_kernel<LD, 8>), dim3(1), dim3(kThr), 0, s, a);
+  else if (a.n <= 16 * kThr) hipLaunchKernelGGL((sample_kernel<LD, 16>), dim3(1), dim3(kThr), 0, s, a);
+  else hipLaunchKernelGGL((sample_kernel<LD, kPerMax>), dim3(1), dim3(kThr), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_sample(const SampleParams& a, hipStream_t s) {
-  if (a.logit_dtype == 0) hipLaunchKernelGGL(sample_kernel<0>, dim3(1), dim3(kThr), 0, s, a);
-  else if (a.logit_dtype == 1) hipLaunchKernelGGL(sample_kernel<1>, dim3(1), dim3(kThr), 0, s, a);
-  else hipLaunchKernelGGL(sample_kernel<2>, dim3(1), dim3(kThr), 0, s, a);
+  if (a.logit_dtype == 0) launch_ld<0>(a, s);
+  else if (a.logit_dtype == 1) launch_ld<1>(a, s);
+  else launch_ld<2>(a, s);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ def _run(case, level, inv_temp, top_k, embed=True, in_place=False):
         assert np.array_equal(_host(out, case.emb_dtype), ref_out.view(_host(out, case.emb_dtype).dtype))
 
 
-@pytest.mark.parametrize("n", [1, 7, 1000, 2048, 8192])
+@pytest.mark.parametrize("n", [1, 7, 1000, 2048, 2049, 4096, 4097, 8192])
 @pytest.mark.parametrize("kfrac", [0.0, 0.05, 1.0])
 def test_sample_sizes(n, kfrac):
     case = synth.sample_case(10 + n, n, 64, 3)
