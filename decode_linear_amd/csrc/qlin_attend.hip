@@ -90,6 +90,10 @@ __device__ __forceinline__ void store_elem(void* y, int dtype, long idx, float v
   }
 }
 
+// DT, the dtype of qkv and kv (1 fp16, 2 bf16), is part of the instantiation: as a runtime
+// flag every element was widened both ways and one result selected (6.49 -> 5.41 us on the
+// 16-head, 24 + 8 position band).
+template <int DT>
 __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
   const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
   const int H = a.H, HD = a.HD, P = a.P, T = a.T;
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
     for (int u = 0; u < 4; ++u) {
       if (b + u >= hp) break;
       float qf[8], kf[8];
-      widen8(qw[u], a.dtype, qf);
-      widen8(kw[u], a.dtype, kf);
+      widen8(qw[u], DT, qf);
+      widen8(kw[u], DT, kf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(qf[e], kf[e], dot);
     }
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
 #pragma unroll
     for (int jj = 0; jj < kAttendKeys; ++jj) {
       const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), jj));
-      o = jj <= pos ? fmaf(pj, bits_to_float(vv[jj], a.dtype), o) : o;
+      o = jj <= pos ? fmaf(pj, bits_to_float(vv[jj], DT), o) : o;
     }
     store_elem(a.out, a.out_dtype, row * D + (long)h * HD + d, o);
   }
@@ -184,7 +188,8 @@ __global__ __launch_bounds__(64) void attend_kernel(const AttendParams a) {
 }  // namespace
 
 hipError_t launch_attend(const AttendParams& a, hipStream_t s) {
-  hipLaunchKernelGGL(attend_kernel, dim3(a.H, a.T), dim3(64), 0, s, a);
+  if (a.dtype == 1) hipLaunchKernelGGL(attend_kernel<1>, dim3(a.H, a.T), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(attend_kernel<2>, dim3(a.H, a.T), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
