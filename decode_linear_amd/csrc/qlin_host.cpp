@@ -571,10 +571,10 @@ qlin_status qlin_sample(const void* logits, qlin_dtype logit_dtype, int32_t n, c
 }
 
 namespace {
-// Rows per block of the quantized-KV decode: 128 (a workgroup per 128 rows and head, so
-// that a decode step has thousands of waves), 512 once the blocks of all heads would pass
-// 8192 per head (bounding the workspace at large n_rows).
-int kvq_block(int32_t n_rows) { return n_rows <= 128 * 8192 ? 128 : 512; }
+// Rows per block of the quantized-KV decode: 256 (a workgroup of eight waves per 256 rows
+// and head pair), 512 once the blocks would pass 8192 per head (bounding the workspace at
+// large n_rows).
+int kvq_block(int32_t n_rows) { return n_rows <= 256 * 8192 ? 256 : 512; }
 }  // namespace
 
 int64_t qlin_kvq_decode_workspace(int32_t heads, int32_t n_rows, int32_t head_dim) {

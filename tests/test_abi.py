@@ -299,8 +299,9 @@ def test_sample_validation(q):
 
 def test_kvq_validation(q):
     f, ws = q.lib().qlin_kvq_decode, q.lib().qlin_kvq_decode_workspace
-    assert ws(16, 8192, 256) == 16 * 64 * 258 * 4 and ws(2, 100, 128) == 2 * 1 * 130 * 4 and ws(0, 1, 64) == 0
-    assert ws(1, 128 * 8192 + 1, 64) == 1 * 2049 * 66 * 4
+    # blocks of 256 rows up to 256 * 8192 rows, of 512 past that
+    assert ws(16, 8192, 256) == 16 * 32 * 258 * 4 and ws(2, 100, 128) == 2 * 1 * 130 * 4 and ws(0, 1, 64) == 0
+    assert ws(1, 256 * 8192, 64) == 1 * 8192 * 66 * 4 and ws(1, 256 * 8192 + 1, 64) == 1 * 4097 * 66 * 4
     Q, KC, KS, KB, VC, VS, VB, WS, O = (0x9000000 + 0x1000000 * i for i in range(9))
     ok = dict(q=Q, qdt=q.QLIN_BF16, H=16, KV=8, N=8192, D=256, GS=64, bits=4, kc=KC, ks=KS, kb=KB, vc=VC, vs=VS,
               vb=VB, sbdt=q.QLIN_BF16, ws=WS, wsb=ws(16, 8192, 256), out=O, odt=q.QLIN_BF16)
@@ -338,12 +339,12 @@ def test_kvq_noalloc_validation(q):
     assert call(qdt=q.QLIN_F32) == -3 and call(bits=2) == -4 and call(H=12) == -2 and call(D=96) == -2
     assert call(q=Q + 1) == -5 and call(out=O + 1) == -5
     assert call(out=KC + 64) == -7
-    # 64 heads x 512 blocks of 128 rows x (128 + 2) floats = 17 MB of partials: too much
+    # 64 heads x 256 blocks of 256 rows x (128 + 2) floats = 8.5 MB of partials: too much
     assert ws(64, 65536, 128) > q.QLIN_KVQ_SCRATCH_BYTES
     assert call(H=64, KV=8, N=65536, D=128) == -8
-    # the largest heads x rows that still fit, just past it
-    assert ws(32, 64 * 128, 256) <= q.QLIN_KVQ_SCRATCH_BYTES < ws(32, 64 * 128 * 4, 256)
-    assert call(H=32, KV=8, N=64 * 128 * 4, D=256) == -8
+    # 32 heads of 256: 254 blocks of 256 rows still fit, one more row does not
+    assert ws(32, 254 * 256, 256) <= q.QLIN_KVQ_SCRATCH_BYTES < ws(32, 254 * 256 + 1, 256)
+    assert call(H=32, KV=8, N=254 * 256 + 1, D=256) == -8
 
 
 def test_merge_report_entry_points_validate(q):

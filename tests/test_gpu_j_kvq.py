@@ -1,7 +1,7 @@
 """GPU parity of qlin_kvq_decode (one query position per head over a quantized K/V cache)
 against the oracle: the fp32 output under Gate A, the 16-bit output equal to RNE of the fp32
 output (Gate B), across bits, group sizes, head dims, row counts (one block, several blocks,
-ragged last blocks, the 512-row blocks past 2^20 rows, the merge's 256-block and 4096-block
+ragged last blocks, the 512-row blocks past 2^21 rows, the merge's 256-block and 4096-block
 boundaries) and query/KV head sharing."""
 import numpy as np
 import pytest
@@ -45,7 +45,7 @@ def test_kvq_formats(bits, GS, D):
     _run(synth.kvq_case(600 + bits + GS + D, 2, 1, 77, D, GS, bits))
 
 
-@pytest.mark.parametrize("N", [1, 2, 5, 127, 128, 129, 2048, 2049, 5000])
+@pytest.mark.parametrize("N", [1, 2, 5, 127, 128, 129, 255, 256, 257, 2048, 2049, 5000])
 def test_kvq_rows(N):
     _run(synth.kvq_case(700 + N, 4, 2, N, 128, 64, 4), out16=N < 3000)
 
@@ -86,11 +86,11 @@ def test_kvq_rejects_small_workspace():
 
 
 def test_kvq_large_blocks_past_a_million_rows():
-    # past 128 * 8192 rows the blocks grow to 512 rows
-    _run(synth.kvq_case(990, 1, 1, 128 * 8192 + 5, 64, 64, 4), out16=False)
+    # past 256 * 8192 rows the blocks grow to 512 rows
+    _run(synth.kvq_case(990, 1, 1, 256 * 8192 + 5, 64, 64, 4), out16=False)
 
 
-@pytest.mark.parametrize("N", [128 * 256, 128 * 256 + 1])
+@pytest.mark.parametrize("N", [256 * 256, 256 * 256 + 1])
 def test_kvq_merge_statistics_at_256_blocks(N):
     # up to 256 blocks every merge thread holds one block's statistics; past that it loops
     _run(synth.kvq_case(992 + N % 2, 2, 1, N, 64, 64, 4), out16=False)

@@ -33,8 +33,8 @@ def _inputs(c):
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_noalloc_matches_workspace_entry_point(out_dtype):
     from decode_linear_amd import qlin_dispatch_count, qlin_kvq_decode, qlin_kvq_decode_noalloc
-    big = synth.kvq_workload()                               # 16 heads, 8192 rows: 64 blocks per head
-    small = synth.kvq_case(1201, 4, 2, 300, 128, 64, 8)      # 3 blocks per head, another head dim
+    big = synth.kvq_workload()                               # 16 heads, 8192 rows: 32 blocks per head
+    small = synth.kvq_case(1201, 4, 2, 300, 128, 64, 8)      # 2 blocks per head, another head dim
     for c in (big, small):
         print(f"noalloc case {c.name} out {out_dtype}", flush=True)
         q, k, v = _inputs(c)
@@ -54,7 +54,7 @@ def test_noalloc_matches_workspace_entry_point(out_dtype):
 
 def test_noalloc_rejects_oversize_before_launch():
     from decode_linear_amd import QlinError, qlin_dispatch_count, qlin_kvq_decode_noalloc
-    # 64 heads over 65536 rows of 128: 512 blocks per head, 17 MB of partials
+    # 64 heads over 65536 rows of 128: 256 blocks of 256 rows per head, 8.5 MB of partials
     H, KV, N, D = 64, 8, 65536, 128
     q = torch.zeros((H, D), dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros((KV, N, D * 4 // 32), dtype=torch.int32, device="cuda")
