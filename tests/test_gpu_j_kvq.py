@@ -55,6 +55,15 @@ def test_kvq_heads(H, KV):
     _run(synth.kvq_case(800 + H + KV, H, KV, 300, 256, 64, 8, sb_dtype=synth.F16))
 
 
+@pytest.mark.parametrize("q_dtype,sb_dtype", [(synth.F16, synth.BF16), (synth.BF16, synth.F16),
+                                               (synth.F16, synth.F16), (synth.BF16, synth.BF16)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_kvq_query_and_scale_dtypes(q_dtype, sb_dtype, bits):
+    # the query's and the scales' dtypes each pick an instantiation of the block kernel
+    _run(synth.kvq_case(930 + 4 * q_dtype + sb_dtype + bits, 4, 2, 700, 128, 64, bits, q_dtype=q_dtype,
+                        sb_dtype=sb_dtype))
+
+
 def test_kvq_fp16_and_large_scores():
     _run(synth.kvq_case(900, 4, 4, 200, 256, 32, 4, q_dtype=synth.F16, sb_dtype=synth.F16))
     # queries 40x larger: scores spread over tens, the softmax nearly one-hot
