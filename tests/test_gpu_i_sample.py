@@ -67,20 +67,33 @@ def test_sample_dtypes(dt, edt):
     _run(case, 0, 1.0, 64)
 
 
+def _logit_bits(x, dt):
+    """fp32 values (all exact in the 16-bit dtypes used here) as the dtype's logits."""
+    x = np.asarray(x, np.float32)
+    if dt == synth.F32:
+        return x
+    if dt == synth.F16:
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# the 16-bit dtypes run the select on their high digits only and fill the rest from the sign
+@pytest.mark.parametrize("dt", [synth.F32, synth.F16, synth.BF16])
 @pytest.mark.parametrize("k", [1, 2, 9, 50, 300])
-def test_sample_ties_at_kth(k):
-    case = synth.sample_case(30 + k, 2048, 16, 2, logit_dtype=synth.F32)
-    case.logits = np.random.default_rng(k).integers(-6, 7, 2048).astype(np.float32)   # heavy ties
+def test_sample_ties_at_kth(k, dt):
+    case = synth.sample_case(30 + k, 2048, 16, 2, logit_dtype=dt)
+    case.logits = _logit_bits(np.random.default_rng(k).integers(-6, 7, 2048), dt)   # heavy ties, both signs
     _run(case, 1, 1.0, k)
     case.gumbel[:] = 0.0                                   # equal scores: the smaller index
     _run(case, 1, 1.0, k)
 
 
-def test_sample_special_values():
-    case = synth.sample_case(40, 512, 16, 1, logit_dtype=synth.F32)
-    x = case.logits.copy()
+@pytest.mark.parametrize("dt", [synth.F32, synth.F16, synth.BF16])
+def test_sample_special_values(dt):
+    case = synth.sample_case(40, 512, 16, 1, logit_dtype=dt)
+    x = np.random.default_rng(40).normal(0.0, 2.0, 512).astype(np.float32)   # rounded or cut to the dtype
     x[:8] = [0.0, -0.0, np.inf, -np.inf, np.nan, 3.0, 3.0, -0.0]
-    case.logits = x
+    case.logits = _logit_bits(x, dt)
     for k in (1, 2, 3, 6, 9, 512):
         _run(case, 0, 1.0, k)
     g = case.gumbel.copy()
